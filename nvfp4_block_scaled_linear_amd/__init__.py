@@ -1,0 +1,23 @@
+"""NVFP4 block-scaled linear layer for AMD MI355X (gfx950).
+
+The compute lives in libnvfp4.so (hand-written HIP kernels behind the C ABI of
+include/nvfp4.h); this package is its thin Python binding over torch tensors.
+"""
+from ._binding import (  # noqa: F401
+    ACT_BF16,
+    ACT_NVFP4,
+    EXPORTS,
+    FAULT_BAD_ROUTE,
+    FAULT_NONFINITE,
+    LIB_PATH,
+    NVFP4Error,
+    OUT_COMBINE,
+    OUT_ROUTES,
+    OUT_SWIGLU_BF16,
+    grouped_linear,
+    grouped_workspace_size,
+    linear,
+    load_library,
+    quantize_act,
+    status_string,
+)

@@ -1,0 +1,217 @@
+// C ABI of libnvfp4 (declared and documented in include/nvfp4.h): argument checks on the
+// host, then kernel dispatch on the caller's stream. Nothing here allocates memory,
+// synchronizes, or keeps state between calls.
+#include <limits.h>
+#include <stdint.h>
+
+#include "kernels.hpp"
+#include "nvfp4.h"
+
+using namespace nvfp4;
+
+namespace {
+
+constexpr int64_t kMaxDim = (int64_t)1 << 30;  // sizes must fit the kernels' int indices
+constexpr int kMaxExperts = 4096;               // route grouping keeps per-expert counters in LDS
+constexpr int kStreamMaxRows = 16;              // rows of one weight-streaming pass
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+nvfp4_status launch_status(hipError_t e) { return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_LAUNCH; }
+
+// checks shared by the weight operand and the activation operand of linear/grouped calls
+nvfp4_status check_act(int32_t act_kind, const void* x, const uint8_t* x_scales,
+                       const float* x_ts, int64_t ldx, int64_t K) {
+  if (act_kind != NVFP4_ACT_BF16 && act_kind != NVFP4_ACT_NVFP4) return NVFP4_ERR_ARG;
+  if (!x) return NVFP4_ERR_NULL;
+  if (!aligned(x, 16)) return NVFP4_ERR_ALIGN;
+  if (act_kind == NVFP4_ACT_BF16) {
+    if (x_scales || x_ts) return NVFP4_ERR_ARG;
+    if (ldx < K || ldx > kMaxDim) return NVFP4_ERR_SHAPE;
+    if (ldx % 8 != 0) return NVFP4_ERR_ALIGN;
+  } else {
+    if (!x_scales || !x_ts) return NVFP4_ERR_NULL;
+    if (!aligned(x_scales, 2) || !aligned(x_ts, 4)) return NVFP4_ERR_ALIGN;
+  }
+  return NVFP4_OK;
+}
+
+nvfp4_status check_weight(const uint8_t* w_codes, const uint8_t* w_scales, const float* w_ts) {
+  if (!w_codes || !w_scales || !w_ts) return NVFP4_ERR_NULL;
+  if (!aligned(w_codes, 16) || !aligned(w_scales, 2) || !aligned(w_ts, 4)) return NVFP4_ERR_ALIGN;
+  return NVFP4_OK;
+}
+
+nvfp4_status check_k(int64_t K) {
+  if (K <= 0 || K > kMaxDim || K % 32 != 0) return NVFP4_ERR_SHAPE;
+  return NVFP4_OK;
+}
+
+// grouped-call workspace layout: 256-byte aligned regions
+struct Layout {
+  size_t offsets, active, n_active, route_expert, sorted, order, rows, total;
+};
+
+size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+Layout grouped_layout(int64_t T, int top_k, int E, int64_t N, int32_t out_mode) {
+  Layout L;
+  const size_t R = (size_t)T * (size_t)top_k;
+  size_t o = 0;
+  L.offsets = o; o = up256(o + sizeof(int32_t) * ((size_t)E + 1));
+  L.active = o; o = up256(o + sizeof(int32_t) * (size_t)E);
+  L.n_active = o; o = up256(o + sizeof(int32_t));
+  L.route_expert = o; o = up256(o + sizeof(int32_t) * R);
+  L.sorted = o; o = up256(o + sizeof(int32_t) * R);
+  L.order = o; o = up256(o + sizeof(int32_t) * R);
+  L.rows = o;
+  if (out_mode != NVFP4_OUT_ROUTES) o = up256(o + sizeof(float) * R * (size_t)N);
+  L.total = o;
+  return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* nvfp4_status_string(int32_t status) {
+  switch (status) {
+    case NVFP4_OK: return "NVFP4_OK";
+    case NVFP4_ERR_NULL: return "NVFP4_ERR_NULL: a required pointer is NULL";
+    case NVFP4_ERR_SHAPE: return "NVFP4_ERR_SHAPE: a size is invalid (<= 0, K % 32 != 0, ld too small, or too large)";
+    case NVFP4_ERR_ALIGN: return "NVFP4_ERR_ALIGN: a pointer or leading dimension is misaligned";
+    case NVFP4_ERR_ARG: return "NVFP4_ERR_ARG: an enum value or count is out of range";
+    case NVFP4_ERR_WORKSPACE: return "NVFP4_ERR_WORKSPACE: workspace too small";
+    case NVFP4_ERR_LAUNCH: return "NVFP4_ERR_LAUNCH: the HIP runtime refused a launch";
+    default: return "unknown nvfp4_status";
+  }
+}
+
+nvfp4_status nvfp4_linear(int32_t act_kind, const void* x, const uint8_t* x_scales,
+                          const float* x_ts, int64_t ldx, int64_t M, int64_t N, int64_t K,
+                          const uint8_t* w_codes, const uint8_t* w_scales, const float* w_ts,
+                          float* y, int64_t ldy, void* stream) {
+  nvfp4_status st;
+  if ((st = check_k(K)) != NVFP4_OK) return st;
+  if (M <= 0 || N <= 0 || M > kMaxDim || N > kMaxDim) return NVFP4_ERR_SHAPE;
+  if ((st = check_act(act_kind, x, x_scales, x_ts, ldx, K)) != NVFP4_OK) return st;
+  if ((st = check_weight(w_codes, w_scales, w_ts)) != NVFP4_OK) return st;
+  if (!y) return NVFP4_ERR_NULL;
+  if (ldy < N || ldy > kMaxDim) return NVFP4_ERR_SHAPE;
+  if (!aligned(y, 4)) return NVFP4_ERR_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (M <= kStreamMaxRows) {
+    StreamArgs a{};
+    a.x = x; a.x_scales = x_scales; a.x_ts = x_ts; a.ldx = ldx;
+    a.w_codes = w_codes; a.w_scales = w_scales; a.w_ts = w_ts;
+    a.N = N; a.K = K; a.y = y; a.ldy = ldy; a.M = (int32_t)M; a.apply_ts = 1;
+    return launch_status(launch_stream(a, act_kind, false, 1, s));
+  }
+  GemmArgs g{};
+  g.x = x; g.x_scales = x_scales; g.x_ts = x_ts; g.ldx = ldx;
+  g.w_codes = w_codes; g.w_scales = w_scales; g.w_ts = w_ts;
+  g.M = M; g.N = N; g.K = K; g.y = y; g.ldy = ldy;
+  return launch_status(launch_gemm(g, act_kind, s));
+}
+
+nvfp4_status nvfp4_quantize_act(int32_t in_type, const void* x, int64_t ldx, int64_t M,
+                                int64_t K, int32_t ts_mode, uint8_t* codes, uint8_t* scales,
+                                float* ts, uint32_t* faults, void* stream) {
+  nvfp4_status st;
+  if ((st = check_k(K)) != NVFP4_OK) return st;
+  if (in_type != NVFP4_IN_BF16 && in_type != NVFP4_IN_F32) return NVFP4_ERR_ARG;
+  if (ts_mode != NVFP4_TS_PER_ROW && ts_mode != NVFP4_TS_PER_TENSOR) return NVFP4_ERR_ARG;
+  if (M <= 0 || M > kMaxDim || ldx < K || ldx > kMaxDim) return NVFP4_ERR_SHAPE;
+  if (M * (K / 16) > ((int64_t)1 << 40)) return NVFP4_ERR_SHAPE;
+  if (!x || !codes || !scales || !ts) return NVFP4_ERR_NULL;
+  const int64_t elem = in_type == NVFP4_IN_BF16 ? 2 : 4;
+  if (!aligned(x, 16) || (ldx * elem) % 16 != 0) return NVFP4_ERR_ALIGN;
+  if (!aligned(codes, 16) || !aligned(ts, 4) || (faults && !aligned(faults, 4)))
+    return NVFP4_ERR_ALIGN;
+  if (ts_mode == NVFP4_TS_PER_ROW && M > (int64_t)UINT32_MAX / 2) return NVFP4_ERR_SHAPE;
+  return launch_status(launch_quantize(in_type == NVFP4_IN_BF16 ? 0 : 1, x, ldx, M, K,
+                                       ts_mode == NVFP4_TS_PER_ROW ? 0 : 1, codes, scales, ts,
+                                       faults, static_cast<hipStream_t>(stream)));
+}
+
+nvfp4_status nvfp4_grouped_linear(int32_t act_kind, const void* x, const uint8_t* x_scales,
+                                  const float* x_ts, int64_t ldx, int32_t rows_mode,
+                                  int64_t T, int32_t top_k, int64_t N, int64_t K,
+                                  int32_t num_experts, const uint8_t* w_codes,
+                                  const uint8_t* w_scales, const float* w_ts,
+                                  const int32_t* topk_ids, const float* topk_w,
+                                  int32_t out_mode, void* y, void* workspace,
+                                  size_t* workspace_bytes, uint32_t* faults, void* stream) {
+  nvfp4_status st;
+  if (!workspace_bytes) return NVFP4_ERR_NULL;
+  if ((st = check_k(K)) != NVFP4_OK) return st;
+  if (num_experts <= 0 || num_experts > kMaxExperts) return NVFP4_ERR_ARG;
+  if (top_k <= 0 || top_k > num_experts || top_k > 64) return NVFP4_ERR_ARG;
+  if (rows_mode != NVFP4_ROWS_PER_TOKEN && rows_mode != NVFP4_ROWS_PER_ROUTE) return NVFP4_ERR_ARG;
+  if (out_mode != NVFP4_OUT_ROUTES && out_mode != NVFP4_OUT_SWIGLU_BF16 &&
+      out_mode != NVFP4_OUT_COMBINE)
+    return NVFP4_ERR_ARG;
+  if (T <= 0 || N <= 0 || T > kMaxDim || N > kMaxDim || T * top_k > kMaxDim) return NVFP4_ERR_SHAPE;
+  if (out_mode == NVFP4_OUT_SWIGLU_BF16 && N % 2 != 0) return NVFP4_ERR_SHAPE;
+  if ((int64_t)num_experts * N * (K / 2) > ((int64_t)1 << 46)) return NVFP4_ERR_SHAPE;
+  const Layout L = grouped_layout(T, top_k, num_experts, N, out_mode);
+  if (!workspace) {
+    *workspace_bytes = L.total;
+    return NVFP4_OK;
+  }
+  if (*workspace_bytes < L.total) return NVFP4_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return NVFP4_ERR_ALIGN;
+  if ((st = check_act(act_kind, x, x_scales, x_ts, ldx, K)) != NVFP4_OK) return st;
+  if ((st = check_weight(w_codes, w_scales, w_ts)) != NVFP4_OK) return st;
+  if (!topk_ids || !y) return NVFP4_ERR_NULL;
+  if (out_mode == NVFP4_OUT_COMBINE && !topk_w) return NVFP4_ERR_NULL;
+  if (!aligned(topk_ids, 4) || (topk_w && !aligned(topk_w, 4)) || !aligned(y, 4) ||
+      (faults && !aligned(faults, 4)))
+    return NVFP4_ERR_ALIGN;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* base = static_cast<char*>(workspace);
+  RouteWorkspace ws;
+  ws.offsets = reinterpret_cast<int32_t*>(base + L.offsets);
+  ws.active = reinterpret_cast<int32_t*>(base + L.active);
+  ws.n_active = reinterpret_cast<int32_t*>(base + L.n_active);
+  ws.route_expert = reinterpret_cast<int32_t*>(base + L.route_expert);
+  ws.sorted = reinterpret_cast<int32_t*>(base + L.sorted);
+  ws.order = reinterpret_cast<int32_t*>(base + L.order);
+  ws.rows = reinterpret_cast<float*>(base + L.rows);
+
+  hipError_t e = launch_route_sort(topk_ids, T, top_k, num_experts, ws, faults, s);
+  if (e != hipSuccess) return NVFP4_ERR_LAUNCH;
+
+  const int64_t R = T * top_k;
+  StreamArgs a{};
+  a.x = x; a.x_scales = x_scales; a.x_ts = x_ts; a.ldx = ldx;
+  a.w_codes = w_codes; a.w_scales = w_scales; a.w_ts = w_ts;
+  a.N = N; a.K = K;
+  a.offsets = ws.offsets; a.sorted = ws.sorted; a.active = ws.active; a.n_active = ws.n_active;
+  a.rows_per_token = rows_mode == NVFP4_ROWS_PER_TOKEN ? 1 : 0;
+  a.top_k = top_k;
+  a.M = 0;
+  if (out_mode == NVFP4_OUT_ROUTES) {
+    // dropped routes must read as zero rows: clear y first (a fill kernel, capture-safe)
+    a.y = static_cast<float*>(y); a.ldy = N; a.apply_ts = 1;
+  } else {
+    a.y = ws.rows; a.ldy = N; a.apply_ts = out_mode == NVFP4_OUT_SWIGLU_BF16 ? 1 : 0;
+  }
+  const int max_active = (int)(R < num_experts ? R : num_experts);
+  if (out_mode == NVFP4_OUT_ROUTES) {
+    e = launch_zero_rows(static_cast<float*>(y), ws.route_expert, R, N, s);
+    if (e != hipSuccess) return NVFP4_ERR_LAUNCH;
+  }
+  e = launch_stream(a, act_kind, true, max_active, s);
+  if (e != hipSuccess) return NVFP4_ERR_LAUNCH;
+  if (out_mode == NVFP4_OUT_SWIGLU_BF16) {
+    e = launch_swiglu(ws.rows, ws.route_expert, R, N, static_cast<uint16_t*>(y), s);
+  } else if (out_mode == NVFP4_OUT_COMBINE) {
+    e = launch_combine(ws.rows, ws.route_expert, ws.order, topk_w, w_ts, T, top_k, N,
+                       static_cast<float*>(y), s);
+  }
+  return launch_status(e);
+}
+
+}  // extern "C"

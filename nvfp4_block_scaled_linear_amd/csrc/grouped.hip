@@ -1,0 +1,198 @@
+// Helpers of the expert-grouped call: route grouping, SwiGLU to BF16, ordered combine.
+//
+// Routes are grouped expert-ascending ("true rows, expert-ascending" with expert-first
+// offsets: Rocket log entry "Rank-local E256 MoE misses the Qwen K1 and K4 step
+// budgets", and run_moe_grouped in the entry "The expert split decodes the same
+// tokens; ..."), so one workgroup can stream an expert's weight once for all its
+// routes. The combine accumulates each token's routes in fp32 in ascending expert order
+// with the expert's tensor scale folded into the router weight (same entry, section
+// "Why rows and not partial sums"), which keeps it deterministic: no atomics touch
+// floating-point data anywhere in this file.
+#include "device.hpp"
+#include "kernels.hpp"
+
+namespace nvfp4 {
+namespace {
+
+constexpr int kSortThreads = 1024;
+
+// Single workgroup. E <= max_experts fits the LDS arrays sized at launch.
+__global__ __launch_bounds__(kSortThreads) void route_sort(const int32_t* ids, int64_t T,
+                                                           int top_k, int E, RouteWorkspace ws,
+                                                           uint32_t* faults) {
+  extern __shared__ int32_t sh[];
+  int32_t* cnt = sh;             // [E]  route count per expert, later the running cursor
+  int32_t* scan = sh + E;        // [E+1]
+  int32_t* chunk_e = sh + 2 * E + 1;  // [kSortThreads] experts of the current chunk
+  const int64_t R = T * top_k;
+  const int tid = threadIdx.x;
+
+  // (1) validate: id in range and not repeated earlier in its token; dropped -> -1
+  bool bad = false;
+  for (int64_t r = tid; r < R; r += kSortThreads) {
+    const int32_t e = ids[r];
+    bool ok = (e >= 0 && e < E);
+    const int64_t t = r / top_k;
+    const int j = (int)(r - t * top_k);
+    for (int jj = 0; jj < j && ok; jj++)
+      if (ids[t * top_k + jj] == e) ok = false;
+    ws.route_expert[r] = ok ? e : -1;
+    bad = bad || !ok;
+  }
+  if (bad && faults) atomicOr(faults, (uint32_t)NVFP4_FAULT_BAD_ROUTE);
+  for (int e = tid; e < E; e += kSortThreads) cnt[e] = 0;
+  __syncthreads();
+
+  // (2) histogram (integer atomics: order-independent)
+  for (int64_t r = tid; r < R; r += kSortThreads) {
+    const int32_t e = ws.route_expert[r];
+    if (e >= 0) atomicAdd(&cnt[e], 1);
+  }
+  __syncthreads();
+
+  // (3) exclusive scan of counts and of the active flags (thread 0: E is small)
+  if (tid == 0) {
+    int32_t run = 0, act = 0;
+    for (int e = 0; e < E; e++) {
+      scan[e] = run;
+      ws.offsets[e] = run;
+      run += cnt[e];
+      if (cnt[e] > 0) ws.active[act++] = e;
+    }
+    scan[E] = run;
+    ws.offsets[E] = run;
+    *ws.n_active = act;
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += kSortThreads) cnt[e] = scan[e];  // cursors
+  __syncthreads();
+
+  // (4) stable scatter, chunk by chunk in route order
+  for (int64_t c0 = 0; c0 < R; c0 += kSortThreads) {
+    const int64_t r = c0 + tid;
+    const int32_t e = (r < R) ? ws.route_expert[r] : -1;
+    chunk_e[tid] = e;
+    __syncthreads();
+    int rank = 0;
+    bool last = true;
+    if (e >= 0) {
+      for (int i = 0; i < tid; i++) rank += (chunk_e[i] == e);
+      const int lim = (int)((R - c0) < kSortThreads ? (R - c0) : kSortThreads);
+      for (int i = tid + 1; i < lim && last; i++) last = (chunk_e[i] != e);
+      ws.sorted[cnt[e] + rank] = (int32_t)r;
+    }
+    __syncthreads();  // every cursor read of this chunk is done
+    if (e >= 0 && last) cnt[e] += rank + 1;  // one writer per expert: its last route
+    __syncthreads();
+  }
+
+  // (5) per token: its route slots in ascending expert id, dropped routes last (-1)
+  for (int64_t t = tid; t < T; t += kSortThreads) {
+    int32_t* o = ws.order + t * top_k;
+    int n = 0;
+    for (int j = 0; j < top_k; j++)
+      if (ws.route_expert[t * top_k + j] >= 0) o[n++] = j;
+    for (int i = 1; i < n; i++) {  // insertion sort by expert id
+      const int32_t v = o[i];
+      const int32_t ev = ws.route_expert[t * top_k + v];
+      int p = i - 1;
+      while (p >= 0 && ws.route_expert[t * top_k + o[p]] > ev) {
+        o[p + 1] = o[p];
+        p--;
+      }
+      o[p + 1] = v;
+    }
+    for (int j = n; j < top_k; j++) o[j] = -1;
+  }
+}
+
+// a[r][n] = bf16_rne(silu(h[r][n]) * h[r][n + N/2]), silu(g) = g / (1 + exp(-g))
+__global__ __launch_bounds__(256) void swiglu_kernel(const float* rows,
+                                                     const int32_t* route_expert, int64_t R,
+                                                     int64_t N, uint16_t* out) {
+  const int64_t half = N >> 1;
+  const int64_t total = R * half;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = i / half, n = i - r * half;
+    uint32_t bits = 0u;
+    if (route_expert[r] >= 0) {
+      const float g = rows[r * N + n];
+      const float u = rows[r * N + half + n];
+      const float silu = g / (1.0f + expf(-g));
+      bits = f32_to_bf16_rne(silu * u);
+    }
+    out[i] = (uint16_t)bits;
+  }
+}
+
+// y[t][n] = sum over the token's routes in ascending expert id of (w * ts_e) * row[n]
+__global__ __launch_bounds__(256) void combine_kernel(const float* rows,
+                                                      const int32_t* route_expert,
+                                                      const int32_t* order, const float* topk_w,
+                                                      const float* w_ts, int64_t T, int top_k,
+                                                      int64_t N, float* y) {
+  const int64_t total = T * N;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t t = i / N, n = i - t * N;
+    float acc = 0.0f;
+    for (int jj = 0; jj < top_k; jj++) {
+      const int j = order[t * top_k + jj];
+      if (j < 0) break;
+      const int64_t r = t * top_k + j;
+      const float wr = topk_w[r] * w_ts[route_expert[r]];
+      acc = __builtin_fmaf(wr, rows[r * N + n], acc);
+    }
+    y[i] = acc;
+  }
+}
+
+// rows of dropped routes read as zero in the per-route output form
+__global__ __launch_bounds__(256) void zero_rows_kernel(float* y, const int32_t* route_expert,
+                                                        int64_t R, int64_t N) {
+  const int64_t total = R * N;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    if (route_expert[i / N] < 0) y[i] = 0.0f;
+  }
+}
+
+int64_t grid_for(int64_t total) {
+  int64_t g = (total + 255) / 256;
+  return g < 1 ? 1 : (g > 8192 ? 8192 : g);
+}
+
+}  // namespace
+
+hipError_t launch_route_sort(const int32_t* topk_ids, int64_t T, int top_k, int E,
+                             const RouteWorkspace& ws, uint32_t* faults, hipStream_t stream) {
+  const size_t lds = sizeof(int32_t) * ((size_t)2 * E + 1 + kSortThreads);
+  hipLaunchKernelGGL(route_sort, dim3(1), dim3(kSortThreads), lds, stream, topk_ids, T, top_k, E,
+                     ws, faults);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero_rows(float* y, const int32_t* route_expert, int64_t R, int64_t N,
+                            hipStream_t stream) {
+  hipLaunchKernelGGL(zero_rows_kernel, dim3((uint32_t)grid_for(R * N)), dim3(256), 0, stream, y,
+                     route_expert, R, N);
+  return hipGetLastError();
+}
+
+hipError_t launch_swiglu(const float* rows, const int32_t* route_expert, int64_t R, int64_t N,
+                         uint16_t* out, hipStream_t stream) {
+  hipLaunchKernelGGL(swiglu_kernel, dim3((uint32_t)grid_for(R * (N / 2))), dim3(256), 0, stream,
+                     rows, route_expert, R, N, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const float* rows, const int32_t* route_expert, const int32_t* order,
+                          const float* topk_w, const float* w_ts, int64_t T, int top_k,
+                          int64_t N, float* y, hipStream_t stream) {
+  hipLaunchKernelGGL(combine_kernel, dim3((uint32_t)grid_for(T * N)), dim3(256), 0, stream, rows,
+                     route_expert, order, topk_w, w_ts, T, top_k, N, y);
+  return hipGetLastError();
+}
+
+}  // namespace nvfp4

@@ -1,0 +1,80 @@
+// Internal launch interface between the C ABI (api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "nvfp4.h"
+
+namespace nvfp4 {
+
+// Rows of one weight-streaming pass: up to 16 activation rows against one weight.
+struct StreamArgs {
+  // activations: BF16 bits [rows][ldx], or NVFP4 codes [rows][K/2] + scales + row ts
+  const void* x;
+  const uint8_t* x_scales;
+  const float* x_ts;
+  int64_t ldx;      // BF16: elements per row
+  // weight (for the grouped form: expert 0; expert e is offset by e * N * K/2 etc.)
+  const uint8_t* w_codes;
+  const uint8_t* w_scales;
+  const float* w_ts;
+  int64_t N, K;
+  // output fp32 [rows][ldy]
+  float* y;
+  int64_t ldy;
+  int32_t M;        // dense: number of rows (<= 16)
+  int32_t apply_ts; // multiply the accumulator by the weight's tensor scale
+  // grouped form (NULL for dense)
+  const int32_t* offsets;    // [E+1] route ranges per expert in `sorted`
+  const int32_t* sorted;     // route ids grouped by expert
+  const int32_t* active;     // [E] active experts, ascending
+  const int32_t* n_active;   // [1]
+  int32_t rows_per_token;    // x row of route r: r / top_k (1) or r (0)
+  int32_t top_k;
+};
+
+hipError_t launch_stream(const StreamArgs& a, int act_kind, bool grouped, int max_active,
+                         hipStream_t stream);
+
+struct GemmArgs {
+  const void* x;
+  const uint8_t* x_scales;
+  const float* x_ts;
+  int64_t ldx;
+  const uint8_t* w_codes;
+  const uint8_t* w_scales;
+  const float* w_ts;
+  int64_t M, N, K;
+  float* y;
+  int64_t ldy;
+};
+
+hipError_t launch_gemm(const GemmArgs& a, int act_kind, hipStream_t stream);
+
+hipError_t launch_quantize(int in_type, const void* x, int64_t ldx, int64_t M, int64_t K,
+                           int ts_mode, uint8_t* codes, uint8_t* scales, float* ts,
+                           uint32_t* faults, hipStream_t stream);
+
+// grouped-call helpers
+struct RouteWorkspace {
+  int32_t* offsets;       // [E+1]
+  int32_t* active;        // [E]
+  int32_t* n_active;      // [1]
+  int32_t* route_expert;  // [R] expert of route r, or -1 when dropped
+  int32_t* sorted;        // [R]
+  int32_t* order;         // [T][top_k] token's route slots in ascending expert id (-1 last)
+  float* rows;            // [R][N] fp32 per-route rows (SwiGLU / combine forms)
+};
+
+hipError_t launch_route_sort(const int32_t* topk_ids, int64_t T, int top_k, int E,
+                             const RouteWorkspace& ws, uint32_t* faults, hipStream_t stream);
+hipError_t launch_zero_rows(float* y, const int32_t* route_expert, int64_t R, int64_t N,
+                            hipStream_t stream);
+hipError_t launch_swiglu(const float* rows, const int32_t* route_expert, int64_t R, int64_t N,
+                         uint16_t* out, hipStream_t stream);
+hipError_t launch_combine(const float* rows, const int32_t* route_expert, const int32_t* order,
+                          const float* topk_w, const float* w_ts, int64_t T, int top_k,
+                          int64_t N, float* y, hipStream_t stream);
+
+}  // namespace nvfp4

@@ -1,0 +1,280 @@
+"""GPU parity of libnvfp4 against the CPU oracle: device decode, quantizer, W4A16 and
+W4A4 linear on ragged shapes and on the full workload shapes.
+
+Bar: codes, scales and tensor scales bit-exact; every linear output within
+|gpu - oracle| <= 1e-4 * sum_k |x_k w_k| + 1e-6 (the oracle sums in float64)."""
+import numpy as np
+import pytest
+import torch
+
+import nvfp4_block_scaled_linear_amd as nv
+import oracle
+from gpu_helpers import assert_within, device, quantize_both, to_dev_bf16
+from synth import WORKLOADS, act_bf16, weight_f32
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return device()
+
+
+@pytest.fixture(scope="module")
+def o():
+    return oracle.Oracle()
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+# ---- decode ------------------------------------------------------------------------------
+
+def _decode_weight(dev):
+    """256 rows (row n uses scale byte n for both of its 16-blocks), K = 32, row codes
+    0..15 twice (low nibble first), ts = 1."""
+    codes = np.zeros((256, 16), np.uint8)
+    for j in range(16):
+        codes[:, j] = ((2 * j) % 16) | (((2 * j + 1) % 16) << 4)
+    scales = np.repeat(np.arange(256, dtype=np.uint8)[:, None], 2, axis=1)
+    ts = np.ones(1, np.float32)
+    return [torch.from_numpy(a).to(dev) for a in (codes, scales, ts)]
+
+
+@pytest.mark.parametrize("M", [16, 32])  # 16: weight-streaming kernel; 32: tiled MFMA kernel
+def test_decode_every_code_and_scale(dev, o, M):
+    """One-hot rows pick single weight elements: y[m][n] = e2m1(m % 16) * e4m3(n) exactly,
+    for all 16 codes x 256 scale bytes (NaN scale bytes give NaN)."""
+    _say(f"decode exhaustive through the M={M} path")
+    c, s, t = _decode_weight(dev)
+    x = np.zeros((M, 32), np.float32)
+    for m in range(M):
+        x[m, m] = 1.0
+    y = nv.linear(torch.from_numpy(x).to(dev).to(torch.bfloat16), c, s, t).cpu().numpy()
+    for m in range(M):
+        for n in range(256):
+            want = o.e2m1_value(m % 16) * o.e4m3_value(n)
+            got = y[m, n]
+            if np.isnan(want):
+                assert np.isnan(got), (m, n)
+            else:
+                assert got == np.float32(want), (m, n, got, want)
+
+
+# ---- quantizer ---------------------------------------------------------------------------
+
+def _edge_tensors():
+    rng = np.random.default_rng(5)
+    tie = np.array([[6.0, 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, -0.25, -0.75, -1.25,
+                     -1.75, -2.5, -3.5, -5.0, -0.0] * 2], np.float32)
+    crafted = np.zeros((1, 64), np.float32)
+    crafted[0, 0] = 1.0
+    for blk, bits in ((1, 0x3F524924), (2, 0x3CF6DB6D), (3, 0x3EC00001)):
+        crafted[0, 16 * blk + 3] = np.array(bits, np.uint32).view(np.float32)
+        crafted[0, 16 * blk + 7] = -0.5 * crafted[0, 16 * blk + 3]
+    zero_rows = np.zeros((3, 96), np.float32)
+    zero_rows[1] = rng.normal(0, 1, 96)
+    zero_rows[2, :16] = -0.0
+    wide = np.r_[np.full(16, 1e-30), np.full(16, 3e20), np.full(16, 1e-40), rng.normal(0, 1, 16)]
+    return {
+        "tie_block": tie,
+        "op_order_ties": crafted,
+        "zero_and_negzero_rows": zero_rows,
+        "wide_range": wide.astype(np.float32)[None, :],
+        "cauchy": (rng.standard_cauchy((5, 160)) * 0.1).astype(np.float32),
+        "normal_ragged": rng.normal(0, 0.02, (7, 96)).astype(np.float32),
+    }
+
+
+@pytest.mark.parametrize("name", sorted(_edge_tensors()))
+@pytest.mark.parametrize("per_tensor", [False, True])
+def test_quantizer_edges_bit_exact(dev, o, name, per_tensor):
+    w = _edge_tensors()[name]
+    _say(f"quantize {name} {w.shape} per_tensor={per_tensor}")
+    quantize_both(o, w, dev, per_tensor=per_tensor)
+
+
+@pytest.mark.parametrize("M", WORKLOADS["w4a4"]["Ms"] + (3,))
+def test_quantizer_bf16_rows_bit_exact(dev, o, M):
+    K = WORKLOADS["w4a4"]["K"]
+    xb = act_bf16(WORKLOADS["w4a4"]["x_seed_base"] + M, M, K)
+    _say(f"quantize bf16 rows M={M} K={K}")
+    c, s, t = nv.quantize_act(to_dev_bf16(xb, dev))
+    oc, os_, ot = o.quantize_bf16(xb, per_row=True)
+    assert np.array_equal(t.cpu().numpy().view(np.uint32), ot.view(np.uint32))
+    assert np.array_equal(s.cpu().numpy(), os_)
+    assert np.array_equal(c.cpu().numpy(), oc)
+
+
+@pytest.mark.parametrize("name", ["single_linear", "decode_sweep", "prefill", "w4a4"])
+def test_quantizer_weights_bit_exact(dev, o, name):
+    cfg = WORKLOADS[name]
+    w = weight_f32(cfg["w_seed"], cfg["N"], cfg["K"])
+    _say(f"quantize weight {name} {w.shape}")
+    quantize_both(o, w, dev, per_tensor=True)
+
+
+def test_quantizer_flags_nonfinite(dev):
+    faults = torch.zeros(1, dtype=torch.int32, device=dev)
+    for bad in (np.nan, np.inf):
+        w = np.ones((2, 32), np.float32)
+        w[1, 7] = bad
+        faults.zero_()
+        nv.quantize_act(torch.from_numpy(w).to(dev), faults=faults)
+        assert int(faults.item()) & nv.FAULT_NONFINITE
+        faults.zero_()
+        nv.quantize_act(torch.from_numpy(w).to(dev), per_tensor=True, faults=faults)
+        assert int(faults.item()) & nv.FAULT_NONFINITE
+    faults.zero_()
+    nv.quantize_act(torch.ones((2, 32), device=dev), faults=faults)
+    assert int(faults.item()) == 0
+
+
+# ---- linear, ragged shapes ------------------------------------------------------------------
+
+def _linear_case(dev, o, M, N, K, seed, pad_x=0, pad_y=0):
+    w = weight_f32(seed, N, K)
+    (c, s, t), (oc, os_, ot) = quantize_both(o, w, dev)
+    xb = act_bf16(seed + 1000, M, K + pad_x)
+    xd = to_dev_bf16(xb, dev)[:, :K]
+    out = torch.full((M, N + pad_y), float("nan"), device=dev)[:, :N]
+    y = nv.linear(xd, c, s, t, out=out)
+    yr, b = o.linear(xb[:, :K], oc, os_, ot)
+    return y.cpu().numpy(), yr, b
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 32), (3, 17, 96), (16, 200, 544), (5, 1000, 4128),
+                                   (2, 3000, 64), (16, 48, 8192)])
+def test_linear_stream_ragged(dev, o, M, N, K):
+    _say(f"stream linear M={M} N={N} K={K}")
+    y, yr, b = _linear_case(dev, o, M, N, K, seed=M * 7 + N)
+    assert_within(y, yr, b, f"M={M} N={N} K={K}")
+
+
+@pytest.mark.parametrize("M,N,K", [(17, 255, 64), (130, 600, 1056), (300, 130, 96), (64, 256, 32)])
+def test_linear_gemm_ragged(dev, o, M, N, K):
+    _say(f"gemm linear M={M} N={N} K={K}")
+    y, yr, b = _linear_case(dev, o, M, N, K, seed=M * 3 + N)
+    assert_within(y, yr, b, f"M={M} N={N} K={K}")
+
+
+def test_linear_leading_dimensions(dev, o):
+    _say("linear with padded x and y rows")
+    for M in (4, 40):
+        y, yr, b = _linear_case(dev, o, M, 300, 256, seed=11, pad_x=40, pad_y=13)
+        assert_within(y, yr, b, f"padded M={M}")
+
+
+# ---- the workloads at full size --------------------------------------------------------------
+
+def test_single_linear_full(dev, o):
+    cfg = WORKLOADS["single_linear"]
+    _say("single linear M=1 K=2048 N=2048")
+    w = weight_f32(cfg["w_seed"], cfg["N"], cfg["K"])
+    (c, s, t), (oc, os_, ot) = quantize_both(o, w, dev)
+    xb = act_bf16(cfg["x_seed"], cfg["M"], cfg["K"])
+    y = nv.linear(to_dev_bf16(xb, dev), c, s, t).cpu().numpy()
+    yr, b = o.linear(xb, oc, os_, ot)
+    assert_within(y, yr, b, "single_linear")
+
+
+@pytest.fixture(scope="module")
+def sweep_weight(dev, o):
+    cfg = WORKLOADS["decode_sweep"]
+    w = weight_f32(cfg["w_seed"], cfg["N"], cfg["K"])
+    dq, oq = quantize_both(o, w, dev)
+    wdq = o.dequant(*oq, per_row=False)
+    return dq, oq, wdq
+
+
+@pytest.mark.parametrize("M", WORKLOADS["decode_sweep"]["Ms"])
+def test_decode_sweep_full(dev, o, sweep_weight, M):
+    cfg = WORKLOADS["decode_sweep"]
+    _say(f"decode sweep M={M} K={cfg['K']} N={cfg['N']}")
+    (c, s, t), _, wdq = sweep_weight
+    xb = act_bf16(cfg["x_seed_base"] + M, M, cfg["K"])
+    y = nv.linear(to_dev_bf16(xb, dev), c, s, t).cpu().numpy()
+    yr, b = o.linear_f64(o.bf16_to_f64(xb), wdq)
+    assert_within(y, yr, b, f"decode sweep M={M}")
+
+
+def test_decode_rows_batch_invariant_and_deterministic(dev, sweep_weight):
+    """Row m's bits do not depend on the other rows of the pass, and repeat exactly."""
+    cfg = WORKLOADS["decode_sweep"]
+    (c, s, t), _, _ = sweep_weight
+    xb = act_bf16(cfg["x_seed_base"] + 16, 16, cfg["K"])
+    xd = to_dev_bf16(xb, dev)
+    y16 = nv.linear(xd, c, s, t)
+    for m in (0, 5, 15):
+        y1 = nv.linear(xd[m:m + 1], c, s, t)
+        assert torch.equal(y1[0], y16[m]), m
+    for _ in range(3):
+        assert torch.equal(nv.linear(xd, c, s, t), y16)
+
+
+def test_negative_control_corrupted_scale_is_detected(dev, o, sweep_weight):
+    """One flipped scale byte in the GPU's copy of the weight must break parity."""
+    cfg = WORKLOADS["decode_sweep"]
+    (c, s, t), _, wdq = sweep_weight
+    s_bad = s.clone()
+    s_bad[123, 45] ^= 0x08  # changes that block's scale by a power of two
+    xb = act_bf16(cfg["x_seed_base"] + 4, 4, cfg["K"])
+    y = nv.linear(to_dev_bf16(xb, dev), c, s_bad, t).cpu().numpy()
+    yr, b = o.linear_f64(o.bf16_to_f64(xb), wdq)
+    ok, worst = oracle.within_bound(y, yr, b)
+    assert not ok and worst > 1.0
+    bad_cols = np.nonzero(np.any(np.abs(y - yr) > 1e-4 * b + 1e-6, axis=0))[0]
+    assert bad_cols.tolist() == [123]
+
+
+def test_prefill_full_sampled_rows(dev, o):
+    cfg = WORKLOADS["prefill"]
+    M, N, K = cfg["M"], cfg["N"], cfg["K"]
+    _say(f"prefill M={M} K={K} N={N} (64 sampled rows vs oracle)")
+    w = weight_f32(cfg["w_seed"], N, K)
+    (c, s, t), oq = quantize_both(o, w, dev)
+    xb = act_bf16(cfg["x_seed"], M, K)
+    y = nv.linear(to_dev_bf16(xb, dev), c, s, t)
+    rows = np.unique(np.r_[0, 1, 127, 128, 1023, 2047, np.random.default_rng(1).choice(M, 58, replace=False)])
+    wdq = o.dequant(*oq, per_row=False)
+    yr, b = o.linear_f64(o.bf16_to_f64(xb[rows]), wdq)
+    assert_within(y[torch.from_numpy(rows).to(dev)].cpu().numpy(), yr, b, "prefill rows")
+    # rows do not depend on M (the tile they fall in is computed the same way)
+    y_small = nv.linear(to_dev_bf16(xb[:130], dev), c, s, t)
+    assert torch.equal(y_small, y[:130])
+    assert bool(torch.isfinite(y).all())
+
+
+@pytest.mark.parametrize("M", WORKLOADS["w4a4"]["Ms"])
+def test_w4a4_full(dev, o, M):
+    cfg = WORKLOADS["w4a4"]
+    K, N = cfg["K"], cfg["N"]
+    _say(f"w4a4 M={M} K={K} N={N}")
+    w = weight_f32(cfg["w_seed"], N, K)
+    (c, s, t), oq = quantize_both(o, w, dev)
+    xb = act_bf16(cfg["x_seed_base"] + M, M, K)
+    xc, xs, xt = nv.quantize_act(to_dev_bf16(xb, dev))
+    oc, os_, ot = o.quantize_bf16(xb, per_row=True)
+    assert np.array_equal(xc.cpu().numpy(), oc) and np.array_equal(xs.cpu().numpy(), os_)
+    assert np.array_equal(xt.cpu().numpy().view(np.uint32), ot.view(np.uint32))
+    y = nv.linear(xc, c, s, t, x_scales=xs, x_ts=xt).cpu().numpy()
+    rows = np.arange(M) if M <= 64 else np.unique(np.r_[0, M - 1, np.random.default_rng(2).choice(M, 62, replace=False)])
+    yr, b = o.linear_w4a4(oc[rows], os_[rows], ot[rows], *oq)
+    assert_within(y[rows], yr, b, f"w4a4 M={M}")
+
+
+def test_w4a4_equals_w4a16_on_decoded_rows(dev, o):
+    """W4A4 = ts_a[m] * (W4A16 with x' = e2m1 * e4m3 of the activation codes, exact in
+    BF16), bit for bit through the same kernel."""
+    cfg = WORKLOADS["w4a4"]
+    K, N = cfg["K"], cfg["N"]
+    w = weight_f32(cfg["w_seed"], N, K)
+    (c, s, t), _ = quantize_both(o, w, dev)
+    xb = act_bf16(77, 4, K)
+    xc, xs, xt = nv.quantize_act(to_dev_bf16(xb, dev))
+    y4 = nv.linear(xc, c, s, t, x_scales=xs, x_ts=xt)
+    xhat = o.dequant(xc.cpu().numpy(), xs.cpu().numpy(), np.ones(4, np.float32), per_row=True)
+    y16 = nv.linear(torch.from_numpy(xhat.astype(np.float32)).to(dev).to(torch.bfloat16), c, s, t)
+    want = y16 / t * (xt[:, None] * t)
+    assert torch.allclose(y4, want, rtol=1e-6, atol=1e-30)

@@ -1,0 +1,177 @@
+"""GPU parity of the expert-grouped call (nvfp4_grouped_linear) against the oracle's MoE
+reading: 128 experts, gate_up 2048 -> 1536 and down 768 -> 2048, 16 tokens, top-8.
+
+Stage-wise, on the GPU's own intermediates:
+ (i)   gate_up per-route rows within the linear bound;
+ (ii)  SwiGLU -> BF16 equal to the BF16 rounding of the float64 SwiGLU of the GPU's
+       fp32 rows, up to one BF16 ulp where fp32 and fp64 straddle a rounding point;
+ (iii) down + ordered combine within 1e-4 * sum_routes |r| sum_k |a_k w_k| + 1e-6;
+ (iv)  end-to-end against the oracle's own chain: error/bound ratio reported only."""
+import numpy as np
+import pytest
+import torch
+
+import nvfp4_block_scaled_linear_amd as nv
+import oracle
+from gpu_helpers import assert_within, device, quantize_both, to_dev_bf16
+from synth import WORKLOADS, act_bf16, moe_expert_weights, moe_routes, weight_f32
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return device()
+
+
+@pytest.fixture(scope="module")
+def o():
+    return oracle.Oracle()
+
+
+@pytest.fixture(scope="module")
+def moe(dev, o):
+    cfg = WORKLOADS["moe_decode"]
+    E, T, k = cfg["E"], cfg["T"], cfg["top_k"]
+    _say(f"MoE weights: {E} experts, quantized on both sides")
+    g = {name: [] for name in ("gc", "gs", "gt", "dc", "ds", "dt", "ogc", "ogs", "ogt", "odc", "ods", "odt")}
+    for e in range(E):
+        gu, dn = moe_expert_weights(cfg["w_seed"], e, cfg["N_gu"], cfg["K_gu"], cfg["N_d"], cfg["K_d"])
+        (c, s, t), (oc, os_, ot) = quantize_both(o, gu, dev)
+        g["gc"].append(c); g["gs"].append(s); g["gt"].append(t)
+        g["ogc"].append(oc); g["ogs"].append(os_); g["ogt"].append(ot)
+        (c, s, t), (oc, os_, ot) = quantize_both(o, dn, dev)
+        g["dc"].append(c); g["ds"].append(s); g["dt"].append(t)
+        g["odc"].append(oc); g["ods"].append(os_); g["odt"].append(ot)
+    d = {}
+    for key in ("gc", "gs", "dc", "ds"):
+        d[key] = torch.stack(g[key])
+    for key in ("gt", "dt"):
+        d[key] = torch.cat(g[key])
+    for key in ("ogc", "ogs", "odc", "ods"):
+        d[key] = np.stack(g[key])
+    for key in ("ogt", "odt"):
+        d[key] = np.concatenate(g[key])
+    ids, rw = moe_routes(cfg["route_seed"], T, E, k)
+    xb = act_bf16(cfg["x_seed"], T, cfg["K_gu"])
+    d.update(ids=ids, rw=rw, xb=xb, ids_d=torch.from_numpy(ids).to(dev),
+             rw_d=torch.from_numpy(rw).to(dev), x_d=to_dev_bf16(xb, dev))
+    return d
+
+
+def test_moe_gate_up_routes(dev, o, moe):
+    _say("MoE stage (i): gate_up per-route rows")
+    h = nv.grouped_linear(moe["x_d"], moe["gc"], moe["gs"], moe["gt"], moe["ids_d"])
+    hr, hb = o.moe_gate_up(moe["xb"], moe["ids"], moe["ogc"], moe["ogs"], moe["ogt"])
+    assert_within(h.cpu().numpy(), hr, hb, "gate_up rows")
+
+
+def test_moe_swiglu_bf16(dev, o, moe):
+    _say("MoE stage (ii): SwiGLU to BF16 on the GPU's rows")
+    h = nv.grouped_linear(moe["x_d"], moe["gc"], moe["gs"], moe["gt"], moe["ids_d"])
+    a = nv.grouped_linear(moe["x_d"], moe["gc"], moe["gs"], moe["gt"], moe["ids_d"],
+                          out_mode=nv.OUT_SWIGLU_BF16)
+    a_bits = a.view(torch.int16).cpu().numpy().view(np.uint16)
+    ref = o.swiglu(h.cpu().numpy().astype(np.float64))
+    ref_bits = np.array([o.bf16_round(v) for v in ref.ravel()], np.uint16).reshape(ref.shape)
+    exact = np.mean(a_bits == ref_bits)
+    # within one BF16 ulp: adjacent bit patterns of the same sign
+    diff = np.abs(a_bits.astype(np.int32) - ref_bits.astype(np.int32))
+    assert np.all(diff <= 1), np.argwhere(diff > 1)[:5]
+    assert exact >= 0.999, exact
+    _say(f"SwiGLU BF16 bit-exact fraction {exact:.6f}")
+
+
+def test_moe_down_combine_and_end_to_end(dev, o, moe):
+    _say("MoE stage (iii): down + ordered combine on the GPU's BF16 activations")
+    a = nv.grouped_linear(moe["x_d"], moe["gc"], moe["gs"], moe["gt"], moe["ids_d"],
+                          out_mode=nv.OUT_SWIGLU_BF16)
+    y = nv.grouped_linear(a, moe["dc"], moe["ds"], moe["dt"], moe["ids_d"], topk_w=moe["rw_d"],
+                          out_mode=nv.OUT_COMBINE, rows_per_route=True)
+    a_bits = a.view(torch.int16).cpu().numpy().view(np.uint16)
+    yr, yb = o.moe_down_combine(a_bits, moe["ids"], moe["rw"], moe["odc"], moe["ods"], moe["odt"])
+    assert_within(y.cpu().numpy(), yr, yb, "down+combine")
+    # (iv) the oracle's own chain end to end: reported, not gated
+    hr, _ = o.moe_gate_up(moe["xb"], moe["ids"], moe["ogc"], moe["ogs"], moe["ogt"])
+    ar = o.swiglu(hr)
+    ar_bits = np.array([o.bf16_round(v) for v in ar.ravel()], np.uint16).reshape(ar.shape)
+    ye, eb = o.moe_down_combine(ar_bits, moe["ids"], moe["rw"], moe["odc"], moe["ods"], moe["odt"])
+    ratio = np.max(np.abs(y.cpu().numpy() - ye) / (1e-4 * eb + 1e-6))
+    _say(f"MoE end-to-end worst error/bound ratio (not gated): {ratio:.4f}")
+
+
+def test_moe_deterministic_and_token_permutation(dev, moe):
+    a = nv.grouped_linear(moe["x_d"], moe["gc"], moe["gs"], moe["gt"], moe["ids_d"],
+                          out_mode=nv.OUT_SWIGLU_BF16)
+    y1 = nv.grouped_linear(a, moe["dc"], moe["ds"], moe["dt"], moe["ids_d"], topk_w=moe["rw_d"],
+                           out_mode=nv.OUT_COMBINE, rows_per_route=True)
+    for _ in range(3):
+        y2 = nv.grouped_linear(a, moe["dc"], moe["ds"], moe["dt"], moe["ids_d"], topk_w=moe["rw_d"],
+                               out_mode=nv.OUT_COMBINE, rows_per_route=True)
+        assert torch.equal(y1, y2)
+    T, k = moe["ids"].shape
+    perm = torch.from_numpy(np.random.default_rng(4).permutation(T)).to(dev)
+    ids_p = moe["ids_d"][perm].contiguous()
+    rw_p = moe["rw_d"][perm].contiguous()
+    a_p = a.view(T, k, -1)[perm].reshape(T * k, -1).contiguous()
+    y_p = nv.grouped_linear(a_p, moe["dc"], moe["ds"], moe["dt"], ids_p, topk_w=rw_p,
+                            out_mode=nv.OUT_COMBINE, rows_per_route=True)
+    assert torch.equal(y_p, y1[perm])
+
+
+def test_grouped_top1_equals_dense(dev, moe):
+    """With one route per token, each route row is the dense linear of that expert,
+    bit for bit (same kernel, same K split)."""
+    ids1 = moe["ids_d"][:, :1].contiguous()
+    h = nv.grouped_linear(moe["x_d"], moe["gc"], moe["gs"], moe["gt"], ids1)
+    for t in range(ids1.shape[0]):
+        e = int(ids1[t, 0])
+        yd = nv.linear(moe["x_d"][t:t + 1], moe["gc"][e], moe["gs"][e], moe["gt"][e:e + 1])
+        assert torch.equal(h[t], yd[0]), t
+
+
+def test_grouped_bad_routes_flagged_and_dropped(dev, o):
+    E, N, K, T, k = 6, 40, 64, 4, 3
+    ws = [quantize_both(o, weight_f32(8, N, K, stream=30 + e), dev) for e in range(E)]
+    wc = torch.stack([q[0][0] for q in ws]); wsc = torch.stack([q[0][1] for q in ws])
+    wts = torch.cat([q[0][2] for q in ws])
+    ids = np.array([[0, 5, 2], [1, 1, 3], [7, 2, -1], [4, 0, 5]], np.int32)
+    xb = act_bf16(12, T, K)
+    faults = torch.zeros(1, dtype=torch.int32, device=dev)
+    h = nv.grouped_linear(to_dev_bf16(xb, dev), wc, wsc, wts, torch.from_numpy(ids).to(dev),
+                          faults=faults).cpu().numpy()
+    assert int(faults.item()) & nv.FAULT_BAD_ROUTE
+    dropped = {(1, 1), (2, 0), (2, 2)}
+    for t in range(T):
+        for j in range(k):
+            r = t * k + j
+            if (t, j) in dropped:
+                assert np.all(h[r] == 0), (t, j)
+            else:
+                e = ids[t, j]
+                yr, b = o.linear(xb[t:t + 1], ws[e][1][0], ws[e][1][1], ws[e][1][2])
+                assert_within(h[r:r + 1], yr, b, f"route {t},{j}")
+
+
+def test_grouped_w4a4_and_many_routes_per_expert(dev, o):
+    """NVFP4 activations per token, and an expert with more than 16 routes (several
+    16-row passes over its weight)."""
+    E, N, K, T, k = 3, 72, 96, 40, 2
+    ws = [quantize_both(o, weight_f32(9, N, K, stream=40 + e), dev) for e in range(E)]
+    wc = torch.stack([q[0][0] for q in ws]); wsc = torch.stack([q[0][1] for q in ws])
+    wts = torch.cat([q[0][2] for q in ws])
+    ids = np.stack([np.zeros(T, np.int32), 1 + (np.arange(T) % 2)], axis=1).astype(np.int32)
+    xb = act_bf16(13, T, K)
+    xc, xs, xt = nv.quantize_act(to_dev_bf16(xb, dev))
+    h = nv.grouped_linear(xc, wc, wsc, wts, torch.from_numpy(ids).to(dev), x_scales=xs,
+                          x_ts=xt).cpu().numpy()
+    oc, os_, ot = o.quantize_bf16(xb, per_row=True)
+    for t in range(T):
+        for j in range(k):
+            e = ids[t, j]
+            yr, b = o.linear_w4a4(oc[t:t + 1], os_[t:t + 1], ot[t:t + 1], *ws[e][1])
+            assert_within(h[t * k + j:t * k + j + 1], yr, b, f"w4a4 route {t},{j}")
