@@ -1,0 +1,379 @@
+"""Benchmark of the NVFP4 block-scaled linear layer on one MI355X.
+
+The step (what `--steps` counts) is the decode-bucket sweep: one NVFP4 linear launch per
+M in {1, 2, 4, 8, 16} on a fused-QKV-sized weight (K=4096, N=12288), BF16 activations,
+fp32 output. Every launch streams a different copy of the packed weight (the copies
+total > 1 GiB, well past the 256 MB Infinity Cache), so each reads its weight from HBM
+as a real decode step does for each layer. Launches are replayed from a HIP graph so the
+GPU runs them back to back; HIP events on the launching stream time the replays.
+
+Printed: one JSON line. `value` is the sweep's algorithmic bytes per second; `roofline`
+is the weight-streaming kernel against the 8 TB/s HBM peak; `cpu_baseline` is the CPU
+oracle (plain C, float64) on the same sweep. Other workloads (the single 2048x2048
+linear, the prefill GEMM, the MoE decode layer and W4A4) are timed the same way and
+reported under their own keys.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+import torch  # noqa: E402
+
+METRIC = "NVFP4 linear µs & achieved HBM GB/s (M=1..16); prefill TFLOP/s; % roofline"
+HBM_PEAK_GBPS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+ROTATE_BYTES = 1 << 30
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def weight_bytes(N, K):
+    return N * K // 2 + N * K // 16
+
+
+def linear_bytes(M, N, K):
+    """Algorithmic HBM bytes of one linear launch: packed weight + tensor scale + BF16
+    activations read once + fp32 output written once."""
+    return weight_bytes(N, K) + 4 + 2 * M * K + 4 * M * N
+
+
+class Timer:
+    """Times graph replays with HIP events on the current stream."""
+
+    def __init__(self):
+        self.a = torch.cuda.Event(enable_timing=True)
+        self.b = torch.cuda.Event(enable_timing=True)
+
+    def time(self, fn, reps):
+        torch.cuda.synchronize()
+        self.a.record()
+        for _ in range(reps):
+            fn()
+        self.b.record()
+        torch.cuda.synchronize()
+        return self.a.elapsed_time(self.b) / reps  # ms per fn()
+
+
+def capture(fn):
+    """Records fn's launches into a HIP graph (torch's capture on a side stream)."""
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()  # warm the allocator / library outside the capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def quantize_weight(nv, w, dev):
+    wd = torch.from_numpy(w).to(dev)
+    c, s, t = nv.quantize_act(wd, per_tensor=True)
+    del wd
+    return c, s, t
+
+
+def copies(c, s, n):
+    return [(c.clone(), s.clone()) for _ in range(n)]
+
+
+def to_bf16(xb, dev):
+    return torch.from_numpy(np.ascontiguousarray(xb).view(np.int16)).to(dev).view(torch.bfloat16)
+
+
+# ---------------------------------------------------------------------------------------
+def bench_decode_sweep(nv, dev, steps, warmup):
+    from synth import WORKLOADS, act_bf16, weight_f32
+    cfg = WORKLOADS["decode_sweep"]
+    N, K, Ms = cfg["N"], cfg["K"], cfg["Ms"]
+    c, s, t = quantize_weight(nv, weight_f32(cfg["w_seed"], N, K), dev)
+    R = max(len(Ms), math.ceil(ROTATE_BYTES / weight_bytes(N, K)))
+    R = len(Ms) * math.ceil(R / len(Ms))
+    W = copies(c, s, R)
+    xs = {M: to_bf16(act_bf16(cfg["x_seed_base"] + M, M, K), dev) for M in Ms}
+    ys = {M: torch.empty((M, N), dtype=torch.float32, device=dev) for M in Ms}
+    steps_per_graph = R // len(Ms)
+
+    def sweep_steps():
+        j = 0
+        for _ in range(steps_per_graph):
+            for M in Ms:
+                nv.linear(xs[M], W[j][0], W[j][1], t, out=ys[M])
+                j += 1
+
+    # eager reference for the replay check
+    ref = {M: nv.linear(xs[M], c, s, t).clone() for M in Ms}
+    g = capture(sweep_steps)
+    g.replay()
+    torch.cuda.synchronize()
+    for M in Ms:
+        assert torch.equal(ys[M], ref[M]), f"graph replay differs from eager at M={M}"
+    timer = Timer()
+    reps_w = max(1, math.ceil(warmup / steps_per_graph))
+    reps = max(1, math.ceil(steps / steps_per_graph))
+    timer.time(g.replay, reps_w)
+    ms_graph = timer.time(g.replay, reps)
+    ms_step = ms_graph / steps_per_graph
+    timed_steps = reps * steps_per_graph
+    step_bytes = sum(linear_bytes(M, N, K) for M in Ms)
+
+    # per-M launches (same kernel, one M at a time), for the per-bucket table
+    per_m = {}
+    for M in Ms:
+        def one_m(M=M):
+            for j in range(R):
+                nv.linear(xs[M], W[j][0], W[j][1], t, out=ys[M])
+        gm = capture(one_m)
+        timer.time(gm.replay, 1)
+        ms = timer.time(gm.replay, max(2, reps)) / R
+        b = linear_bytes(M, N, K)
+        per_m[str(M)] = {"us": round(ms * 1e3, 3), "GBps": round(b / (ms * 1e-3) / 1e9, 1),
+                         "frac_hbm": round(b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                         "bytes": b}
+        del gm
+    del g
+    return dict(N=N, K=K, Ms=Ms, R=R, ms_step=ms_step, step_bytes=step_bytes,
+                timed_steps=timed_steps, per_m=per_m, launches_per_step=len(Ms))
+
+
+def bench_single(nv, dev):
+    from synth import WORKLOADS, act_bf16, weight_f32
+    cfg = WORKLOADS["single_linear"]
+    M, N, K = cfg["M"], cfg["N"], cfg["K"]
+    c, s, t = quantize_weight(nv, weight_f32(cfg["w_seed"], N, K), dev)
+    R = math.ceil(ROTATE_BYTES / weight_bytes(N, K))
+    W = copies(c, s, R)
+    x = to_bf16(act_bf16(cfg["x_seed"], M, K), dev)
+    y = torch.empty((M, N), dtype=torch.float32, device=dev)
+
+    def run():
+        for j in range(R):
+            nv.linear(x, W[j][0], W[j][1], t, out=y)
+    g = capture(run)
+    timer = Timer()
+    timer.time(g.replay, 1)
+    ms = timer.time(g.replay, 3) / R
+    b = linear_bytes(M, N, K)
+    return {"workload": "M=1 K=2048 N=2048", "us": round(ms * 1e3, 3),
+            "GBps": round(b / (ms * 1e-3) / 1e9, 1), "bytes": b}
+
+
+def bench_prefill(nv, dev):
+    from synth import WORKLOADS, act_bf16, weight_f32
+    cfg = WORKLOADS["prefill"]
+    M, N, K = cfg["M"], cfg["N"], cfg["K"]
+    c, s, t = quantize_weight(nv, weight_f32(cfg["w_seed"], N, K), dev)
+    R = 8
+    W = copies(c, s, R)
+    x = to_bf16(act_bf16(cfg["x_seed"], M, K), dev)
+    y = torch.empty((M, N), dtype=torch.float32, device=dev)
+
+    def run():
+        for j in range(R):
+            nv.linear(x, W[j][0], W[j][1], t, out=y)
+    g = capture(run)
+    timer = Timer()
+    timer.time(g.replay, 1)
+    ms = timer.time(g.replay, 3) / R
+    flops = 2.0 * M * N * K
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"workload": "M=2048 K=4096 N=14336", "us": round(ms * 1e3, 2), "TFLOPs": round(tf, 1),
+            "frac_bf16_mfma": round(tf / BF16_PEAK_TFLOPS, 4), "flop": flops}
+
+
+def bench_w4a4(nv, dev):
+    from synth import WORKLOADS, act_bf16, weight_f32
+    cfg = WORKLOADS["w4a4"]
+    N, K = cfg["N"], cfg["K"]
+    c, s, t = quantize_weight(nv, weight_f32(cfg["w_seed"], N, K), dev)
+    R = math.ceil(ROTATE_BYTES / weight_bytes(N, K))
+    W = copies(c, s, R)
+    out = {}
+    timer = Timer()
+    for M in cfg["Ms"]:
+        x = to_bf16(act_bf16(cfg["x_seed_base"] + M, M, K), dev)
+        xc, xs_, xt = nv.quantize_act(x)
+        y = torch.empty((M, N), dtype=torch.float32, device=dev)
+        reps_in = R if M <= 16 else 8
+
+        def run():
+            for j in range(reps_in):
+                nv.quantize_act(x, codes=xc, scales=xs_, ts=xt)
+                nv.linear(xc, W[j][0], W[j][1], t, x_scales=xs_, x_ts=xt, out=y)
+        g = capture(run)
+        timer.time(g.replay, 1)
+        ms = timer.time(g.replay, 3) / reps_in
+        b = weight_bytes(N, K) + 4 + M * (2 * K + K // 2 + K // 16 + 4) + M * (K // 2 + K // 16 + 4) + 4 * M * N
+        fl = 2.0 * M * N * K
+        out[str(M)] = {"us_quantize_plus_linear": round(ms * 1e3, 3),
+                       "GBps": round(b / (ms * 1e-3) / 1e9, 1),
+                       "TFLOPs": round(fl / (ms * 1e-3) / 1e12, 2)}
+        del g
+    return out
+
+
+def bench_moe(nv, dev):
+    from synth import WORKLOADS, act_bf16, moe_expert_weights, moe_routes
+    cfg = WORKLOADS["moe_decode"]
+    E, T, k = cfg["E"], cfg["T"], cfg["top_k"]
+    gc, gs, gt, dc, ds, dt = [], [], [], [], [], []
+    for e in range(E):
+        gu, dn = moe_expert_weights(cfg["w_seed"], e, cfg["N_gu"], cfg["K_gu"], cfg["N_d"], cfg["K_d"])
+        c, s, t = quantize_weight(nv, gu, dev); gc.append(c); gs.append(s); gt.append(t)
+        c, s, t = quantize_weight(nv, dn, dev); dc.append(c); ds.append(s); dt.append(t)
+    sets = [(torch.stack(gc), torch.stack(gs), torch.cat(gt), torch.stack(dc), torch.stack(ds), torch.cat(dt))]
+    per_set = sum(x.numel() for x in sets[0][:2]) + sum(x.numel() for x in sets[0][3:5])
+    R = max(1, math.ceil(ROTATE_BYTES / per_set))
+    sets += [tuple(x.clone() for x in sets[0]) for _ in range(R - 1)]
+    ids, rw = moe_routes(cfg["route_seed"], T, E, k)
+    ids_d = torch.from_numpy(ids).to(dev)
+    rw_d = torch.from_numpy(rw).to(dev)
+    x = to_bf16(act_bf16(cfg["x_seed"], T, cfg["K_gu"]), dev)
+    a = torch.empty((T * k, cfg["N_gu"] // 2), dtype=torch.bfloat16, device=dev)
+    y = torch.empty((T, cfg["N_d"]), dtype=torch.float32, device=dev)
+    w1 = torch.empty(nv.grouped_workspace_size(T, k, cfg["N_gu"], cfg["K_gu"], E, nv.OUT_SWIGLU_BF16),
+                     dtype=torch.uint8, device=dev)
+    w2 = torch.empty(nv.grouped_workspace_size(T, k, cfg["N_d"], cfg["K_d"], E, nv.OUT_COMBINE),
+                     dtype=torch.uint8, device=dev)
+
+    def run():
+        for st in sets:
+            nv.grouped_linear(x, st[0], st[1], st[2], ids_d, out_mode=nv.OUT_SWIGLU_BF16, out=a,
+                              workspace=w1)
+            nv.grouped_linear(a, st[3], st[4], st[5], ids_d, topk_w=rw_d, out_mode=nv.OUT_COMBINE,
+                              rows_per_route=True, out=y, workspace=w2)
+    g = capture(run)
+    timer = Timer()
+    timer.time(g.replay, 1)
+    ms = timer.time(g.replay, 3) / R
+    D = len(np.unique(ids))
+    per_expert = weight_bytes(cfg["N_gu"], cfg["K_gu"]) + weight_bytes(cfg["N_d"], cfg["K_d"]) + 8
+    b = D * per_expert + T * cfg["K_gu"] * 2 + T * cfg["N_d"] * 4
+    return {"workload": "128 experts, gate_up 2048->1536 + down 768->2048, 16 tokens, top-8",
+            "distinct_experts": D, "us_layer": round(ms * 1e3, 2),
+            "GBps": round(b / (ms * 1e-3) / 1e9, 1), "frac_hbm": round(b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "bytes": b}
+
+
+def hbm_copy_probe(dev):
+    """Device-to-device copy of 1 GiB: measured read+write bandwidth of a plain copy."""
+    n = 1 << 29  # int16 elements = 1 GiB
+    a = torch.empty(n, dtype=torch.int16, device=dev)
+    b = torch.empty_like(a)
+    a.fill_(1)
+    timer = Timer()
+    timer.time(lambda: b.copy_(a), 2)
+    ms = timer.time(lambda: b.copy_(a), 5)
+    return round(2 * a.numel() * 2 / (ms * 1e-3) / 1e9, 1)
+
+
+def cpu_baseline(decode):
+    """The CPU oracle (as written for the tests) on the same decode sweep: dequantize the
+    weight, then the float64 linear for each M. Repeated until ~10 s of work."""
+    import oracle
+    from synth import WORKLOADS, act_bf16, weight_f32
+    cfg = WORKLOADS["decode_sweep"]
+    N, K = cfg["N"], cfg["K"]
+    o = oracle.Oracle()
+    oc, os_, ot = o.quantize(weight_f32(cfg["w_seed"], N, K), per_row=False)
+    xs = {M: act_bf16(cfg["x_seed_base"] + M, M, K) for M in cfg["Ms"]}
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        wdq = o.dequant(oc, os_, ot, per_row=False)
+        for M in cfg["Ms"]:
+            o.linear_f64(o.bf16_to_f64(xs[M]), wdq)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= 10.0 or reps >= 50:
+            break
+    per_step = el / reps
+    return {"value": round(decode["step_bytes"] / per_step / 1e9, 3), "unit": "GB/s",
+            "cores": o.num_threads(), "kind": "oracle",
+            "sample": f"full decode sweep (dequantize W 12288x4096, float64 linear for M=1,2,4,8,16) x{reps}, "
+                      f"{per_step:.2f} s per sweep on {o.num_threads()} OpenMP threads ({os.cpu_count()} host CPUs visible)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--only", choices=["all", "decode"], default="all")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--copy-probe", action="store_true", help="also time a 1 GiB device copy")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this library has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import nvfp4_block_scaled_linear_amd as nv
+    if not os.path.exists(nv.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    nv.load_library()
+
+    log("decode sweep ...")
+    d = bench_decode_sweep(nv, dev, args.steps, args.warmup)
+    value = d["step_bytes"] / (d["ms_step"] * 1e-3) / 1e9
+    achieved = value  # one kernel (the weight-streaming kernel) makes every launch of the step
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": d["timed_steps"],
+        "warmup": args.warmup,
+        "ms_per_step": round(d["ms_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "decode bucket sweep: NVFP4 linear K=4096 N=12288, one launch per "
+                               "M in {1,2,4,8,16} per step, BF16 activations, fp32 out; weight "
+                               f"rotated over {d['R']} copies ({d['R'] * weight_bytes(d['N'], d['K']) / 2**30:.2f} GiB) "
+                               "so every launch streams it from HBM",
+                   "global_batch": 31, "parallelism": "none (one GPU)"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "stream_dense (weight-streaming MFMA kernel)",
+                     "avg_launch_us": round(d["ms_step"] * 1e3 / d["launches_per_step"], 3),
+                     "bytes_per_launch_avg": d["step_bytes"] // d["launches_per_step"]},
+        "per_m": d["per_m"],
+    }
+    if args.only == "all":
+        log("single linear ...")
+        rec["single_linear"] = bench_single(nv, dev)
+        log("prefill ...")
+        rec["prefill"] = bench_prefill(nv, dev)
+        log("w4a4 ...")
+        rec["w4a4"] = bench_w4a4(nv, dev)
+        log("moe ...")
+        rec["moe"] = bench_moe(nv, dev)
+    if args.copy_probe or args.only == "all":
+        rec["hbm_copy_GBps"] = hbm_copy_probe(dev)
+    if not args.no_cpu:
+        log("cpu oracle baseline ...")
+        rec["cpu_baseline"] = cpu_baseline(d)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -12,6 +12,8 @@ using namespace nvfp4;
 namespace {
 
 constexpr int64_t kMaxDim = (int64_t)1 << 30;  // sizes must fit the kernels' int indices
+constexpr int64_t kMaxK = (int64_t)1 << 22;    // a 64-row weight block stays under 2^31 bytes
+constexpr int64_t kMaxBufferBytes = ((int64_t)1 << 31) - 1;  // 32-bit buffer offsets
 constexpr int kMaxExperts = 4096;               // route grouping keeps per-expert counters in LDS
 constexpr int kStreamMaxRows = 16;              // rows of one weight-streaming pass
 
@@ -43,7 +45,7 @@ nvfp4_status check_weight(const uint8_t* w_codes, const uint8_t* w_scales, const
 }
 
 nvfp4_status check_k(int64_t K) {
-  if (K <= 0 || K > kMaxDim || K % 32 != 0) return NVFP4_ERR_SHAPE;
+  if (K <= 0 || K > kMaxK || K % 32 != 0) return NVFP4_ERR_SHAPE;
   return NVFP4_OK;
 }
 
@@ -104,7 +106,7 @@ nvfp4_status nvfp4_linear(int32_t act_kind, const void* x, const uint8_t* x_scal
     StreamArgs a{};
     a.x = x; a.x_scales = x_scales; a.x_ts = x_ts; a.ldx = ldx;
     a.w_codes = w_codes; a.w_scales = w_scales; a.w_ts = w_ts;
-    a.N = N; a.K = K; a.y = y; a.ldy = ldy; a.M = (int32_t)M; a.apply_ts = 1;
+    a.N = N; a.K = K; a.y = y; a.ldy = ldy; a.M = (int32_t)M; a.apply_ts = 1; a.x_rows = M;
     return launch_status(launch_stream(a, act_kind, false, 1, s));
   }
   GemmArgs g{};
@@ -163,6 +165,11 @@ nvfp4_status nvfp4_grouped_linear(int32_t act_kind, const void* x, const uint8_t
   if (!aligned(workspace, 256)) return NVFP4_ERR_ALIGN;
   if ((st = check_act(act_kind, x, x_scales, x_ts, ldx, K)) != NVFP4_OK) return st;
   if ((st = check_weight(w_codes, w_scales, w_ts)) != NVFP4_OK) return st;
+  {
+    const int64_t xrows = rows_mode == NVFP4_ROWS_PER_TOKEN ? T : T * top_k;
+    const int64_t xbytes = act_kind == NVFP4_ACT_BF16 ? ((xrows - 1) * ldx + K) * 2 : xrows * (K / 2);
+    if (xbytes > kMaxBufferBytes) return NVFP4_ERR_SHAPE;
+  }
   if (!topk_ids || !y) return NVFP4_ERR_NULL;
   if (out_mode == NVFP4_OUT_COMBINE && !topk_w) return NVFP4_ERR_NULL;
   if (!aligned(topk_ids, 4) || (topk_w && !aligned(topk_w, 4)) || !aligned(y, 4) ||
@@ -190,8 +197,13 @@ nvfp4_status nvfp4_grouped_linear(int32_t act_kind, const void* x, const uint8_t
   a.N = N; a.K = K;
   a.offsets = ws.offsets; a.sorted = ws.sorted; a.active = ws.active; a.n_active = ws.n_active;
   a.rows_per_token = rows_mode == NVFP4_ROWS_PER_TOKEN ? 1 : 0;
+  a.x_rows = rows_mode == NVFP4_ROWS_PER_TOKEN ? T : T * top_k;
   a.top_k = top_k;
-  a.M = 0;
+  // rows per expert pass (sets of four): sized from the mean routes per active expert
+  {
+    const int64_t active = R < num_experts ? R : num_experts;
+    a.M = (int32_t)((R + active - 1) / active);
+  }
   if (out_mode == NVFP4_OUT_ROUTES) {
     // dropped routes must read as zero rows: clear y first (a fill kernel, capture-safe)
     a.y = static_cast<float*>(y); a.ldy = N; a.apply_ts = 1;

@@ -48,6 +48,22 @@ __device__ __forceinline__ u32x4 decode8(uint32_t codes, float s) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+// 4x4 transpose of dwords across the four 16-lane rows of a wave: lane (c, g) = c + 16g
+// enters holding dword j of 16-byte chunk g in v[j] and leaves holding dword g of chunk j
+// in v[j]. Two butterfly stages: v_permlane32_swap exchanges the upper lanes (rows 2, 3)
+// of its first operand with the lower lanes (rows 0, 1) of its second; v_permlane16_swap
+// exchanges odd rows of its first operand with even rows of its second.
+__device__ __forceinline__ void transpose4(u32x4& v) {
+  const auto a = __builtin_amdgcn_permlane32_swap(v[0], v[2], false, false);
+  const auto b = __builtin_amdgcn_permlane32_swap(v[1], v[3], false, false);
+  const auto c = __builtin_amdgcn_permlane16_swap(a[0], b[0], false, false);
+  const auto d = __builtin_amdgcn_permlane16_swap(a[1], b[1], false, false);
+  v[0] = c[0];
+  v[1] = c[1];
+  v[2] = d[0];
+  v[3] = d[1];
+}
+
 // ---------------------------------------------------------------------------------------
 // MFMA wrappers (BF16 in, fp32 accumulate). Lane layouts, checked on the hardware:
 //  16x16x32: lane l holds A[l%16][8*(l/16)+j], B[8*(l/16)+j][l%16] (j = 0..7) and

@@ -23,7 +23,8 @@ struct StreamArgs {
   // output fp32 [rows][ldy]
   float* y;
   int64_t ldy;
-  int32_t M;        // dense: number of rows (<= 16)
+  int64_t x_rows;   // rows in x (bounds the activation reads)
+  int32_t M;        // dense: number of rows (<= 16); grouped: rows per expert pass hint
   int32_t apply_ts; // multiply the accumulator by the weight's tensor scale
   // grouped form (NULL for dense)
   const int32_t* offsets;    // [E+1] route ranges per expert in `sorted`
@@ -36,6 +37,9 @@ struct StreamArgs {
 
 hipError_t launch_stream(const StreamArgs& a, int act_kind, bool grouped, int max_active,
                          hipStream_t stream);
+// the same with an explicit tile choice: tn 16-row tiles per workgroup, W waves splitting K
+hipError_t launch_stream_cfg(const StreamArgs& a, int act_kind, bool grouped, int max_active,
+                             int tn, int W, hipStream_t stream);
 
 struct GemmArgs {
   const void* x;

@@ -4,127 +4,258 @@
 // Each weight byte is read from HBM exactly once for all rows of the pass — the fix the
 // pages apply to multi-row verify (bloomery issue #565, section 4 "Round 1": a run of
 // several tokens dots each selected expert's rows for all its slots in one pass, PR
-// #808; several rows as one multi-column walk, PR #652) — and many loads are kept in
-// flight per lane (the m-column walk keeping eight chunks in flight, section 9, PR
-// #511).
+// #808; several rows as one multi-column walk, PR #652) — and several steps of loads
+// stay in flight per lane (the m-column walk keeping eight chunks in flight, section 9,
+// PR #511).
 //
-// gfx950 mapping. A workgroup owns 16*TN weight rows (n) and splits K over its waves;
-// within a wave the four 16-lane groups take four contiguous K ranges. Each lane streams
-// 16-byte code loads (32 nibbles of one row) plus the two E4M3 scale bytes that cover
-// them, decodes them in registers to exact BF16 (device.hpp), and feeds the 16x16x32 BF16
-// MFMA with the activation rows (padded to 16) as the A operand. Partial sums of the
-// waves meet in LDS and are added in a fixed order (no atomics), then scaled by the
-// tensor scale and stored as fp32.
+// gfx950 mapping: post-block-scaled 4x4x4 MFMAs.
+//  - The E2M1 codes decode *unscaled* to BF16 with v_cvt_scalef32_pk_bf16_fp4 at scale
+//    1.0 (exact, two values per instruction). Each group of four MFMAs covers exactly one
+//    16-value scale block, and its fp32 partial is multiplied by that block's E4M3 scale
+//    once (one FMA per output), so the scale never touches the per-element path.
+//  - v_mfma_f32_4x4x4_16b_bf16 runs 16 independent 4x4x4 products. Lane l = 4b + j
+//    (block b, column j) is weight row n = 4*(b % 4) + j of a 16-row tile at k-group
+//    g = l / 16, so a lane holds whole 16-k blocks of its own row: its 16-byte code load
+//    is 32 consecutive k, and the 16 lanes of a row group read 64 contiguous bytes of
+//    each row per instruction. The four blocks with the same g share their A (the
+//    activations): CBSZ = 2 broadcasts the A of block ABID of each group of four, so each
+//    lane loads only one 16-byte piece of activations per step (row j, piece b % 4).
+//  - Activation rows are padded to sets of four (R sets for M <= 4R); a workgroup owns
+//    16*TN weight rows and each of its W waves takes a contiguous run of 128-k steps of
+//    K, with a ring of kDepth steps of loads in flight per wave.
+//  - Loads are raw buffer loads: out-of-range offsets read as zero without touching
+//    memory, so bounds and predication need no branches (a branch around a load forces a
+//    wait for it at the join and serializes the stream).
+//  - Partial sums of the lane groups and waves meet in LDS and are added in a fixed order
+//    (no atomics), then scaled by the tensor scale and stored as fp32.
 #include "device.hpp"
 #include "kernels.hpp"
 
 namespace nvfp4 {
 namespace {
 
-constexpr int kUnroll = 4;  // 32-k pieces per lane whose loads are issued together
+constexpr int kDepth = 4;            // steps of loads in flight per wave
+constexpr uint32_t kOOB = 0x80000000u;
 
-template <int TN, int ACT>
-__device__ __forceinline__ void stream_pass(const StreamArgs& a, const uint8_t* wc,
-                                            const uint8_t* ws, int64_t n0, const void* xrow,
-                                            const uint8_t* xsrow, bool row_ok,
-                                            f32x4 (&acc)[TN]) {
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+
+// kOOB when chunk start `k` is at or past K (offsets stay below 2^31 otherwise)
+__device__ __forceinline__ uint32_t past(uint32_t K, uint32_t k) {
+  return ((K - 1u - k) >> 31) << 31;
+}
+
+template <int TN, int R, int ACT>
+struct StepBuf {
+  u32x4 w[TN];       // 32 codes of this lane's row (per tile)
+  uint32_t s[TN];    // the two E4M3 scales of those 32 codes
+  u32x4 x[R];        // BF16: this lane's 16-byte activation piece (per row set)
+  uint32_t xs[R];    // NVFP4 activations: the piece's scale byte (the piece is x[r][0])
+};
+
+// MFMA 4x4x4 over one 4-k slice: A from block ABID of each group of four blocks
+template <int ABID>
+__device__ __forceinline__ f32x4 mfma4(uint32_t a01, uint32_t a23, uint32_t b01, uint32_t b23,
+                                       f32x4 c) {
+  const uint32_t av[2] = {a01, a23};
+  const uint32_t bv[2] = {b01, b23};
+  return __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(__builtin_bit_cast(bf16x4, av),
+                                                __builtin_bit_cast(bf16x4, bv), c, 2, ABID, 0);
+}
+
+// Two BF16 values of byte SEL of `codes`, unscaled (exact)
+template <int SEL>
+__device__ __forceinline__ uint32_t cvt2(uint32_t codes) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, 1.0f, SEL));
+}
+
+// Descriptor offsets of this lane's activation row in each row set (kOOB for padding).
+struct RowMap {
+  uint32_t off[4];   // activation row
+  uint32_t soff[4];  // NVFP4 activations: scale row
+};
+
+// Row stride (bytes) of the tile's scales in LDS: K/16 plus 4, so the 16 rows a wave
+// reads together fall in different banks.
+__host__ __device__ __forceinline__ uint32_t lds_scale_stride(int64_t K) {
+  return (uint32_t)(K >> 4) + 4u;
+}
+
+template <int TN, int R, int ACT, bool SLDS>
+__device__ __forceinline__ void pass4(const StreamArgs& a, const uint8_t* wc, const uint8_t* ws,
+                                      int64_t n0, const RowMap& rm, uint8_t* lds_s,
+                                      f32x4 (&acc)[TN][R]) {
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // scalar: uniform guards
   const int W = blockDim.x >> 6;
-  const int col = lane & 15;
-  const int slot = wave * 4 + (lane >> 4);
-  const int64_t K = a.K;
-  const int Kc = (int)(K >> 5);  // 32-k pieces per row
-  const int S = 4 * W;
-  const int P = (Kc + S - 1) / S;
-  const int p_begin = slot * P;
-  const int64_t kb = K >> 1;
-  const int64_t sb = K >> 4;
+  const int g = lane >> 4;             // k-group of the lane (32 k of the 128-k step)
+  const int bp = (lane >> 2) & 3;      // block within the group: activation piece index
+  const int nl = 4 * bp + (lane & 3);  // weight row of the lane within a 16-row tile
+  const uint32_t K = (uint32_t)a.K;
+  const uint32_t kb = K >> 1, sb = K >> 4;
+  // Each wave takes a contiguous run of 128-k steps, so the two 64-byte halves of every
+  // 128-byte line of a row are requested by one wave in consecutive loads.
+  const int NS = (int)((K + 127u) >> 7);
+  const int per_wave = (NS + W - 1) / W;
+  const int first = wave * per_wave;
+  const int NSW = first < NS ? min(per_wave, NS - first) : 0;  // uniform over the wave
 
 #pragma unroll
-  for (int t = 0; t < TN; t++) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < TN; t++)
+#pragma unroll
+    for (int r = 0; r < R; r++) acc[t][r] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const uint8_t* wrow[TN];
-  const uint8_t* srow[TN];
-  bool nok[TN];
+  const int64_t rows_here = (a.N - n0) < 16 * TN ? (a.N - n0) : 16 * TN;
+  const auto wr = make_rsrc(wc + n0 * kb, (uint32_t)(rows_here * kb));
+  const auto sr = make_rsrc(ws + n0 * sb, (uint32_t)(rows_here * sb));
+  uint32_t wrow[TN], srow[TN];
 #pragma unroll
   for (int t = 0; t < TN; t++) {
-    const int64_t n = n0 + 16 * t + col;
-    nok[t] = n < a.N;
-    const int64_t nn = nok[t] ? n : 0;
-    wrow[t] = wc + nn * kb;
-    srow[t] = ws + nn * sb;
+    const bool ok = 16 * t + nl < rows_here;
+    wrow[t] = ok ? (uint32_t)((16 * t + nl) * kb) : kOOB;
+    srow[t] = ok ? (uint32_t)((16 * t + nl) * sb) : kOOB;
+  }
+  __amdgpu_buffer_rsrc_t xr, xsr;
+  if (ACT == 0) {
+    xr = make_rsrc(a.x, (uint32_t)(((a.x_rows - 1) * a.ldx + a.K) * 2));  // last row: K values
+    xsr = xr;
+  } else {
+    xr = make_rsrc(a.x, (uint32_t)(a.x_rows * kb));
+    xsr = make_rsrc(a.x_scales, (uint32_t)(a.x_rows * sb));
   }
 
-  for (int s0 = 0; s0 < P; s0 += kUnroll) {
-    u32x4 cw[kUnroll][TN];
-    uint32_t sc[kUnroll][TN];
-    u32x4 xa[kUnroll][ACT == 0 ? 4 : 1];
-    uint32_t xsc[kUnroll];
+  const uint32_t sls = lds_scale_stride(a.K);
+
+  // Step i of this wave. Every load is issued unconditionally; a step past the wave's
+  // last one and chunks past K get out-of-range offsets and read zeros. With SLDS the
+  // scales come from the tile's copy in LDS at compute time instead.
+  auto load = [&](int i, StepBuf<TN, R, ACT>& b) {
+    const uint32_t k0 = (uint32_t)((first + i) * 128);
+    const uint32_t step_out = i < NSW ? 0u : kOOB;  // uniform
+    const uint32_t kg = k0 + 32u * g;                // this lane's 32 weight k
+    const uint32_t out_g = step_out | past(K, kg);
 #pragma unroll
-    for (int u = 0; u < kUnroll; u++) {
-      const int piece = p_begin + s0 + u;
-      const bool pv = (s0 + u < P) && (piece < Kc);
+    for (int t = 0; t < TN; t++) {
+      b.w[t] = __builtin_amdgcn_raw_buffer_load_b128(wr, (wrow[t] + (kg >> 1)) | out_g, 0, 0);
+      if (SLDS) b.s[t] = kg;  // remembered for the LDS read
+      else b.s[t] = __builtin_amdgcn_raw_buffer_load_b16(sr, (srow[t] + (kg >> 4)) | out_g, 0, 0);
+    }
+    const uint32_t kp = kg + 8u * bp;  // this lane's activation piece: 8 k
+    const uint32_t out_p = step_out | past(K, kp);
 #pragma unroll
-      for (int t = 0; t < TN; t++) {
-        if (pv && nok[t]) {
-          cw[u][t] = *reinterpret_cast<const u32x4*>(wrow[t] + (int64_t)piece * 16);
-          sc[u][t] = *reinterpret_cast<const uint16_t*>(srow[t] + (int64_t)piece * 2);
-        } else {
-          cw[u][t] = u32x4{0u, 0u, 0u, 0u};
-          sc[u][t] = 0u;
-        }
-      }
+    for (int r = 0; r < R; r++) {
       if (ACT == 0) {
-#pragma unroll
-        for (int d = 0; d < (ACT == 0 ? 4 : 1); d++) {
-          xa[u][d] = (pv && row_ok)
-                         ? reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(xrow) +
-                                                          (int64_t)piece * 32)[d]
-                         : u32x4{0u, 0u, 0u, 0u};
-        }
-        xsc[u] = 0u;
+        b.x[r] = __builtin_amdgcn_raw_buffer_load_b128(xr, (rm.off[r] + 2u * kp) | out_p, 0, 0);
+        b.xs[r] = 0u;
       } else {
-        if (pv && row_ok) {
-          xa[u][0] = *reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(xrow) +
-                                                     (int64_t)piece * 16);
-          xsc[u] = *reinterpret_cast<const uint16_t*>(xsrow + (int64_t)piece * 2);
-        } else {
-          xa[u][0] = u32x4{0u, 0u, 0u, 0u};
-          xsc[u] = 0u;
-        }
+        b.x[r][0] = __builtin_amdgcn_raw_buffer_load_b32(xr, (rm.off[r] + (kp >> 1)) | out_p, 0, 0);
+        b.xs[r] = __builtin_amdgcn_raw_buffer_load_b8(xsr, (rm.soff[r] + (kp >> 4)) | out_p, 0, 0);
       }
     }
+  };
+
+  auto compute = [&](StepBuf<TN, R, ACT>& b) {
+    u32x4 A[R];
 #pragma unroll
-    for (int u = 0; u < kUnroll; u++) {
-      u32x4 A[4];
-      if (ACT == 0) {
+    for (int r = 0; r < R; r++) {
+      if (ACT == 0) A[r] = b.x[r];
+      else A[r] = decode8(b.x[r][0], e4m3_to_f32<0>(b.xs[r]));  // exact BF16 activations
+    }
 #pragma unroll
-        for (int d = 0; d < 4; d++) A[d] = xa[u][ACT == 0 ? d : 0];
-      } else {
-        const float xs0 = e4m3_to_f32<0>(xsc[u]);
-        const float xs1 = e4m3_to_f32<1>(xsc[u]);
-        A[0] = decode8(xa[u][0][0], xs0);
-        A[1] = decode8(xa[u][0][1], xs0);
-        A[2] = decode8(xa[u][0][2], xs1);
-        A[3] = decode8(xa[u][0][3], xs1);
+    for (int t = 0; t < TN; t++) {
+      uint32_t sc = b.s[t];
+      if (SLDS) {
+        // past-K chunks read a real scale here but their codes are zero
+        const uint32_t kg = b.s[t];
+        sc = *reinterpret_cast<const uint16_t*>(lds_s + (16 * t + nl) * sls + (kg >> 4));
+      }
+      const float s0 = e4m3_to_f32<0>(sc);
+      const float s1 = e4m3_to_f32<1>(sc);
+      // unscaled BF16 weights: dword d holds k = 8d .. 8d+7 of the lane's 32
+      uint32_t wb[16];
+#pragma unroll
+      for (int d = 0; d < 4; d++) {
+        wb[4 * d + 0] = cvt2<0>(b.w[t][d]);
+        wb[4 * d + 1] = cvt2<1>(b.w[t][d]);
+        wb[4 * d + 2] = cvt2<2>(b.w[t][d]);
+        wb[4 * d + 3] = cvt2<3>(b.w[t][d]);
       }
 #pragma unroll
-      for (int t = 0; t < TN; t++) {
-        const float s0v = e4m3_to_f32<0>(sc[u][t]);
-        const float s1v = e4m3_to_f32<1>(sc[u][t]);
-        acc[t] = mfma16(A[0], decode8(cw[u][t][0], s0v), acc[t]);
-        acc[t] = mfma16(A[1], decode8(cw[u][t][1], s0v), acc[t]);
-        acc[t] = mfma16(A[2], decode8(cw[u][t][2], s1v), acc[t]);
-        acc[t] = mfma16(A[3], decode8(cw[u][t][3], s1v), acc[t]);
+      for (int r = 0; r < R; r++) {
+        // scale block 0: k 0..15 of the lane's 32, pieces 0, 1 (suppliers bp = 0, 1)
+        f32x4 c = f32x4{0.f, 0.f, 0.f, 0.f};
+        c = mfma4<0>(A[r][0], A[r][1], wb[0], wb[1], c);
+        c = mfma4<0>(A[r][2], A[r][3], wb[2], wb[3], c);
+        c = mfma4<1>(A[r][0], A[r][1], wb[4], wb[5], c);
+        c = mfma4<1>(A[r][2], A[r][3], wb[6], wb[7], c);
+#pragma unroll
+        for (int q = 0; q < 4; q++) acc[t][r][q] = __builtin_fmaf(s0, c[q], acc[t][r][q]);
+        // scale block 1: k 16..31, pieces 2, 3
+        c = f32x4{0.f, 0.f, 0.f, 0.f};
+        c = mfma4<2>(A[r][0], A[r][1], wb[8], wb[9], c);
+        c = mfma4<2>(A[r][2], A[r][3], wb[10], wb[11], c);
+        c = mfma4<3>(A[r][0], A[r][1], wb[12], wb[13], c);
+        c = mfma4<3>(A[r][2], A[r][3], wb[14], wb[15], c);
+#pragma unroll
+        for (int q = 0; q < 4; q++) acc[t][r][q] = __builtin_fmaf(s1, c[q], acc[t][r][q]);
       }
+    }
+  };
+
+  // With SLDS the workgroup first copies its tile's scale rows (one contiguous block of
+  // rows_here * K/16 bytes) into LDS with 16-byte loads; the weight ring is issued before
+  // the copy is waited on, so the two latencies overlap.
+  constexpr int kScaleRegs = 4;  // 16-byte scale chunks per thread held in flight
+  u32x4 sreg[kScaleRegs];
+  const uint32_t s_chunks = (uint32_t)((rows_here * sb + 15) >> 4);
+  const uint32_t chunks_per_row = sb >> 4;  // SLDS requires K % 256 == 0
+  if (SLDS) {
+#pragma unroll
+    for (int q = 0; q < kScaleRegs; q++) {
+      const uint32_t cidx = threadIdx.x + q * blockDim.x;
+      sreg[q] = __builtin_amdgcn_raw_buffer_load_b128(sr, cidx < s_chunks ? cidx * 16u : kOOB, 0, 0);
+    }
+  }
+  StepBuf<TN, R, ACT> buf[kDepth];
+#pragma unroll
+  for (int j = 0; j < kDepth; j++) load(j, buf[j]);
+  if (SLDS) {
+    // Chunks past the tile go to the spare 16 bytes after the scale rows, so the stores
+    // need no branch (a branch would make the wave wait for every load in flight).
+    const uint32_t spare = 16u * TN * sls;
+    auto put = [&](uint32_t cidx, u32x4 v) {
+      const uint32_t row = cidx / chunks_per_row, col = (cidx % chunks_per_row) * 16;
+      const uint32_t at = cidx < s_chunks ? row * sls + col : spare;
+      uint32_t* d = reinterpret_cast<uint32_t*>(lds_s + at);
+      d[0] = v[0];
+      d[1] = v[1];
+      d[2] = v[2];
+      d[3] = v[3];
+    };
+#pragma unroll
+    for (int q = 0; q < kScaleRegs; q++) put(threadIdx.x + q * blockDim.x, sreg[q]);
+    // tiles with more chunks than the prefetch holds copy the rest directly
+    for (uint32_t cidx = threadIdx.x + kScaleRegs * blockDim.x; cidx < s_chunks; cidx += blockDim.x)
+      put(cidx, __builtin_amdgcn_raw_buffer_load_b128(sr, cidx * 16u, 0, 0));
+    __syncthreads();
+  }
+  for (int i0 = 0; i0 < NSW; i0 += kDepth) {
+#pragma unroll
+    for (int j = 0; j < kDepth; j++) {
+      if (i0 + j < NSW) compute(buf[j]);
+      load(i0 + j + kDepth, buf[j]);
     }
   }
 }
 
-// Adds the waves' partial tiles in wave order and hands each (row, n, sum) to `store`.
-template <int TN, typename Store>
-__device__ __forceinline__ void reduce_store(const f32x4 (&acc)[TN], float* red, int64_t n0,
+// Adds the partials of the four k-groups and of the waves in a fixed order and hands each
+// (x row m, weight row n, sum) to `store`. acc[t][r][q] is x row 4r + q, weight row
+// 16t + nl. LDS: red[wave][t][r][lane][q].
+template <int TN, int R, typename Store>
+__device__ __forceinline__ void reduce_store(const f32x4 (&acc)[TN][R], float* red, int64_t n0,
                                              Store store) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -132,47 +263,64 @@ __device__ __forceinline__ void reduce_store(const f32x4 (&acc)[TN], float* red,
 #pragma unroll
   for (int t = 0; t < TN; t++)
 #pragma unroll
-    for (int r = 0; r < 4; r++) red[((wave * TN + t) * 4 + r) * 64 + lane] = acc[t][r];
+    for (int r = 0; r < R; r++)
+      *reinterpret_cast<f32x4*>(red + (((wave * TN + t) * R + r) * 64 + lane) * 4) = acc[t][r];
   __syncthreads();
-  for (int o = threadIdx.x; o < TN * 256; o += blockDim.x) {
-    const int t = o >> 8, mm = (o >> 4) & 15, cc = o & 15;
-    const int src = cc + 16 * (mm >> 2), r = mm & 3;
+  // one output per (t, r, q, nl)
+  for (int o = threadIdx.x; o < TN * R * 64; o += blockDim.x) {
+    const int nl = o & 15, q = (o >> 4) & 3, r = (o >> 6) % R, t = (o >> 6) / R;
+    const int lane0 = 4 * (nl >> 2) + (nl & 3);  // the group-0 lane holding row nl
     float s = 0.f;
-    for (int w = 0; w < W; w++) s += red[((w * TN + t) * 4 + r) * 64 + src];
-    store(mm, n0 + 16 * t + cc, s);
+    for (int w = 0; w < W; w++)
+#pragma unroll
+      for (int gg = 0; gg < 4; gg++)
+        s += red[(((w * TN + t) * R + r) * 64 + lane0 + 16 * gg) * 4 + q];
+    store(4 * r + q, n0 + 16 * t + nl, s);
   }
   __syncthreads();
 }
 
-template <int TN, int ACT>
+// bytes of LDS the tile's scales take (0 without SLDS), rounded to 16
+__host__ __device__ __forceinline__ uint32_t lds_scale_bytes(int TN, int64_t K, bool slds) {
+  return slds ? ((16u * TN * lds_scale_stride(K) + 31u) & ~15u) : 0u;  // + 16 spare bytes
+}
+
+template <int TN, int R, int ACT, bool SLDS>
 __global__ __launch_bounds__(512) void stream_dense(StreamArgs a) {
-  extern __shared__ float red[];
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  uint8_t* lds_s = lds;
+  float* red = reinterpret_cast<float*>(lds + lds_scale_bytes(TN, a.K, SLDS));
   const int64_t n0 = (int64_t)blockIdx.x * 16 * TN;
-  const int m = threadIdx.x & 15;
-  const bool row_ok = m < a.M;
-  const int mr = row_ok ? m : 0;
-  const void* xrow;
-  const uint8_t* xsrow = nullptr;
-  if (ACT == 0) {
-    xrow = static_cast<const uint16_t*>(a.x) + (int64_t)mr * a.ldx;
-  } else {
-    xrow = static_cast<const uint8_t*>(a.x) + (int64_t)mr * (a.K >> 1);
-    xsrow = a.x_scales + (int64_t)mr * (a.K >> 4);
+  const int i = threadIdx.x & 3;  // the x row this lane supplies within a set of four
+  RowMap rm;
+#pragma unroll
+  for (int r = 0; r < 4; r++) {
+    const int m = 4 * r + i;
+    const bool ok = m < a.M;
+    if (ACT == 0) {
+      rm.off[r] = ok ? (uint32_t)(m * a.ldx * 2) : kOOB;
+      rm.soff[r] = kOOB;
+    } else {
+      rm.off[r] = ok ? (uint32_t)(m * (a.K >> 1)) : kOOB;
+      rm.soff[r] = ok ? (uint32_t)(m * (a.K >> 4)) : kOOB;
+    }
   }
-  f32x4 acc[TN];
-  stream_pass<TN, ACT>(a, a.w_codes, a.w_scales, n0, xrow, xsrow, row_ok, acc);
+  f32x4 acc[TN][R];
+  pass4<TN, R, ACT, SLDS>(a, a.w_codes, a.w_scales, n0, rm, lds_s, acc);
   const float ts = a.apply_ts ? a.w_ts[0] : 1.0f;
-  reduce_store<TN>(acc, red, n0, [&](int mm, int64_t n, float s) {
-    if (mm < a.M && n < a.N) {
-      const float f = (ACT == 0) ? ts : a.x_ts[mm] * ts;
-      a.y[(int64_t)mm * a.ldy + n] = s * f;
+  reduce_store<TN, R>(acc, red, n0, [&](int m, int64_t n, float s) {
+    if (m < a.M && n < a.N) {
+      const float f = (ACT == 0) ? ts : a.x_ts[m] * ts;
+      a.y[(int64_t)m * a.ldy + n] = s * f;
     }
   });
 }
 
-template <int TN, int ACT>
+template <int R, int ACT, bool SLDS>
 __global__ __launch_bounds__(512) void stream_grouped(StreamArgs a) {
-  extern __shared__ float red[];
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  uint8_t* lds_s = lds;
+  float* red = reinterpret_cast<float*>(lds + lds_scale_bytes(1, a.K, SLDS));
   const int slot = blockIdx.y;
   if (slot >= *a.n_active) return;  // uniform over the workgroup
   const int e = a.active[slot];
@@ -180,26 +328,31 @@ __global__ __launch_bounds__(512) void stream_grouped(StreamArgs a) {
   const uint8_t* wc = a.w_codes + (int64_t)e * a.N * (a.K >> 1);
   const uint8_t* ws = a.w_scales + (int64_t)e * a.N * (a.K >> 4);
   const float ts = a.apply_ts ? a.w_ts[e] : 1.0f;
-  const int64_t n0 = (int64_t)blockIdx.x * 16 * TN;
-  for (int c0 = beg; c0 < end; c0 += 16) {
-    const int rows = min(16, end - c0);
-    const int m = threadIdx.x & 15;
-    const bool row_ok = m < rows;
-    const int r = a.sorted[c0 + (row_ok ? m : 0)];
-    const int64_t xr = a.rows_per_token ? r / a.top_k : r;
-    const void* xrow;
-    const uint8_t* xsrow = nullptr;
-    if (ACT == 0) {
-      xrow = static_cast<const uint16_t*>(a.x) + xr * a.ldx;
-    } else {
-      xrow = static_cast<const uint8_t*>(a.x) + xr * (a.K >> 1);
-      xsrow = a.x_scales + xr * (a.K >> 4);
+  const int64_t n0 = (int64_t)blockIdx.x * 16;
+  const int i = threadIdx.x & 3;
+  for (int c0 = beg; c0 < end; c0 += 4 * R) {
+    const int rows = min(4 * R, end - c0);
+    RowMap rm;
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+      const int m = 4 * r + i;
+      const bool ok = r < R && m < rows;
+      const int route = a.sorted[c0 + (ok ? m : 0)];
+      const int64_t xrow = a.rows_per_token ? route / a.top_k : route;
+      if (ACT == 0) {
+        rm.off[r] = ok ? (uint32_t)(xrow * a.ldx * 2) : kOOB;
+        rm.soff[r] = kOOB;
+      } else {
+        rm.off[r] = ok ? (uint32_t)(xrow * (a.K >> 1)) : kOOB;
+        rm.soff[r] = ok ? (uint32_t)(xrow * (a.K >> 4)) : kOOB;
+      }
     }
-    f32x4 acc[TN];
-    stream_pass<TN, ACT>(a, wc, ws, n0, xrow, xsrow, row_ok, acc);
-    reduce_store<TN>(acc, red, n0, [&](int mm, int64_t n, float s) {
-      if (mm < rows && n < a.N) {
-        const int rr = a.sorted[c0 + mm];
+    f32x4 acc[1][R];
+    if (SLDS && c0 != beg) __syncthreads();  // the previous pass's scale reads are done
+    pass4<1, R, ACT, SLDS>(a, wc, ws, n0, rm, lds_s, acc);
+    reduce_store<1, R>(acc, red, n0, [&](int m, int64_t n, float s) {
+      if (m < rows && n < a.N) {
+        const int rr = a.sorted[c0 + m];
         float f = ts;
         if (ACT != 0) {
           const int64_t xrr = a.rows_per_token ? rr / a.top_k : rr;
@@ -211,19 +364,61 @@ __global__ __launch_bounds__(512) void stream_grouped(StreamArgs a) {
   }
 }
 
-template <int TN, int ACT>
-hipError_t launch_tn(const StreamArgs& a, bool grouped, int max_active, int W,
-                     hipStream_t stream) {
-  const dim3 block(64 * W);
-  const size_t lds = (size_t)W * TN * 4 * 64 * sizeof(float);
+template <int TN, int R, int ACT>
+hipError_t launch_dense(const StreamArgs& a, int W, bool slds, hipStream_t stream) {
+  const size_t lds = lds_scale_bytes(TN, a.K, slds) + (size_t)W * TN * R * 64 * 4 * sizeof(float);
   const int64_t groups = (a.N + 16 * TN - 1) / (16 * TN);
-  if (grouped) {
-    hipLaunchKernelGGL((stream_grouped<TN, ACT>), dim3((uint32_t)groups, (uint32_t)max_active),
-                       block, lds, stream, a);
-  } else {
-    hipLaunchKernelGGL((stream_dense<TN, ACT>), dim3((uint32_t)groups), block, lds, stream, a);
-  }
+  if (slds)
+    hipLaunchKernelGGL((stream_dense<TN, R, ACT, true>), dim3((uint32_t)groups), dim3(64 * W), lds,
+                       stream, a);
+  else
+    hipLaunchKernelGGL((stream_dense<TN, R, ACT, false>), dim3((uint32_t)groups), dim3(64 * W),
+                       lds, stream, a);
   return hipGetLastError();
+}
+
+template <int R, int ACT>
+hipError_t launch_grouped(const StreamArgs& a, int max_active, int W, bool slds,
+                          hipStream_t stream) {
+  const size_t lds = lds_scale_bytes(1, a.K, slds) + (size_t)W * R * 64 * 4 * sizeof(float);
+  const int64_t groups = (a.N + 15) / 16;
+  if (slds)
+    hipLaunchKernelGGL((stream_grouped<R, ACT, true>), dim3((uint32_t)groups, (uint32_t)max_active),
+                       dim3(64 * W), lds, stream, a);
+  else
+    hipLaunchKernelGGL((stream_grouped<R, ACT, false>),
+                       dim3((uint32_t)groups, (uint32_t)max_active), dim3(64 * W), lds, stream, a);
+  return hipGetLastError();
+}
+
+template <int TN, int ACT>
+hipError_t dense_r(const StreamArgs& a, int R, int W, bool slds, hipStream_t stream) {
+  switch (R) {
+    case 1: return launch_dense<TN, 1, ACT>(a, W, slds, stream);
+    case 2: return launch_dense<TN, 2, ACT>(a, W, slds, stream);
+    case 3: return launch_dense<TN, 3, ACT>(a, W, slds, stream);
+    case 4: return launch_dense<TN, 4, ACT>(a, W, slds, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int ACT>
+hipError_t dense_tn(const StreamArgs& a, int tn, int R, int W, bool slds, hipStream_t stream) {
+  switch (tn) {
+    case 1: return dense_r<1, ACT>(a, R, W, slds, stream);
+    case 2: return dense_r<2, ACT>(a, R, W, slds, stream);
+    case 3: return dense_r<3, ACT>(a, R, W, slds, stream);
+    case 4: return dense_r<4, ACT>(a, R, W, slds, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// The scale copy needs whole 16-byte chunks per row (K % 256 == 0; then every tile's and
+// expert's scale block starts 16-byte aligned when the scales do) and a modest LDS
+// footprint.
+bool use_lds_scales(const StreamArgs& a, int tn) {
+  if (a.K % 256 != 0 || (uintptr_t)a.w_scales % 16 != 0) return false;
+  return lds_scale_bytes(tn, a.K, true) <= 32768;
 }
 
 // Picks 16-row tiles per workgroup so that whole rounds of workgroups fill the 256 CUs:
@@ -231,7 +426,7 @@ hipError_t launch_tn(const StreamArgs& a, bool grouped, int max_active, int W,
 int pick_tn(int64_t N) {
   int best = 1;
   int64_t best_cost = -1;
-  for (int tn = 1; tn <= 4; tn++) {
+  for (int tn : {1, 2, 4}) {
     const int64_t groups = (N + 16 * tn - 1) / (16 * tn);
     const int64_t cost = ((groups + 255) / 256) * tn;
     if (best_cost < 0 || cost <= best_cost) {
@@ -244,25 +439,34 @@ int pick_tn(int64_t N) {
 
 }  // namespace
 
+hipError_t launch_stream_cfg(const StreamArgs& a, int act_kind, bool grouped, int max_active,
+                             int tn, int W, hipStream_t stream) {
+  if (W < 1 || W > 8) return hipErrorInvalidValue;
+  const bool slds = use_lds_scales(a, grouped ? 1 : tn);
+  if (grouped) {
+    // rows of one expert pass in sets of four: one set covers decode-sized loads
+    const int R = a.M > 0 ? (a.M + 3) / 4 : 1;
+    switch (R) {
+      case 1: return act_kind == 0 ? launch_grouped<1, 0>(a, max_active, W, slds, stream)
+                                   : launch_grouped<1, 1>(a, max_active, W, slds, stream);
+      case 2: return act_kind == 0 ? launch_grouped<2, 0>(a, max_active, W, slds, stream)
+                                   : launch_grouped<2, 1>(a, max_active, W, slds, stream);
+      default: return act_kind == 0 ? launch_grouped<4, 0>(a, max_active, W, slds, stream)
+                                    : launch_grouped<4, 1>(a, max_active, W, slds, stream);
+    }
+  }
+  const int R = (a.M + 3) / 4;
+  return act_kind == 0 ? dense_tn<0>(a, tn, R, W, slds, stream)
+                       : dense_tn<1>(a, tn, R, W, slds, stream);
+}
+
 hipError_t launch_stream(const StreamArgs& a, int act_kind, bool grouped, int max_active,
                          hipStream_t stream) {
-  const int64_t Kc = a.K / 32;
-  int W = (int)((Kc + 15) / 16);
-  W = W < 1 ? 1 : (W > 8 ? 8 : W);
+  const int64_t NS = (a.K + 127) / 128;  // 128-k steps per row
+  int W = (int)((NS + 7) / 8);           // about 8 steps per wave
+  W = W < 1 ? 1 : (W > 4 ? 4 : W);
   const int tn = grouped ? 1 : pick_tn(a.N);
-#define NVFP4_TN_CASE(TNV)                                                       \
-  case TNV:                                                                      \
-    return act_kind == 0 ? launch_tn<TNV, 0>(a, grouped, max_active, W, stream)  \
-                         : launch_tn<TNV, 1>(a, grouped, max_active, W, stream);
-  switch (tn) {
-    NVFP4_TN_CASE(1)
-    NVFP4_TN_CASE(2)
-    NVFP4_TN_CASE(3)
-    NVFP4_TN_CASE(4)
-    default:
-      return hipErrorInvalidValue;
-  }
-#undef NVFP4_TN_CASE
+  return launch_stream_cfg(a, act_kind, grouped, max_active, tn, W, stream);
 }
 
 }  // namespace nvfp4

@@ -205,7 +205,7 @@ void oracle_dequant(const uint8_t* codes, const uint8_t* scales, const float* ts
  * bound[m][n] = sum_k |x[m][k] * w[n][k]| (the scale of the accepted error). */
 void oracle_linear(const double* x, int64_t M, const double* w, int64_t N, int64_t K,
                    double* y, double* bound) {
-#pragma omp parallel for schedule(dynamic, 1)
+#pragma omp parallel for collapse(2) schedule(static)
   for (int64_t m = 0; m < M; m++) {
     for (int64_t n = 0; n < N; n++) {
       double s = 0.0, b = 0.0;
