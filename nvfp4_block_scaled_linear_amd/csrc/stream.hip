@@ -16,13 +16,19 @@
 //  - v_mfma_f32_4x4x4_16b_bf16 runs 16 independent 4x4x4 products. Lane l = 4b + j
 //    (block b, column j) is weight row n = 4*(b % 4) + j of a 16-row tile at k-group
 //    g = l / 16, so a lane holds whole 16-k blocks of its own row: its 16-byte code load
-//    is 32 consecutive k, and the 16 lanes of a row group read 64 contiguous bytes of
-//    each row per instruction. The four blocks with the same g share their A (the
+//    is 32 consecutive k. The four blocks with the same g share their A (the
 //    activations): CBSZ = 2 broadcasts the A of block ABID of each group of four, so each
-//    lane loads only one 16-byte piece of activations per step (row j, piece b % 4).
+//    lane supplies one 16-byte piece of activations per step (row j, piece b % 4).
+//  - Memory requests are shaped for the vector L1, which is the narrow point of this
+//    stream: each wave takes a contiguous run of 128-k steps, so the two 64-byte halves
+//    of every 128-byte weight line are requested by one wave in consecutive loads, and
+//    activations are loaded row-contiguous (16 lanes read 256 bytes of one row) and
+//    moved into the operand layout above through a small wave-private LDS buffer.
+//  - The workgroup's scale rows are one contiguous block; it is copied into LDS once
+//    with 16-byte loads and each lane reads its two scale bytes from there.
 //  - Activation rows are padded to sets of four (R sets for M <= 4R); a workgroup owns
-//    16*TN weight rows and each of its W waves takes a contiguous run of 128-k steps of
-//    K, with a ring of kDepth steps of loads in flight per wave.
+//    16*TN weight rows and W waves, with a ring of kDepth steps of loads in flight per
+//    wave.
 //  - Loads are raw buffer loads: out-of-range offsets read as zero without touching
 //    memory, so bounds and predication need no branches (a branch around a load forces a
 //    wait for it at the join and serializes the stream).
@@ -36,6 +42,11 @@ namespace {
 
 constexpr int kDepth = 4;            // steps of loads in flight per wave
 constexpr uint32_t kOOB = 0x80000000u;
+// Activation transpose buffer: one 16-byte piece per lane, rows of 16 pieces padded to
+// 288 bytes so that both the row-contiguous writes and the operand-layout reads are free
+// of bank conflicts.
+constexpr uint32_t kXRow = 288;
+constexpr uint32_t kXSet = 4 * kXRow;  // one set of four activation rows
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
@@ -51,9 +62,8 @@ __device__ __forceinline__ uint32_t past(uint32_t K, uint32_t k) {
 template <int TN, int R, int ACT>
 struct StepBuf {
   u32x4 w[TN];       // 32 codes of this lane's row (per tile)
-  uint32_t s[TN];    // the two E4M3 scales of those 32 codes
-  u32x4 x[R];        // BF16: this lane's 16-byte activation piece (per row set)
-  uint32_t xs[R];    // NVFP4 activations: the piece's scale byte (the piece is x[r][0])
+  u32x4 x[R];        // BF16: 8 k of activation row 4r + lane/16 at k0 + 8*(lane%16);
+                     // NVFP4: x[r][0] the same piece as 8 codes, x[r][1] its scale byte
 };
 
 // MFMA 4x4x4 over one 4-k slice: A from block ABID of each group of four blocks
@@ -72,7 +82,8 @@ __device__ __forceinline__ uint32_t cvt2(uint32_t codes) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, 1.0f, SEL));
 }
 
-// Descriptor offsets of this lane's activation row in each row set (kOOB for padding).
+// Descriptor offsets of this lane's activation row (row 4r + lane/16) in each row set
+// (kOOB for padding rows).
 struct RowMap {
   uint32_t off[4];   // activation row
   uint32_t soff[4];  // NVFP4 activations: scale row
@@ -84,20 +95,32 @@ __host__ __device__ __forceinline__ uint32_t lds_scale_stride(int64_t K) {
   return (uint32_t)(K >> 4) + 4u;
 }
 
+// LDS bytes of the tile's scales (0 without SLDS): rows, 16 spare bytes, rounded to 16
+__host__ __device__ __forceinline__ uint32_t lds_scale_bytes(int TN, int64_t K, bool slds) {
+  return slds ? ((16u * TN * lds_scale_stride(K) + 31u) & ~15u) : 0u;
+}
+
+// LDS layout of a workgroup: [scales | transpose buffers of the W waves] during the
+// stream, then the reduction buffer over the same bytes.
+__host__ __device__ __forceinline__ size_t lds_bytes(int TN, int R, int W, int64_t K, bool slds) {
+  const size_t stream = lds_scale_bytes(TN, K, slds) + (size_t)W * R * kXSet;
+  const size_t red = (size_t)W * TN * R * 64 * 4 * sizeof(float);
+  return stream > red ? stream : red;
+}
+
 template <int TN, int R, int ACT, bool SLDS>
 __device__ __forceinline__ void pass4(const StreamArgs& a, const uint8_t* wc, const uint8_t* ws,
-                                      int64_t n0, const RowMap& rm, uint8_t* lds_s,
+                                      int64_t n0, const RowMap& rm, uint8_t* lds,
                                       f32x4 (&acc)[TN][R]) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // scalar: uniform guards
   const int W = blockDim.x >> 6;
   const int g = lane >> 4;             // k-group of the lane (32 k of the 128-k step)
   const int bp = (lane >> 2) & 3;      // block within the group: activation piece index
+  const int q = lane & 15;             // activation piece loaded by the lane (row-contiguous)
   const int nl = 4 * bp + (lane & 3);  // weight row of the lane within a 16-row tile
   const uint32_t K = (uint32_t)a.K;
   const uint32_t kb = K >> 1, sb = K >> 4;
-  // Each wave takes a contiguous run of 128-k steps, so the two 64-byte halves of every
-  // 128-byte line of a row are requested by one wave in consecutive loads.
   const int NS = (int)((K + 127u) >> 7);
   const int per_wave = (NS + W - 1) / W;
   const int first = wave * per_wave;
@@ -127,50 +150,70 @@ __device__ __forceinline__ void pass4(const StreamArgs& a, const uint8_t* wc, co
     xsr = make_rsrc(a.x_scales, (uint32_t)(a.x_rows * sb));
   }
 
+  uint8_t* lds_s = lds;
+  uint8_t* xbuf = lds + lds_scale_bytes(TN, a.K, SLDS) + (uint32_t)wave * R * kXSet;
   const uint32_t sls = lds_scale_stride(a.K);
+  const uint32_t xw = kXRow * g + 16u * q;                 // this lane's piece (write)
+  const uint32_t xrd = kXRow * (lane & 3) + 16u * (4 * g + bp);  // operand piece (read)
 
   // Step i of this wave. Every load is issued unconditionally; a step past the wave's
   // last one and chunks past K get out-of-range offsets and read zeros. With SLDS the
-  // scales come from the tile's copy in LDS at compute time instead.
-  auto load = [&](int i, StepBuf<TN, R, ACT>& b) {
+  // scale offset is kept for the LDS read at compute time.
+  uint32_t kstep[kDepth];
+  auto load = [&](int i, StepBuf<TN, R, ACT>& b, uint32_t& kg_out) {
     const uint32_t k0 = (uint32_t)((first + i) * 128);
     const uint32_t step_out = i < NSW ? 0u : kOOB;  // uniform
     const uint32_t kg = k0 + 32u * g;                // this lane's 32 weight k
     const uint32_t out_g = step_out | past(K, kg);
+    kg_out = kg;
 #pragma unroll
-    for (int t = 0; t < TN; t++) {
+    for (int t = 0; t < TN; t++)
       b.w[t] = __builtin_amdgcn_raw_buffer_load_b128(wr, (wrow[t] + (kg >> 1)) | out_g, 0, 0);
-      if (SLDS) b.s[t] = kg;  // remembered for the LDS read
-      else b.s[t] = __builtin_amdgcn_raw_buffer_load_b16(sr, (srow[t] + (kg >> 4)) | out_g, 0, 0);
-    }
-    const uint32_t kp = kg + 8u * bp;  // this lane's activation piece: 8 k
+    const uint32_t kp = k0 + 8u * q;  // this lane's activation piece: 8 k
     const uint32_t out_p = step_out | past(K, kp);
 #pragma unroll
     for (int r = 0; r < R; r++) {
       if (ACT == 0) {
         b.x[r] = __builtin_amdgcn_raw_buffer_load_b128(xr, (rm.off[r] + 2u * kp) | out_p, 0, 0);
-        b.xs[r] = 0u;
       } else {
         b.x[r][0] = __builtin_amdgcn_raw_buffer_load_b32(xr, (rm.off[r] + (kp >> 1)) | out_p, 0, 0);
-        b.xs[r] = __builtin_amdgcn_raw_buffer_load_b8(xsr, (rm.soff[r] + (kp >> 4)) | out_p, 0, 0);
+        b.x[r][1] = __builtin_amdgcn_raw_buffer_load_b8(xsr, (rm.soff[r] + (kp >> 4)) | out_p, 0, 0);
       }
     }
   };
+  // without SLDS: the two scale bytes of each tile straight from memory, per ring slot
+  uint32_t sreg_fallback[kDepth][TN];
+  auto load_scales = [&](int i, int slot) {
+    if (SLDS) return;
+    const uint32_t k0 = (uint32_t)((first + i) * 128);
+    const uint32_t step_out = i < NSW ? 0u : kOOB;
+    const uint32_t kg = k0 + 32u * g;
+    const uint32_t out_g = step_out | past(K, kg);
+#pragma unroll
+    for (int t = 0; t < TN; t++)
+      sreg_fallback[slot][t] =
+          __builtin_amdgcn_raw_buffer_load_b16(sr, (srow[t] + (kg >> 4)) | out_g, 0, 0);
+  };
 
-  auto compute = [&](StepBuf<TN, R, ACT>& b) {
+  auto compute = [&](StepBuf<TN, R, ACT>& b, uint32_t kg, int slot) {
+    // activations: row-contiguous pieces -> LDS -> operand layout
     u32x4 A[R];
 #pragma unroll
     for (int r = 0; r < R; r++) {
-      if (ACT == 0) A[r] = b.x[r];
-      else A[r] = decode8(b.x[r][0], e4m3_to_f32<0>(b.xs[r]));  // exact BF16 activations
+      u32x4 v = b.x[r];
+      if (ACT != 0) v = decode8(b.x[r][0], e4m3_to_f32<0>(b.x[r][1]));  // exact BF16
+      *reinterpret_cast<u32x4*>(xbuf + r * kXSet + xw) = v;
     }
 #pragma unroll
+    for (int r = 0; r < R; r++) A[r] = *reinterpret_cast<const u32x4*>(xbuf + r * kXSet + xrd);
+#pragma unroll
     for (int t = 0; t < TN; t++) {
-      uint32_t sc = b.s[t];
+      uint32_t sc;
       if (SLDS) {
         // past-K chunks read a real scale here but their codes are zero
-        const uint32_t kg = b.s[t];
         sc = *reinterpret_cast<const uint16_t*>(lds_s + (16 * t + nl) * sls + (kg >> 4));
+      } else {
+        sc = sreg_fallback[slot][t];
       }
       const float s0 = e4m3_to_f32<0>(sc);
       const float s1 = e4m3_to_f32<1>(sc);
@@ -192,7 +235,7 @@ __device__ __forceinline__ void pass4(const StreamArgs& a, const uint8_t* wc, co
         c = mfma4<1>(A[r][0], A[r][1], wb[4], wb[5], c);
         c = mfma4<1>(A[r][2], A[r][3], wb[6], wb[7], c);
 #pragma unroll
-        for (int q = 0; q < 4; q++) acc[t][r][q] = __builtin_fmaf(s0, c[q], acc[t][r][q]);
+        for (int qq = 0; qq < 4; qq++) acc[t][r][qq] = __builtin_fmaf(s0, c[qq], acc[t][r][qq]);
         // scale block 1: k 16..31, pieces 2, 3
         c = f32x4{0.f, 0.f, 0.f, 0.f};
         c = mfma4<2>(A[r][0], A[r][1], wb[8], wb[9], c);
@@ -200,7 +243,7 @@ __device__ __forceinline__ void pass4(const StreamArgs& a, const uint8_t* wc, co
         c = mfma4<3>(A[r][0], A[r][1], wb[12], wb[13], c);
         c = mfma4<3>(A[r][2], A[r][3], wb[14], wb[15], c);
 #pragma unroll
-        for (int q = 0; q < 4; q++) acc[t][r][q] = __builtin_fmaf(s1, c[q], acc[t][r][q]);
+        for (int qq = 0; qq < 4; qq++) acc[t][r][qq] = __builtin_fmaf(s1, c[qq], acc[t][r][qq]);
       }
     }
   };
@@ -214,14 +257,17 @@ __device__ __forceinline__ void pass4(const StreamArgs& a, const uint8_t* wc, co
   const uint32_t chunks_per_row = sb >> 4;  // SLDS requires K % 256 == 0
   if (SLDS) {
 #pragma unroll
-    for (int q = 0; q < kScaleRegs; q++) {
-      const uint32_t cidx = threadIdx.x + q * blockDim.x;
-      sreg[q] = __builtin_amdgcn_raw_buffer_load_b128(sr, cidx < s_chunks ? cidx * 16u : kOOB, 0, 0);
+    for (int qq = 0; qq < kScaleRegs; qq++) {
+      const uint32_t cidx = threadIdx.x + qq * blockDim.x;
+      sreg[qq] = __builtin_amdgcn_raw_buffer_load_b128(sr, cidx < s_chunks ? cidx * 16u : kOOB, 0, 0);
     }
   }
   StepBuf<TN, R, ACT> buf[kDepth];
 #pragma unroll
-  for (int j = 0; j < kDepth; j++) load(j, buf[j]);
+  for (int j = 0; j < kDepth; j++) {
+    load(j, buf[j], kstep[j]);
+    load_scales(j, j);
+  }
   if (SLDS) {
     // Chunks past the tile go to the spare 16 bytes after the scale rows, so the stores
     // need no branch (a branch would make the wave wait for every load in flight).
@@ -236,30 +282,42 @@ __device__ __forceinline__ void pass4(const StreamArgs& a, const uint8_t* wc, co
       d[3] = v[3];
     };
 #pragma unroll
-    for (int q = 0; q < kScaleRegs; q++) put(threadIdx.x + q * blockDim.x, sreg[q]);
+    for (int qq = 0; qq < kScaleRegs; qq++) put(threadIdx.x + qq * blockDim.x, sreg[qq]);
     // tiles with more chunks than the prefetch holds copy the rest directly
     for (uint32_t cidx = threadIdx.x + kScaleRegs * blockDim.x; cidx < s_chunks; cidx += blockDim.x)
       put(cidx, __builtin_amdgcn_raw_buffer_load_b128(sr, cidx * 16u, 0, 0));
     __syncthreads();
   }
-  for (int i0 = 0; i0 < NSW; i0 += kDepth) {
+  // Rounds of kDepth steps; every round but the last refills the ring, the last one only
+  // drains it (a peeled round rather than guarded loads, which would make the compiler
+  // wait for every load in flight where the guarded paths join).
+  const int rounds = (NSW + kDepth - 1) / kDepth;  // uniform
+  for (int c = 0; c + 1 < rounds; c++) {
 #pragma unroll
     for (int j = 0; j < kDepth; j++) {
-      if (i0 + j < NSW) compute(buf[j]);
-      load(i0 + j + kDepth, buf[j]);
+      compute(buf[j], kstep[j], j);
+      load((c + 1) * kDepth + j, buf[j], kstep[j]);
+      load_scales((c + 1) * kDepth + j, j);
+      __builtin_amdgcn_sched_barrier(0);  // refill the slot now, not at the end of the round
     }
   }
+  const int last = (rounds - 1) * kDepth;
+#pragma unroll
+  for (int j = 0; j < kDepth; j++)
+    if (last + j < NSW) compute(buf[j], kstep[j], j);
 }
 
 // Adds the partials of the four k-groups and of the waves in a fixed order and hands each
 // (x row m, weight row n, sum) to `store`. acc[t][r][q] is x row 4r + q, weight row
-// 16t + nl. LDS: red[wave][t][r][lane][q].
+// 16t + nl. LDS: red[wave][t][r][lane][q], over the bytes the stream used (hence the
+// barrier first).
 template <int TN, int R, typename Store>
 __device__ __forceinline__ void reduce_store(const f32x4 (&acc)[TN][R], float* red, int64_t n0,
                                              Store store) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int W = blockDim.x >> 6;
+  __syncthreads();
 #pragma unroll
   for (int t = 0; t < TN; t++)
 #pragma unroll
@@ -280,18 +338,12 @@ __device__ __forceinline__ void reduce_store(const f32x4 (&acc)[TN][R], float* r
   __syncthreads();
 }
 
-// bytes of LDS the tile's scales take (0 without SLDS), rounded to 16
-__host__ __device__ __forceinline__ uint32_t lds_scale_bytes(int TN, int64_t K, bool slds) {
-  return slds ? ((16u * TN * lds_scale_stride(K) + 31u) & ~15u) : 0u;  // + 16 spare bytes
-}
-
 template <int TN, int R, int ACT, bool SLDS>
-__global__ __launch_bounds__(512) void stream_dense(StreamArgs a) {
+__global__ __launch_bounds__(256) void stream_dense(StreamArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  uint8_t* lds_s = lds;
-  float* red = reinterpret_cast<float*>(lds + lds_scale_bytes(TN, a.K, SLDS));
+  float* red = reinterpret_cast<float*>(lds);
   const int64_t n0 = (int64_t)blockIdx.x * 16 * TN;
-  const int i = threadIdx.x & 3;  // the x row this lane supplies within a set of four
+  const int i = (threadIdx.x >> 4) & 3;  // the x row this lane loads within a set of four
   RowMap rm;
 #pragma unroll
   for (int r = 0; r < 4; r++) {
@@ -306,7 +358,7 @@ __global__ __launch_bounds__(512) void stream_dense(StreamArgs a) {
     }
   }
   f32x4 acc[TN][R];
-  pass4<TN, R, ACT, SLDS>(a, a.w_codes, a.w_scales, n0, rm, lds_s, acc);
+  pass4<TN, R, ACT, SLDS>(a, a.w_codes, a.w_scales, n0, rm, lds, acc);
   const float ts = a.apply_ts ? a.w_ts[0] : 1.0f;
   reduce_store<TN, R>(acc, red, n0, [&](int m, int64_t n, float s) {
     if (m < a.M && n < a.N) {
@@ -317,10 +369,9 @@ __global__ __launch_bounds__(512) void stream_dense(StreamArgs a) {
 }
 
 template <int R, int ACT, bool SLDS>
-__global__ __launch_bounds__(512) void stream_grouped(StreamArgs a) {
+__global__ __launch_bounds__(256) void stream_grouped(StreamArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  uint8_t* lds_s = lds;
-  float* red = reinterpret_cast<float*>(lds + lds_scale_bytes(1, a.K, SLDS));
+  float* red = reinterpret_cast<float*>(lds);
   const int slot = blockIdx.y;
   if (slot >= *a.n_active) return;  // uniform over the workgroup
   const int e = a.active[slot];
@@ -329,7 +380,7 @@ __global__ __launch_bounds__(512) void stream_grouped(StreamArgs a) {
   const uint8_t* ws = a.w_scales + (int64_t)e * a.N * (a.K >> 4);
   const float ts = a.apply_ts ? a.w_ts[e] : 1.0f;
   const int64_t n0 = (int64_t)blockIdx.x * 16;
-  const int i = threadIdx.x & 3;
+  const int i = (threadIdx.x >> 4) & 3;
   for (int c0 = beg; c0 < end; c0 += 4 * R) {
     const int rows = min(4 * R, end - c0);
     RowMap rm;
@@ -348,8 +399,7 @@ __global__ __launch_bounds__(512) void stream_grouped(StreamArgs a) {
       }
     }
     f32x4 acc[1][R];
-    if (SLDS && c0 != beg) __syncthreads();  // the previous pass's scale reads are done
-    pass4<1, R, ACT, SLDS>(a, wc, ws, n0, rm, lds_s, acc);
+    pass4<1, R, ACT, SLDS>(a, wc, ws, n0, rm, lds, acc);
     reduce_store<1, R>(acc, red, n0, [&](int m, int64_t n, float s) {
       if (m < rows && n < a.N) {
         const int rr = a.sorted[c0 + m];
@@ -366,7 +416,7 @@ __global__ __launch_bounds__(512) void stream_grouped(StreamArgs a) {
 
 template <int TN, int R, int ACT>
 hipError_t launch_dense(const StreamArgs& a, int W, bool slds, hipStream_t stream) {
-  const size_t lds = lds_scale_bytes(TN, a.K, slds) + (size_t)W * TN * R * 64 * 4 * sizeof(float);
+  const size_t lds = lds_bytes(TN, R, W, a.K, slds);
   const int64_t groups = (a.N + 16 * TN - 1) / (16 * TN);
   if (slds)
     hipLaunchKernelGGL((stream_dense<TN, R, ACT, true>), dim3((uint32_t)groups), dim3(64 * W), lds,
@@ -380,7 +430,7 @@ hipError_t launch_dense(const StreamArgs& a, int W, bool slds, hipStream_t strea
 template <int R, int ACT>
 hipError_t launch_grouped(const StreamArgs& a, int max_active, int W, bool slds,
                           hipStream_t stream) {
-  const size_t lds = lds_scale_bytes(1, a.K, slds) + (size_t)W * R * 64 * 4 * sizeof(float);
+  const size_t lds = lds_bytes(1, R, W, a.K, slds);
   const int64_t groups = (a.N + 15) / 16;
   if (slds)
     hipLaunchKernelGGL((stream_grouped<R, ACT, true>), dim3((uint32_t)groups, (uint32_t)max_active),
@@ -426,7 +476,7 @@ bool use_lds_scales(const StreamArgs& a, int tn) {
 int pick_tn(int64_t N) {
   int best = 1;
   int64_t best_cost = -1;
-  for (int tn : {1, 2, 4}) {
+  for (int tn : {1, 2, 3, 4}) {
     const int64_t groups = (N + 16 * tn - 1) / (16 * tn);
     const int64_t cost = ((groups + 255) / 256) * tn;
     if (best_cost < 0 || cost <= best_cost) {
@@ -441,7 +491,7 @@ int pick_tn(int64_t N) {
 
 hipError_t launch_stream_cfg(const StreamArgs& a, int act_kind, bool grouped, int max_active,
                              int tn, int W, hipStream_t stream) {
-  if (W < 1 || W > 8) return hipErrorInvalidValue;
+  if (W < 1 || W > 4) return hipErrorInvalidValue;
   const bool slds = use_lds_scales(a, grouped ? 1 : tn);
   if (grouped) {
     // rows of one expert pass in sets of four: one set covers decode-sized loads
@@ -465,7 +515,9 @@ hipError_t launch_stream(const StreamArgs& a, int act_kind, bool grouped, int ma
   const int64_t NS = (a.K + 127) / 128;  // 128-k steps per row
   int W = (int)((NS + 7) / 8);           // about 8 steps per wave
   W = W < 1 ? 1 : (W > 4 ? 4 : W);
-  const int tn = grouped ? 1 : pick_tn(a.N);
+  // one row set: 16-row tiles keep the most workgroups in flight; more row sets: wider
+  // tiles share each activation load among more weight rows
+  const int tn = (grouped || a.M <= 4) ? 1 : pick_tn(a.N);
   return launch_stream_cfg(a, act_kind, grouped, max_active, tn, W, stream);
 }
 
