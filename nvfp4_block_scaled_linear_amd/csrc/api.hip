@@ -102,6 +102,11 @@ nvfp4_status nvfp4_linear(int32_t act_kind, const void* x, const uint8_t* x_scal
   if (ldy < N || ldy > kMaxDim) return NVFP4_ERR_SHAPE;
   if (!aligned(y, 4)) return NVFP4_ERR_ALIGN;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  // the kernels address activation rows with 32-bit buffer offsets
+  if (act_kind == NVFP4_ACT_BF16 &&
+      (M <= kStreamMaxRows ? M * ldx * 2 > kMaxBufferBytes : ldx > gemm_max_ldx()))
+    return NVFP4_ERR_SHAPE;
+  if (act_kind == NVFP4_ACT_NVFP4 && M * (K / 2) > kMaxBufferBytes) return NVFP4_ERR_SHAPE;
   if (M <= kStreamMaxRows) {
     StreamArgs a{};
     a.x = x; a.x_scales = x_scales; a.x_ts = x_ts; a.ldx = ldx;

@@ -5,14 +5,22 @@
 // #754 and #822), with activations rounded once rather than in every tile (PR #761).
 // That design targets GB10 tensor cores; on gfx950 we keep the ideas that still hold and
 // shape the rest for CDNA4:
-//  - Workgroup tile 128 (M) x 256 (N) x 64 (K), four wave64s side by side along N, each
-//    computing 128 x 64 with the 32x32x16 BF16 MFMA (8 accumulator tiles of 32x32).
+//  - Large M: a 256 (M) x 256 (N) x 64 (K) tile on eight wave64s (two along M, four
+//    along N, each 128 x 64 with the 32x32x16 BF16 MFMA); the weight tile is decoded
+//    once per workgroup into LDS and read by both row halves (gemm_wide below).
+//  - Smaller M: a 32*MT (M) x 256 (N) tile on four wave64s side by side along N, each
+//    computing 32*MT x 64 and decoding its own weight columns in registers; two
+//    workgroups per CU.
 //  - Activations (BF16, or NVFP4 decoded once per tile) are staged through LDS, double
 //    buffered with one barrier per K step, rows padded by 16 bytes against bank
 //    conflicts; all four waves read them.
 //  - The weight never goes through LDS: each wave loads its own 64 columns' nibbles
 //    (16 B per lane per K step) straight into registers and decodes them to exact BF16
-//    operands, so every weight element is decoded once per workgroup.
+//    operands (e2m1 * e4m3 in f32, high halves), so every weight element is decoded once
+//    per workgroup.
+//  - Global loads run two K steps ahead in two register sets; they are raw buffer loads
+//    (out-of-range offsets read zeros), so no branch guards a load and the compiler
+//    waits only for the step it needs.
 //  - Workgroups are numbered so that each XCD (blockIdx % 8) owns a contiguous run of
 //    tiles that share activation rows (A-stationary), keeping the reused operand in its
 //    own L2.
@@ -23,19 +31,42 @@
 namespace nvfp4 {
 namespace {
 
-constexpr int BM = 128;
 constexpr int BN = 256;
 constexpr int BK = 64;
 constexpr int LDA = BK + 8;  // bf16 per LDS row: 64 values + 16-byte pad
+constexpr uint32_t kOOB = 0x80000000u;
 
-template <int ACT>
-__global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * LDA];
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t bytes) {
+  const int64_t b = bytes < 0 ? 0 : (bytes > 0x7FFFFFFF ? 0x7FFFFFFF : bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)b, 0x00020000);
+}
+
+// kOOB when k is at or past K
+__device__ __forceinline__ uint32_t past(uint32_t K, uint32_t k) {
+  return ((K - 1u - k) >> 31) << 31;
+}
+
+template <int MT, int ACT>
+struct RegA {  // one K step of this thread's activation loads
+  u32x4 v[ACT == 0 ? MT : 1];
+  uint32_t c[ACT == 0 ? 1 : MT];   // NVFP4: 8 codes per piece
+  uint32_t s[ACT == 0 ? 1 : MT];   // NVFP4: the piece's scale byte
+};
+struct RegB {  // one K step of this lane's weight loads (two 32-column subtiles)
+  u32x4 c[2];
+  uint32_t s[2];
+};
+
+template <int MT, int ACT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_kernel(GemmArgs a) {
+  constexpr int BM = 32 * MT;
+  extern __shared__ __attribute__((aligned(16))) uint16_t lds_a[];  // [2][BM * LDA]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int64_t M = a.M, N = a.N, K = a.K;
+  const uint32_t Ku = (uint32_t)K;
 
   // XCD-aware tile order: consecutive tiles of one XCD share the same M rows.
   const int64_t nbm = (M + BM - 1) / BM, nbn = (N + BN - 1) / BN;
@@ -45,142 +76,151 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
   if (total % 8 == 0) lin = (bid % 8) * (total / 8) + bid / 8;
   const int64_t m0 = (lin / nbn) * BM;
   const int64_t n0 = (lin % nbn) * BN;
+  const int64_t rows_m = (M - m0) < BM ? (M - m0) : BM;
+  const int64_t rows_n = (N - n0) < BN ? (N - n0) : BN;
 
-  // weight columns of this lane: two 32-column subtiles, K half h of each 64-k step
+  // activation descriptors over this tile's rows
+  __amdgpu_buffer_rsrc_t xr, xsr;
+  if (ACT == 0) {
+    xr = rsrc(static_cast<const uint16_t*>(a.x) + m0 * a.ldx, ((rows_m - 1) * a.ldx + K) * 2);
+    xsr = xr;
+  } else {
+    xr = rsrc(static_cast<const uint8_t*>(a.x) + m0 * (K >> 1), rows_m * (K >> 1));
+    xsr = rsrc(a.x_scales + m0 * (K >> 4), rows_m * (K >> 4));
+  }
+  // weight descriptors over this tile's columns; lane (col, h): two 32-column subtiles,
+  // K half h of each 64-k step
   const int col = lane & 31;
   const int h = lane >> 5;
-  const int64_t kb = K >> 1, sb = K >> 4;
-  const uint8_t* wrow[2];
-  const uint8_t* srow[2];
-  bool nok[2];
+  const auto wr = rsrc(a.w_codes + n0 * (K >> 1), rows_n * (K >> 1));
+  const auto sr = rsrc(a.w_scales + n0 * (K >> 4), rows_n * (K >> 4));
+  uint32_t woff[2], soff[2];
 #pragma unroll
   for (int st = 0; st < 2; st++) {
-    const int64_t n = n0 + 64 * wave + 32 * st + col;
-    nok[st] = n < N;
-    const int64_t nn = nok[st] ? n : 0;
-    wrow[st] = a.w_codes + nn * kb;
-    srow[st] = a.w_scales + nn * sb;
+    const int nl = 64 * wave + 32 * st + col;
+    woff[st] = nl < rows_n ? (uint32_t)(nl * (K >> 1)) : kOOB;
+    soff[st] = nl < rows_n ? (uint32_t)(nl * (K >> 4)) : kOOB;
   }
 
   const int KT = (int)((K + BK - 1) / BK);
+  const int KT2 = KT + (KT & 1);  // even step count: an odd tail step reads zeros
 
-  // activation staging registers
-  u32x4 areg[4];
-  uint32_t asc = 0;
-  // weight registers: next step's loads and the current step's values
-  u32x4 bnext[2], bcur[2];
-  uint32_t snext[2], scur[2];
-
-  auto load_step = [&](int kt) {
-    const int64_t k0 = (int64_t)kt * BK;
+  auto issue = [&](int kt, RegA<MT, ACT>& ra, RegB& rb) {
+    const uint32_t k0 = (uint32_t)kt * BK;
     if (ACT == 0) {
 #pragma unroll
-      for (int q = 0; q < 4; q++) {
+      for (int q = 0; q < MT; q++) {
         const int c = tid + 256 * q;
         const int row = c >> 3, ch = c & 7;
-        const int64_t gm = m0 + row, gk = k0 + 8 * ch;
-        areg[q] = (gm < M && gk < K)
-                      ? *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.x) +
-                                                         gm * a.ldx + gk)
-                      : u32x4{0u, 0u, 0u, 0u};
+        const uint32_t k = k0 + 8u * ch;
+        const uint32_t off = (uint32_t)(row * a.ldx * 2) + 2u * k;
+        ra.v[q] = __builtin_amdgcn_raw_buffer_load_b128(xr, off | past(Ku, k), 0, 0);
       }
     } else {
-      const int row = tid >> 1, half = tid & 1;
-      const int64_t gm = m0 + row, gk = k0 + 32 * half;
-      if (gm < M && gk < K) {
-        areg[0] = *reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(a.x) + gm * kb +
-                                                  (gk >> 1));
-        asc = *reinterpret_cast<const uint16_t*>(a.x_scales + gm * sb + (gk >> 4));
-      } else {
-        areg[0] = u32x4{0u, 0u, 0u, 0u};
-        asc = 0u;
+#pragma unroll
+      for (int q = 0; q < MT; q++) {
+        const int p = tid + 256 * q;
+        const int row = p >> 3, j = p & 7;
+        const uint32_t k = k0 + 8u * j;
+        ra.c[q] = __builtin_amdgcn_raw_buffer_load_b32(
+            xr, ((uint32_t)(row * (K >> 1)) + (k >> 1)) | past(Ku, k), 0, 0);
+        ra.s[q] = __builtin_amdgcn_raw_buffer_load_b8(
+            xsr, ((uint32_t)(row * (K >> 4)) + (k >> 4)) | past(Ku, k), 0, 0);
       }
     }
+    const uint32_t kh = k0 + 32u * h;
 #pragma unroll
     for (int st = 0; st < 2; st++) {
-      const int64_t gk = k0 + 32 * h;
-      if (nok[st] && gk < K) {
-        bnext[st] = *reinterpret_cast<const u32x4*>(wrow[st] + (gk >> 1));
-        snext[st] = *reinterpret_cast<const uint16_t*>(srow[st] + (gk >> 4));
-      } else {
-        bnext[st] = u32x4{0u, 0u, 0u, 0u};
-        snext[st] = 0u;
-      }
+      rb.c[st] = __builtin_amdgcn_raw_buffer_load_b128(wr, (woff[st] + (kh >> 1)) | past(Ku, kh), 0, 0);
+      rb.s[st] = __builtin_amdgcn_raw_buffer_load_b16(sr, (soff[st] + (kh >> 4)) | past(Ku, kh), 0, 0);
     }
   };
 
-  auto store_a = [&](int buf) {
-    uint16_t* dst = As[buf];
+  auto write_a = [&](const RegA<MT, ACT>& ra, int buf) {
+    uint16_t* dst = lds_a + buf * (BM * LDA);
     if (ACT == 0) {
 #pragma unroll
-      for (int q = 0; q < 4; q++) {
+      for (int q = 0; q < MT; q++) {
         const int c = tid + 256 * q;
         const int row = c >> 3, ch = c & 7;
-        *reinterpret_cast<u32x4*>(dst + row * LDA + 8 * ch) = areg[q];
+        *reinterpret_cast<u32x4*>(dst + row * LDA + 8 * ch) = ra.v[q];
       }
     } else {
-      const int row = tid >> 1, half = tid & 1;
-      const float s0 = e4m3_to_f32<0>(asc), s1 = e4m3_to_f32<1>(asc);
-      u32x4* p = reinterpret_cast<u32x4*>(dst + row * LDA + 32 * half);
-      p[0] = decode8(areg[0][0], s0);
-      p[1] = decode8(areg[0][1], s0);
-      p[2] = decode8(areg[0][2], s1);
-      p[3] = decode8(areg[0][3], s1);
+#pragma unroll
+      for (int q = 0; q < MT; q++) {
+        const int p = tid + 256 * q;
+        const int row = p >> 3, j = p & 7;
+        *reinterpret_cast<u32x4*>(dst + row * LDA + 8 * j) =
+            decode8(ra.c[q], e4m3_to_f32<0>(ra.s[q]));  // exact BF16 activations
+      }
     }
   };
 
-  f32x16 acc[4][2];
+  f32x16 acc[MT][2];
 #pragma unroll
-  for (int mt = 0; mt < 4; mt++)
+  for (int mt = 0; mt < MT; mt++)
 #pragma unroll
     for (int st = 0; st < 2; st++)
 #pragma unroll
       for (int r = 0; r < 16; r++) acc[mt][st][r] = 0.f;
 
-  load_step(0);
-  store_a(0);
-#pragma unroll
-  for (int st = 0; st < 2; st++) {
-    bcur[st] = bnext[st];
-    scur[st] = snext[st];
-  }
-
-  for (int kt = 0; kt < KT; kt++) {
-    if (kt + 1 < KT) load_step(kt + 1);
-    __syncthreads();
-    const uint16_t* src = As[kt & 1];
-    float ws[2][2];
+  auto decode = [&](const RegB& rb, u32x4 (&Bd)[2][4]) {
 #pragma unroll
     for (int st = 0; st < 2; st++) {
-      ws[st][0] = e4m3_to_f32<0>(scur[st]);
-      ws[st][1] = e4m3_to_f32<1>(scur[st]);
+      const float s0 = e4m3_to_f32<0>(rb.s[st]);
+      const float s1 = e4m3_to_f32<1>(rb.s[st]);
+#pragma unroll
+      for (int j = 0; j < 4; j++) Bd[st][j] = decode8(rb.c[st][j], j < 2 ? s0 : s1);
     }
+  };
+
+  // One K step: refill the freed register sets with step kt + 2, multiply from LDS
+  // buffer kt & 1 with this step's decoded weights while decoding step kt + 1's (the
+  // decode's VALU work fills the MFMA pipeline's shadow), stage step kt + 1's
+  // activations into the other buffer.
+  auto body = [&](int kt, RegA<MT, ACT>& ra_free, RegB& rb_free, RegA<MT, ACT>& ra_next,
+                  const RegB& rb_next, const u32x4 (&Bd)[2][4], u32x4 (&Bd_next)[2][4]) {
+    issue(kt + 2, ra_free, rb_free);
+    const uint16_t* src = lds_a + (kt & 1) * (BM * LDA);
 #pragma unroll
     for (int j = 0; j < 4; j++) {
-      u32x4 B[2];
 #pragma unroll
-      for (int st = 0; st < 2; st++) B[st] = decode8(bcur[st][j], ws[st][j >> 1]);
-#pragma unroll
-      for (int mt = 0; mt < 4; mt++) {
+      for (int mt = 0; mt < MT; mt++) {
         const u32x4 A =
             *reinterpret_cast<const u32x4*>(src + (32 * mt + col) * LDA + 32 * h + 8 * j);
 #pragma unroll
-        for (int st = 0; st < 2; st++) acc[mt][st] = mfma32(A, B[st], acc[mt][st]);
+        for (int st = 0; st < 2; st++) acc[mt][st] = mfma32(A, Bd[st][j], acc[mt][st]);
       }
     }
-    if (kt + 1 < KT) {
-      store_a((kt + 1) & 1);
+    decode(rb_next, Bd_next);
+    // interleave: each MFMA followed by a share of the decode's VALU work, with the LDS
+    // operand reads spread between them
 #pragma unroll
-      for (int st = 0; st < 2; st++) {
-        bcur[st] = bnext[st];
-        scur[st] = snext[st];
-      }
+    for (int i = 0; i < 8 * MT; i++) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);           // one MFMA
+      if (i % 2 == 0) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+      __builtin_amdgcn_sched_group_barrier(0x002, 160 / (8 * MT) + 1, 0);  // VALU
     }
+    write_a(ra_next, (kt + 1) & 1);
+    __syncthreads();
+  };
+
+  RegA<MT, ACT> ra0, ra1;
+  RegB rb0, rb1;
+  u32x4 Bd0[2][4], Bd1[2][4];
+  issue(0, ra0, rb0);
+  issue(1, ra1, rb1);
+  decode(rb0, Bd0);
+  write_a(ra0, 0);
+  __syncthreads();
+  for (int kt = 0; kt < KT2; kt += 2) {
+    body(kt, ra0, rb0, ra1, rb1, Bd0, Bd1);
+    body(kt + 1, ra1, rb1, ra0, rb0, Bd1, Bd0);
   }
 
   const float ts = a.w_ts[0];
 #pragma unroll
-  for (int mt = 0; mt < 4; mt++) {
+  for (int mt = 0; mt < MT; mt++) {
 #pragma unroll
     for (int r = 0; r < 16; r++) {
       const int64_t row = m0 + 32 * mt + 8 * (r >> 2) + 4 * h + (r & 3);
@@ -195,15 +235,210 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------------------
+// Wide variant for large M: a 256 x 256 tile and eight waves, two along M and four along
+// N, two waves per SIMD. The weight tile is decoded once per workgroup (one 16-byte code
+// chunk per thread) into LDS as exact BF16 and read by both row halves, so each decoded
+// element feeds 256 rows; both operands are double buffered in LDS (147 KB), read with
+// 128-bit LDS loads (about twice the rate of narrower ones on gfx950).
+// ---------------------------------------------------------------------------------------
+template <int ACT>
+struct RegAW {  // one K step of this thread's activation loads (4 chunks)
+  u32x4 v[ACT == 0 ? 4 : 1];
+  uint32_t c[ACT == 0 ? 1 : 4];
+  uint32_t s[ACT == 0 ? 1 : 4];
+};
+struct RegBW {  // one K step of this thread's weight chunk: 32 codes and their 2 scales
+  u32x4 c;
+  uint32_t s;
+};
+
+constexpr int kWideBM = 256;
+
+template <int ACT>
+__global__ __launch_bounds__(512) void gemm_wide(GemmArgs a) {
+  constexpr int BM = kWideBM;
+  extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
+  uint16_t* As = lds;                 // [2][BM * LDA]  activations [row][k]
+  uint16_t* Bs = lds + 2 * BM * LDA;  // [2][BN * LDA]  decoded weight [column][k]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 2, wn = wave & 3;
+  const int64_t M = a.M, N = a.N, K = a.K;
+  const uint32_t Ku = (uint32_t)K;
+
+  const int64_t nbm = (M + BM - 1) / BM, nbn = (N + BN - 1) / BN;
+  const int64_t total = nbm * nbn;
+  const int64_t bid = blockIdx.x;
+  int64_t lin = bid;
+  if (total % 8 == 0) lin = (bid % 8) * (total / 8) + bid / 8;
+  const int64_t m0 = (lin / nbn) * BM;
+  const int64_t n0 = (lin % nbn) * BN;
+  const int64_t rows_m = (M - m0) < BM ? (M - m0) : BM;
+  const int64_t rows_n = (N - n0) < BN ? (N - n0) : BN;
+
+  __amdgpu_buffer_rsrc_t xr, xsr;
+  if (ACT == 0) {
+    xr = rsrc(static_cast<const uint16_t*>(a.x) + m0 * a.ldx, ((rows_m - 1) * a.ldx + K) * 2);
+    xsr = xr;
+  } else {
+    xr = rsrc(static_cast<const uint8_t*>(a.x) + m0 * (K >> 1), rows_m * (K >> 1));
+    xsr = rsrc(a.x_scales + m0 * (K >> 4), rows_m * (K >> 4));
+  }
+  const auto wr = rsrc(a.w_codes + n0 * (K >> 1), rows_n * (K >> 1));
+  const auto sr = rsrc(a.w_scales + n0 * (K >> 4), rows_n * (K >> 4));
+  // this thread's weight chunk: column bc, K half bh of each 64-k step
+  const int bc = tid >> 1, bh = tid & 1;
+  const uint32_t bwoff = bc < rows_n ? (uint32_t)(bc * (K >> 1)) : kOOB;
+  const uint32_t bsoff = bc < rows_n ? (uint32_t)(bc * (K >> 4)) : kOOB;
+  // MFMA operand lanes: row/column c of a 32-wide subtile, K half h
+  const int col = lane & 31;
+  const int h = lane >> 5;
+
+  const int KT = (int)((K + BK - 1) / BK);
+  const int KT2 = KT + (KT & 1);
+
+  auto issue = [&](int kt, RegAW<ACT>& ra, RegBW& rb) {
+    const uint32_t k0 = (uint32_t)kt * BK;
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+      const int c = tid + 512 * q;
+      const int row = c >> 3, j = c & 7;
+      const uint32_t k = k0 + 8u * j;
+      if (ACT == 0) {
+        const uint32_t off = (uint32_t)(row * a.ldx * 2) + 2u * k;
+        ra.v[q] = __builtin_amdgcn_raw_buffer_load_b128(xr, off | past(Ku, k), 0, 0);
+      } else {
+        ra.c[q] = __builtin_amdgcn_raw_buffer_load_b32(
+            xr, ((uint32_t)(row * (K >> 1)) + (k >> 1)) | past(Ku, k), 0, 0);
+        ra.s[q] = __builtin_amdgcn_raw_buffer_load_b8(
+            xsr, ((uint32_t)(row * (K >> 4)) + (k >> 4)) | past(Ku, k), 0, 0);
+      }
+    }
+    const uint32_t kh = k0 + 32u * bh;
+    rb.c = __builtin_amdgcn_raw_buffer_load_b128(wr, (bwoff + (kh >> 1)) | past(Ku, kh), 0, 0);
+    rb.s = __builtin_amdgcn_raw_buffer_load_b16(sr, (bsoff + (kh >> 4)) | past(Ku, kh), 0, 0);
+  };
+
+  // stage one K step: activations as they are (or decoded from NVFP4), weights decoded
+  auto write_tiles = [&](const RegAW<ACT>& ra, const RegBW& rb, int buf) {
+    uint16_t* da = As + buf * (BM * LDA);
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+      const int c = tid + 512 * q;
+      const int row = c >> 3, j = c & 7;
+      u32x4 v;
+      if (ACT == 0) v = ra.v[q];
+      else v = decode8(ra.c[q], e4m3_to_f32<0>(ra.s[q]));  // exact BF16 activations
+      *reinterpret_cast<u32x4*>(da + row * LDA + 8 * j) = v;
+    }
+    uint16_t* db = Bs + buf * (BN * LDA) + bc * LDA + 32 * bh;
+    const float s0 = e4m3_to_f32<0>(rb.s), s1 = e4m3_to_f32<1>(rb.s);
+#pragma unroll
+    for (int d = 0; d < 4; d++)
+      *reinterpret_cast<u32x4*>(db + 8 * d) = decode8(rb.c[d], d < 2 ? s0 : s1);
+  };
+
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int mt = 0; mt < 4; mt++)
+#pragma unroll
+    for (int st = 0; st < 2; st++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) acc[mt][st][r] = 0.f;
+
+  auto body = [&](int kt, RegAW<ACT>& ra_free, RegBW& rb_free, const RegAW<ACT>& ra_next,
+                  const RegBW& rb_next) {
+    issue(kt + 2, ra_free, rb_free);
+    const uint16_t* sa = As + (kt & 1) * (BM * LDA) + (128 * wm + col) * LDA + 32 * h;
+    const uint16_t* sb = Bs + (kt & 1) * (BN * LDA) + (64 * wn + col) * LDA + 32 * h;
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      u32x4 B[2];
+#pragma unroll
+      for (int st = 0; st < 2; st++)
+        B[st] = *reinterpret_cast<const u32x4*>(sb + 32 * st * LDA + 8 * j);
+#pragma unroll
+      for (int mt = 0; mt < 4; mt++) {
+        const u32x4 A = *reinterpret_cast<const u32x4*>(sa + 32 * mt * LDA + 8 * j);
+#pragma unroll
+        for (int st = 0; st < 2; st++) acc[mt][st] = mfma32(A, B[st], acc[mt][st]);
+      }
+    }
+    write_tiles(ra_next, rb_next, (kt + 1) & 1);
+#pragma unroll
+    for (int i = 0; i < 32; i++) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  // one MFMA
+      if (i < 24) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);      // one LDS read
+      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);                  // VALU
+    }
+    __syncthreads();
+  };
+
+  RegAW<ACT> ra0, ra1;
+  RegBW rb0, rb1;
+  issue(0, ra0, rb0);
+  issue(1, ra1, rb1);
+  write_tiles(ra0, rb0, 0);
+  __syncthreads();
+  for (int kt = 0; kt < KT2; kt += 2) {
+    body(kt, ra0, rb0, ra1, rb1);
+    body(kt + 1, ra1, rb1, ra0, rb0);
+  }
+
+  const float ts = a.w_ts[0];
+#pragma unroll
+  for (int mt = 0; mt < 4; mt++) {
+#pragma unroll
+    for (int r = 0; r < 16; r++) {
+      const int64_t row = m0 + 128 * wm + 32 * mt + 8 * (r >> 2) + 4 * h + (r & 3);
+      if (row >= M) continue;
+      const float f = (ACT == 0) ? ts : a.x_ts[row] * ts;
+#pragma unroll
+      for (int st = 0; st < 2; st++) {
+        const int64_t n = n0 + 64 * wn + 32 * st + col;
+        if (n < N) a.y[row * a.ldy + n] = acc[mt][st][r] * f;
+      }
+    }
+  }
+}
+
+template <int MT, int ACT>
+hipError_t launch_mt(const GemmArgs& a, hipStream_t stream) {
+  constexpr int BM = 32 * MT;
+  const int64_t blocks = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
+  const size_t lds = 2 * (size_t)BM * LDA * sizeof(uint16_t);
+  hipLaunchKernelGGL((gemm_kernel<MT, ACT>), dim3((uint32_t)blocks), dim3(256), lds, stream, a);
+  return hipGetLastError();
+}
+
+template <int ACT>
+hipError_t launch_wide(const GemmArgs& a, hipStream_t stream) {
+  const int64_t blocks = ((a.M + kWideBM - 1) / kWideBM) * ((a.N + BN - 1) / BN);
+  const size_t lds = 2 * (size_t)(kWideBM + BN) * LDA * sizeof(uint16_t);
+  hipLaunchKernelGGL((gemm_wide<ACT>), dim3((uint32_t)blocks), dim3(512), lds, stream, a);
+  return hipGetLastError();
+}
+
+// Tile choice: 256 x 256 tiles (each decoded weight element feeds 256 rows) when they give
+// at least one workgroup per CU; otherwise 64-row tiles, whose two workgroups per CU keep
+// more of the chip busy on smaller problems.
+bool use_wide(int64_t M, int64_t N) {
+  return ((M + kWideBM - 1) / kWideBM) * ((N + BN - 1) / BN) >= 256;
+}
+
 }  // namespace
 
+// Largest activation row pitch (elements) the GEMM's 32-bit buffer offsets can address
+// for a 256-row tile.
+int64_t gemm_max_ldx() { return ((int64_t)1 << 31) / (2 * 256) - 1; }
+
 hipError_t launch_gemm(const GemmArgs& a, int act_kind, hipStream_t stream) {
-  const int64_t blocks = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
-  if (act_kind == 0)
-    hipLaunchKernelGGL((gemm_kernel<0>), dim3((uint32_t)blocks), dim3(256), 0, stream, a);
-  else
-    hipLaunchKernelGGL((gemm_kernel<1>), dim3((uint32_t)blocks), dim3(256), 0, stream, a);
-  return hipGetLastError();
+  if (use_wide(a.M, a.N))
+    return act_kind == 0 ? launch_wide<0>(a, stream) : launch_wide<1>(a, stream);
+  return act_kind == 0 ? launch_mt<2, 0>(a, stream) : launch_mt<2, 1>(a, stream);
 }
 
 }  // namespace nvfp4

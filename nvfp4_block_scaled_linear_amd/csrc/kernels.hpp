@@ -55,6 +55,8 @@ struct GemmArgs {
 };
 
 hipError_t launch_gemm(const GemmArgs& a, int act_kind, hipStream_t stream);
+// largest BF16 activation row pitch (elements) the GEMM's buffer offsets address
+int64_t gemm_max_ldx();
 
 hipError_t launch_quantize(int in_type, const void* x, int64_t ldx, int64_t M, int64_t K,
                            int ts_mode, uint8_t* codes, uint8_t* scales, float* ts,

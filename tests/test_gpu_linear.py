@@ -159,6 +159,30 @@ def test_linear_gemm_ragged(dev, o, M, N, K):
     assert_within(y, yr, b, f"M={M} N={N} K={K}")
 
 
+def test_linear_wide_tiles_ragged(dev, o):
+    """The 256 x 256-tile GEMM (chosen when it gives every CU a workgroup) on ragged M, N
+    and an odd number of 64-k steps; sampled rows, including every row of the last,
+    partial row tile."""
+    M, N, K = 600, 86 * 256 - 100, 544
+    _say(f"wide-tile gemm M={M} N={N} K={K} (sampled rows)")
+    w = weight_f32(71, N, K)
+    (c, s, t), oq = quantize_both(o, w, dev)
+    xb = act_bf16(72, M, K)
+    y = nv.linear(to_dev_bf16(xb, dev), c, s, t)
+    rows = np.unique(np.r_[0, 255, 256, 511, np.arange(512, M, 7), M - 1])
+    wdq = o.dequant(*oq, per_row=False)
+    yr, b = o.linear_f64(o.bf16_to_f64(xb[rows]), wdq)
+    assert_within(y[torch.from_numpy(rows).to(dev)].cpu().numpy(), yr, b, "wide ragged rows")
+    assert bool(torch.isfinite(y).all())
+    # the same tiles with NVFP4 activations (W4A4)
+    xc, xs, xt = nv.quantize_act(to_dev_bf16(xb, dev))
+    oc, os_, ot = o.quantize_bf16(xb, per_row=True)
+    assert np.array_equal(xc.cpu().numpy(), oc) and np.array_equal(xs.cpu().numpy(), os_)
+    y4 = nv.linear(xc, c, s, t, x_scales=xs, x_ts=xt)
+    yr4, b4 = o.linear_w4a4(oc[rows], os_[rows], ot[rows], *oq)
+    assert_within(y4[torch.from_numpy(rows).to(dev)].cpu().numpy(), yr4, b4, "wide ragged w4a4")
+
+
 def test_linear_leading_dimensions(dev, o):
     _say("linear with padded x and y rows")
     for M in (4, 40):
