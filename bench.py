@@ -401,7 +401,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--only", choices=["all", "decode"], default="all")
+    ap.add_argument("--only", choices=["all", "decode", "single", "prefill", "w4a4", "moe"],
+                    default="all", help="run the decode sweep plus one other workload (all: every one)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--copy-probe", action="store_true", help="also time a 1 GiB device copy")
     ap.add_argument("--summarize-rocprof", metavar="DIR",
@@ -453,13 +454,18 @@ def main():
                      "bytes_per_launch_avg": d["step_bytes"] // d["launches_per_step"]},
         "per_m": d["per_m"],
     }
-    if args.only == "all":
+    def want(name):
+        return args.only in ("all", name)
+    if want("single"):
         log("single linear ...")
         rec["single_linear"] = bench_single(nv, dev)
+    if want("prefill"):
         log("prefill ...")
         rec["prefill"] = bench_prefill(nv, dev)
+    if want("w4a4"):
         log("w4a4 ...")
         rec["w4a4"] = bench_w4a4(nv, dev)
+    if want("moe"):
         log("moe ...")
         rec["moe"] = bench_moe(nv, dev)
     if args.copy_probe or args.only == "all":

@@ -106,6 +106,119 @@ __global__ __launch_bounds__(kSortThreads) void route_sort(const int32_t* ids, i
   }
 }
 
+// Decode-sized route sets (R <= kFastRoutes): the same result as route_sort, computed in
+// LDS with no dependent global-memory round trips. One route per thread (the block is
+// sized to R); the expert offsets and the active-expert list come from block-wide scans;
+// a route's place among its expert's routes is the number of earlier routes with the
+// same expert (stable, counted with 16-byte LDS reads); its slot within its token is the
+// number of the token's valid routes with a smaller expert id (valid ids are distinct
+// within a token); the slots after them hold -1, as in route_sort.
+constexpr int kFastRoutes = kSortThreads;
+
+// Exclusive prefix sum over the block: a shuffle scan inside each wave, then the wave
+// totals through LDS (two barriers). `wsum` holds blockDim.x / 64 entries.
+__device__ __forceinline__ int32_t block_exclusive_scan(int32_t v, int32_t* wsum, int32_t* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nw = blockDim.x >> 6;
+  int32_t x = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int32_t y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
+  }
+  if (lane == 63) wsum[wave] = x;
+  __syncthreads();
+  int32_t base = 0, tot = 0;
+  for (int w = 0; w < nw; w++) {
+    const int32_t sw = wsum[w];
+    base += w < wave ? sw : 0;
+    tot += sw;
+  }
+  *total = tot;
+  __syncthreads();  // wsum is reused by the next scan
+  return base + x - v;
+}
+
+__global__ __launch_bounds__(kSortThreads) void route_sort_fast(const int32_t* ids, int64_t T,
+                                                                int top_k, int E,
+                                                                RouteWorkspace ws,
+                                                                uint32_t* faults) {
+  extern __shared__ __attribute__((aligned(16))) int32_t sh[];
+  const int nt = blockDim.x;                // >= R, a multiple of 64
+  int32_t* ids_s = sh;                      // [nt]
+  int32_t* rexp = sh + nt;                  // [nt] expert of each route, -1 dropped/padding
+  int32_t* wsum = sh + 2 * nt;              // [16] wave totals of a scan
+  int32_t* cnt = sh + 2 * nt + 16;          // [E] routes per expert
+  const int R = (int)(T * top_k);
+  const int tid = threadIdx.x;
+
+  ids_s[tid] = tid < R ? ids[tid] : -1;
+  for (int e = tid; e < E; e += nt) cnt[e] = 0;
+  __syncthreads();
+
+  // validate: in range and not repeated earlier in its token
+  int32_t my_e = -1;
+  if (tid < R) {
+    const int32_t e = ids_s[tid];
+    bool ok = (e >= 0 && e < E);
+    const int t0 = (tid / top_k) * top_k;
+    for (int r = t0; r < tid; r++) ok = ok && (ids_s[r] != e);
+    my_e = ok ? e : -1;
+    ws.route_expert[tid] = my_e;
+    if (!ok && faults) atomicOr(faults, (uint32_t)NVFP4_FAULT_BAD_ROUTE);
+    if (ok) atomicAdd(&cnt[e], 1);  // integer count: order-independent
+  }
+  rexp[tid] = my_e;
+  __syncthreads();
+
+  // offsets and the active list: exclusive scans over the experts, one per thread per
+  // chunk of nt experts
+  int32_t run = 0, act_run = 0, my_off = 0;
+  for (int e0 = 0; e0 < E; e0 += nt) {
+    const int e = e0 + tid;
+    const int32_t c = e < E ? cnt[e] : 0;
+    int32_t tot, tot_a;
+    const int32_t o = block_exclusive_scan(c, wsum, &tot) + run;
+    const int32_t a = block_exclusive_scan(c > 0 ? 1 : 0, wsum, &tot_a) + act_run;
+    if (e < E) {
+      ws.offsets[e] = o;
+      if (c > 0) ws.active[a] = e;
+      cnt[e] = o;  // now the expert's first sorted slot
+    }
+    run += tot;
+    act_run += tot_a;
+  }
+  if (tid == 0) {
+    ws.offsets[E] = run;
+    *ws.n_active = act_run;
+  }
+  __syncthreads();
+
+  if (tid < R) {
+    const int t0 = (tid / top_k) * top_k;
+    if (my_e >= 0) {
+      // stable place among the expert's routes
+      int rank = 0;
+      const int full = tid & ~3;
+      for (int r = 0; r < full; r += 4) {
+        const int4 v = *reinterpret_cast<const int4*>(rexp + r);
+        rank += (v.x == my_e) + (v.y == my_e) + (v.z == my_e) + (v.w == my_e);
+      }
+      for (int r = full; r < tid; r++) rank += (rexp[r] == my_e);
+      ws.sorted[cnt[my_e] + rank] = tid;
+    }
+    // slot within the token: ascending expert id, dropped routes last as -1
+    int slot = 0;
+    if (my_e >= 0) {
+      for (int r = t0; r < t0 + top_k; r++) slot += (rexp[r] >= 0 && rexp[r] < my_e);
+    } else {
+      for (int r = t0; r < t0 + top_k; r++) slot += (rexp[r] >= 0);
+      for (int r = t0; r < tid; r++) slot += (rexp[r] < 0);
+    }
+    ws.order[t0 + slot] = my_e >= 0 ? tid - t0 : -1;
+  }
+}
+
 // a[r][n] = bf16_rne(silu(h[r][n]) * h[r][n + N/2]), silu(g) = g / (1 + exp(-g))
 __global__ __launch_bounds__(256) void swiglu_kernel(const float* rows,
                                                      const int32_t* route_expert, int64_t R,
@@ -167,6 +280,13 @@ int64_t grid_for(int64_t total) {
 
 hipError_t launch_route_sort(const int32_t* topk_ids, int64_t T, int top_k, int E,
                              const RouteWorkspace& ws, uint32_t* faults, hipStream_t stream) {
+  if (T * top_k <= kFastRoutes) {
+    const int nt = (int)((T * top_k + 63) / 64 * 64);
+    const size_t lds = sizeof(int32_t) * ((size_t)2 * nt + 16 + (size_t)E);
+    hipLaunchKernelGGL(route_sort_fast, dim3(1), dim3(nt), lds, stream, topk_ids, T, top_k, E,
+                       ws, faults);
+    return hipGetLastError();
+  }
   const size_t lds = sizeof(int32_t) * ((size_t)2 * E + 1 + kSortThreads);
   hipLaunchKernelGGL(route_sort, dim3(1), dim3(kSortThreads), lds, stream, topk_ids, T, top_k, E,
                      ws, faults);

@@ -175,3 +175,67 @@ def test_grouped_w4a4_and_many_routes_per_expert(dev, o):
             e = ids[t, j]
             yr, b = o.linear_w4a4(oc[t:t + 1], os_[t:t + 1], ot[t:t + 1], *ws[e][1])
             assert_within(h[t * k + j:t * k + j + 1], yr, b, f"w4a4 route {t},{j}")
+
+
+def _small_experts(o, dev, E, N, K, seed):
+    ws = [quantize_both(o, weight_f32(seed, N, K, stream=60 + e), dev) for e in range(E)]
+    wc = torch.stack([q[0][0] for q in ws]); wsc = torch.stack([q[0][1] for q in ws])
+    wts = torch.cat([q[0][2] for q in ws])
+    oc = np.stack([q[1][0] for q in ws]); os_ = np.stack([q[1][1] for q in ws])
+    ot = np.concatenate([q[1][2] for q in ws])
+    return wc, wsc, wts, oc, os_, ot
+
+
+def _combine_check(dev, o, ids, E, N, K, seed, label):
+    """COMBINE output (rows read per token) against the oracle's ordered combine; a
+    dropped route enters the oracle with router weight 0 (an exact zero term)."""
+    T, k = ids.shape
+    wc, wsc, wts, oc, os_, ot = _small_experts(o, dev, E, N, K, seed)
+    xb = act_bf16(seed + 1, T, K)
+    rw = np.random.default_rng(seed).random((T, k)).astype(np.float32)
+    faults = torch.zeros(1, dtype=torch.int32, device=dev)
+    y = nv.grouped_linear(to_dev_bf16(xb, dev), wc, wsc, wts, torch.from_numpy(ids).to(dev),
+                          topk_w=torch.from_numpy(rw).to(dev), out_mode=nv.OUT_COMBINE,
+                          faults=faults).cpu().numpy()
+    valid = np.zeros_like(ids, dtype=bool)
+    for t in range(T):
+        seen = set()
+        for j in range(k):
+            e = int(ids[t, j])
+            valid[t, j] = 0 <= e < E and e not in seen
+            if valid[t, j]:
+                seen.add(e)
+    ids_o = np.where(valid, ids, 0).astype(np.int32)
+    rw_o = np.where(valid, rw, 0.0).astype(np.float32)
+    a_bits = np.repeat(xb, k, axis=0)  # the route rows are the token rows
+    yr, b = o.moe_down_combine(a_bits, ids_o, rw_o, oc, os_, ot)
+    assert_within(y, yr, b, label)
+    return int(faults.item())
+
+
+def test_grouped_combine_with_dropped_routes(dev, o):
+    ids = np.array([[0, 5, 2], [1, 1, 3], [7, 2, -1], [4, 0, 5]], np.int32)
+    f = _combine_check(dev, o, ids, 6, 40, 64, 81, "combine with dropped routes")
+    assert f & nv.FAULT_BAD_ROUTE
+
+
+def test_grouped_many_routes_general_sort(dev, o):
+    """More routes than one sorting workgroup holds at once (T * top_k > 1024): the
+    general route grouping, several 16-row passes per expert, in both output forms."""
+    E, N, K, T, k = 16, 48, 64, 160, 8
+    ids, _ = moe_routes(91, T, E, k)
+    ids = ids.astype(np.int32)
+    ids[3, 5] = ids[3, 1]  # one repeated id: flagged and dropped
+    f = _combine_check(dev, o, ids, E, N, K, 92, "many routes: combine")
+    assert f & nv.FAULT_BAD_ROUTE
+    wc, wsc, wts, oc, os_, ot = _small_experts(o, dev, E, N, K, 92)
+    xb = act_bf16(93, T, K)
+    h = nv.grouped_linear(to_dev_bf16(xb, dev), wc, wsc, wts, torch.from_numpy(ids).to(dev)).cpu().numpy()
+    assert np.all(h[3 * k + 5] == 0)
+    for r in np.r_[0, 1, 7, 400, 401, 1279, np.random.default_rng(5).choice(T * k, 20, replace=False)]:
+        t, j = divmod(int(r), k)
+        if (t, j) == (3, 5):
+            continue
+        e = int(ids[t, j])
+        yr, b = o.linear(xb[t:t + 1], oc[e], os_[e], ot[e:e + 1])
+        assert_within(h[r:r + 1], yr, b, f"many routes: route {t},{j}")
