@@ -65,6 +65,15 @@ class Timer:
         return self.a.elapsed_time(self.b) / reps  # ms per fn()
 
 
+def warm_until(fn, seconds):
+    """Untimed repetitions of fn for about `seconds` of wall time."""
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        fn()
+        torch.cuda.synchronize()
+
+
 def capture(fn):
     """Records fn's launches into a HIP graph (torch's capture on a side stream)."""
     g = torch.cuda.CUDAGraph()
@@ -187,8 +196,8 @@ def bench_prefill(nv, dev):
             nv.linear(x, W[j][0], W[j][1], t, out=y)
     g = capture(run)
     timer = Timer()
-    timer.time(g.replay, 1)
-    ms = timer.time(g.replay, 3) / R
+    warm_until(g.replay, 0.15)  # the clock settles under sustained MFMA load
+    ms = timer.time(g.replay, 10) / R
     flops = 2.0 * M * N * K
     tf = flops / (ms * 1e-3) / 1e12
     return {"workload": "M=2048 K=4096 N=14336", "us": round(ms * 1e3, 2), "TFLOPs": round(tf, 1),
@@ -215,8 +224,8 @@ def bench_w4a4(nv, dev):
                 nv.quantize_act(x, codes=xc, scales=xs_, ts=xt)
                 nv.linear(xc, W[j][0], W[j][1], t, x_scales=xs_, x_ts=xt, out=y)
         g = capture(run)
-        timer.time(g.replay, 1)
-        ms = timer.time(g.replay, 3) / reps_in
+        warm_until(g.replay, 0.1)
+        ms = timer.time(g.replay, 5) / reps_in
         b = weight_bytes(N, K) + 4 + M * (2 * K + K // 2 + K // 16 + 4) + M * (K // 2 + K // 16 + 4) + 4 * M * N
         fl = 2.0 * M * N * K
         out[str(M)] = {"us_quantize_plus_linear": round(ms * 1e3, 3),
