@@ -67,7 +67,7 @@ Layout grouped_layout(int64_t T, int top_k, int E, int64_t N, int32_t out_mode) 
   L.sorted = o; o = up256(o + sizeof(int32_t) * R);
   L.order = o; o = up256(o + sizeof(int32_t) * R);
   L.rows = o;
-  if (out_mode != NVFP4_OUT_ROUTES) o = up256(o + sizeof(float) * R * (size_t)N);
+  if (out_mode == NVFP4_OUT_COMBINE) o = up256(o + sizeof(float) * R * (size_t)N);
   L.total = o;
   return L;
 }
@@ -161,6 +161,7 @@ nvfp4_status nvfp4_grouped_linear(int32_t act_kind, const void* x, const uint8_t
   if (T <= 0 || N <= 0 || T > kMaxDim || N > kMaxDim || T * top_k > kMaxDim) return NVFP4_ERR_SHAPE;
   if (out_mode == NVFP4_OUT_SWIGLU_BF16 && N % 2 != 0) return NVFP4_ERR_SHAPE;
   if ((int64_t)num_experts * N * (K / 2) > ((int64_t)1 << 46)) return NVFP4_ERR_SHAPE;
+  if (N * (K / 2) > kMaxBufferBytes) return NVFP4_ERR_SHAPE;  // one expert, 32-bit offsets
   const Layout L = grouped_layout(T, top_k, num_experts, N, out_mode);
   if (!workspace) {
     *workspace_bytes = L.total;
@@ -192,7 +193,12 @@ nvfp4_status nvfp4_grouped_linear(int32_t act_kind, const void* x, const uint8_t
   ws.order = reinterpret_cast<int32_t*>(base + L.order);
   ws.rows = reinterpret_cast<float*>(base + L.rows);
 
-  hipError_t e = launch_route_sort(topk_ids, T, top_k, num_experts, ws, faults, s);
+  // dropped routes read as zero rows in the per-route output forms; the grouping kernel
+  // clears them
+  void* zero_out = out_mode == NVFP4_OUT_COMBINE ? nullptr : y;
+  const int64_t zero_row_bytes = out_mode == NVFP4_OUT_ROUTES ? N * 4 : N;  // fp32 / BF16 N/2
+  hipError_t e = launch_route_sort(topk_ids, T, top_k, num_experts, ws, faults, zero_out,
+                                   zero_row_bytes, s);
   if (e != hipSuccess) return NVFP4_ERR_LAUNCH;
 
   const int64_t R = T * top_k;
@@ -210,21 +216,17 @@ nvfp4_status nvfp4_grouped_linear(int32_t act_kind, const void* x, const uint8_t
     a.M = (int32_t)((R + active - 1) / active);
   }
   if (out_mode == NVFP4_OUT_ROUTES) {
-    // dropped routes must read as zero rows: clear y first (a fill kernel, capture-safe)
     a.y = static_cast<float*>(y); a.ldy = N; a.apply_ts = 1;
+  } else if (out_mode == NVFP4_OUT_SWIGLU_BF16) {
+    // the streaming kernel's epilogue applies SwiGLU and writes the BF16 rows
+    a.a_out = static_cast<uint16_t*>(y); a.apply_ts = 1;
   } else {
-    a.y = ws.rows; a.ldy = N; a.apply_ts = out_mode == NVFP4_OUT_SWIGLU_BF16 ? 1 : 0;
+    a.y = ws.rows; a.ldy = N; a.apply_ts = 0;
   }
   const int max_active = (int)(R < num_experts ? R : num_experts);
-  if (out_mode == NVFP4_OUT_ROUTES) {
-    e = launch_zero_rows(static_cast<float*>(y), ws.route_expert, R, N, s);
-    if (e != hipSuccess) return NVFP4_ERR_LAUNCH;
-  }
   e = launch_stream(a, act_kind, true, max_active, s);
   if (e != hipSuccess) return NVFP4_ERR_LAUNCH;
-  if (out_mode == NVFP4_OUT_SWIGLU_BF16) {
-    e = launch_swiglu(ws.rows, ws.route_expert, R, N, static_cast<uint16_t*>(y), s);
-  } else if (out_mode == NVFP4_OUT_COMBINE) {
+  if (out_mode == NVFP4_OUT_COMBINE) {
     e = launch_combine(ws.rows, ws.route_expert, ws.order, topk_w, w_ts, T, top_k, N,
                        static_cast<float*>(y), s);
   }

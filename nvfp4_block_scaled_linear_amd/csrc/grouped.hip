@@ -1,4 +1,5 @@
-// Helpers of the expert-grouped call: route grouping, SwiGLU to BF16, ordered combine.
+// Helpers of the expert-grouped call: route grouping and the ordered combine (the SwiGLU
+// to BF16 is the streaming kernel's epilogue).
 //
 // Routes are grouped expert-ascending ("true rows, expert-ascending" with expert-first
 // offsets: Rocket log entry "Rank-local E256 MoE misses the Qwen K1 and K4 step
@@ -16,10 +17,23 @@ namespace {
 
 constexpr int kSortThreads = 1024;
 
+// Zeroes `bytes` bytes (even) of output row r of a dropped route; dword stores when the
+// row allows them.
+__device__ __forceinline__ void zero_route_row(void* out, int64_t bytes, int64_t r) {
+  if (!out) return;
+  char* row = static_cast<char*>(out) + r * bytes;
+  if ((bytes & 3) == 0 && ((uintptr_t)row & 3) == 0) {
+    for (int64_t b = 0; b < bytes; b += 4) *reinterpret_cast<uint32_t*>(row + b) = 0u;
+  } else {
+    for (int64_t b = 0; b < bytes; b += 2) *reinterpret_cast<uint16_t*>(row + b) = 0u;
+  }
+}
+
 // Single workgroup. E <= max_experts fits the LDS arrays sized at launch.
 __global__ __launch_bounds__(kSortThreads) void route_sort(const int32_t* ids, int64_t T,
                                                            int top_k, int E, RouteWorkspace ws,
-                                                           uint32_t* faults) {
+                                                           uint32_t* faults, void* zero_out,
+                                                           int64_t zero_row_bytes) {
   extern __shared__ int32_t sh[];
   int32_t* cnt = sh;             // [E]  route count per expert, later the running cursor
   int32_t* scan = sh + E;        // [E+1]
@@ -37,6 +51,7 @@ __global__ __launch_bounds__(kSortThreads) void route_sort(const int32_t* ids, i
     for (int jj = 0; jj < j && ok; jj++)
       if (ids[t * top_k + jj] == e) ok = false;
     ws.route_expert[r] = ok ? e : -1;
+    if (!ok) zero_route_row(zero_out, zero_row_bytes, r);
     bad = bad || !ok;
   }
   if (bad && faults) atomicOr(faults, (uint32_t)NVFP4_FAULT_BAD_ROUTE);
@@ -142,7 +157,8 @@ __device__ __forceinline__ int32_t block_exclusive_scan(int32_t v, int32_t* wsum
 __global__ __launch_bounds__(kSortThreads) void route_sort_fast(const int32_t* ids, int64_t T,
                                                                 int top_k, int E,
                                                                 RouteWorkspace ws,
-                                                                uint32_t* faults) {
+                                                                uint32_t* faults, void* zero_out,
+                                                                int64_t zero_row_bytes) {
   extern __shared__ __attribute__((aligned(16))) int32_t sh[];
   const int nt = blockDim.x;                // >= R, a multiple of 64
   int32_t* ids_s = sh;                      // [nt]
@@ -165,6 +181,7 @@ __global__ __launch_bounds__(kSortThreads) void route_sort_fast(const int32_t* i
     for (int r = t0; r < tid; r++) ok = ok && (ids_s[r] != e);
     my_e = ok ? e : -1;
     ws.route_expert[tid] = my_e;
+    if (!ok) zero_route_row(zero_out, zero_row_bytes, tid);
     if (!ok && faults) atomicOr(faults, (uint32_t)NVFP4_FAULT_BAD_ROUTE);
     if (ok) atomicAdd(&cnt[e], 1);  // integer count: order-independent
   }
@@ -219,26 +236,6 @@ __global__ __launch_bounds__(kSortThreads) void route_sort_fast(const int32_t* i
   }
 }
 
-// a[r][n] = bf16_rne(silu(h[r][n]) * h[r][n + N/2]), silu(g) = g / (1 + exp(-g))
-__global__ __launch_bounds__(256) void swiglu_kernel(const float* rows,
-                                                     const int32_t* route_expert, int64_t R,
-                                                     int64_t N, uint16_t* out) {
-  const int64_t half = N >> 1;
-  const int64_t total = R * half;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
-       i += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t r = i / half, n = i - r * half;
-    uint32_t bits = 0u;
-    if (route_expert[r] >= 0) {
-      const float g = rows[r * N + n];
-      const float u = rows[r * N + half + n];
-      const float silu = g / (1.0f + expf(-g));
-      bits = f32_to_bf16_rne(silu * u);
-    }
-    out[i] = (uint16_t)bits;
-  }
-}
-
 // y[t][n] = sum over the token's routes in ascending expert id of (w * ts_e) * row[n]
 __global__ __launch_bounds__(256) void combine_kernel(const float* rows,
                                                       const int32_t* route_expert,
@@ -261,16 +258,6 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* rows,
   }
 }
 
-// rows of dropped routes read as zero in the per-route output form
-__global__ __launch_bounds__(256) void zero_rows_kernel(float* y, const int32_t* route_expert,
-                                                        int64_t R, int64_t N) {
-  const int64_t total = R * N;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
-       i += (int64_t)gridDim.x * blockDim.x) {
-    if (route_expert[i / N] < 0) y[i] = 0.0f;
-  }
-}
-
 int64_t grid_for(int64_t total) {
   int64_t g = (total + 255) / 256;
   return g < 1 ? 1 : (g > 8192 ? 8192 : g);
@@ -279,31 +266,18 @@ int64_t grid_for(int64_t total) {
 }  // namespace
 
 hipError_t launch_route_sort(const int32_t* topk_ids, int64_t T, int top_k, int E,
-                             const RouteWorkspace& ws, uint32_t* faults, hipStream_t stream) {
+                             const RouteWorkspace& ws, uint32_t* faults, void* zero_out,
+                             int64_t zero_row_bytes, hipStream_t stream) {
   if (T * top_k <= kFastRoutes) {
     const int nt = (int)((T * top_k + 63) / 64 * 64);
     const size_t lds = sizeof(int32_t) * ((size_t)2 * nt + 16 + (size_t)E);
     hipLaunchKernelGGL(route_sort_fast, dim3(1), dim3(nt), lds, stream, topk_ids, T, top_k, E,
-                       ws, faults);
+                       ws, faults, zero_out, zero_row_bytes);
     return hipGetLastError();
   }
   const size_t lds = sizeof(int32_t) * ((size_t)2 * E + 1 + kSortThreads);
   hipLaunchKernelGGL(route_sort, dim3(1), dim3(kSortThreads), lds, stream, topk_ids, T, top_k, E,
-                     ws, faults);
-  return hipGetLastError();
-}
-
-hipError_t launch_zero_rows(float* y, const int32_t* route_expert, int64_t R, int64_t N,
-                            hipStream_t stream) {
-  hipLaunchKernelGGL(zero_rows_kernel, dim3((uint32_t)grid_for(R * N)), dim3(256), 0, stream, y,
-                     route_expert, R, N);
-  return hipGetLastError();
-}
-
-hipError_t launch_swiglu(const float* rows, const int32_t* route_expert, int64_t R, int64_t N,
-                         uint16_t* out, hipStream_t stream) {
-  hipLaunchKernelGGL(swiglu_kernel, dim3((uint32_t)grid_for(R * (N / 2))), dim3(256), 0, stream,
-                     rows, route_expert, R, N, out);
+                     ws, faults, zero_out, zero_row_bytes);
   return hipGetLastError();
 }
 

@@ -33,6 +33,9 @@ struct StreamArgs {
   const int32_t* n_active;   // [1]
   int32_t rows_per_token;    // x row of route r: r / top_k (1) or r (0)
   int32_t top_k;
+  // grouped gate_up with the SwiGLU epilogue (NULL otherwise): a[route][n] =
+  // bf16(silu(h[n]) * h[n + N/2]) for n < N/2, BF16 rows of N/2 values
+  uint16_t* a_out;
 };
 
 hipError_t launch_stream(const StreamArgs& a, int act_kind, bool grouped, int max_active,
@@ -73,12 +76,11 @@ struct RouteWorkspace {
   float* rows;            // [R][N] fp32 per-route rows (SwiGLU / combine forms)
 };
 
+// also zeroes output row r (zero_row_bytes bytes of zero_out, when not NULL) of every
+// dropped route
 hipError_t launch_route_sort(const int32_t* topk_ids, int64_t T, int top_k, int E,
-                             const RouteWorkspace& ws, uint32_t* faults, hipStream_t stream);
-hipError_t launch_zero_rows(float* y, const int32_t* route_expert, int64_t R, int64_t N,
-                            hipStream_t stream);
-hipError_t launch_swiglu(const float* rows, const int32_t* route_expert, int64_t R, int64_t N,
-                         uint16_t* out, hipStream_t stream);
+                             const RouteWorkspace& ws, uint32_t* faults, void* zero_out,
+                             int64_t zero_row_bytes, hipStream_t stream);
 hipError_t launch_combine(const float* rows, const int32_t* route_expert, const int32_t* order,
                           const float* topk_w, const float* w_ts, int64_t T, int top_k,
                           int64_t N, float* y, hipStream_t stream);

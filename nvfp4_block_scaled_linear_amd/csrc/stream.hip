@@ -108,10 +108,12 @@ __host__ __device__ __forceinline__ size_t lds_bytes(int TN, int R, int W, int64
   return stream > red ? stream : red;
 }
 
+// Tile t of the workgroup is weight rows n0 + t * tstride + [0, 16), of which the first
+// lim[t] exist (rows past them read as zero).
 template <int TN, int R, int ACT, bool SLDS>
 __device__ __forceinline__ void pass4(const StreamArgs& a, const uint8_t* wc, const uint8_t* ws,
-                                      int64_t n0, const RowMap& rm, uint8_t* lds,
-                                      f32x4 (&acc)[TN][R]) {
+                                      int64_t n0, int64_t tstride, const int (&lim)[TN],
+                                      const RowMap& rm, uint8_t* lds, f32x4 (&acc)[TN][R]) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // scalar: uniform guards
   const int W = blockDim.x >> 6;
@@ -131,15 +133,17 @@ __device__ __forceinline__ void pass4(const StreamArgs& a, const uint8_t* wc, co
 #pragma unroll
     for (int r = 0; r < R; r++) acc[t][r] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int64_t rows_here = (a.N - n0) < 16 * TN ? (a.N - n0) : 16 * TN;
-  const auto wr = make_rsrc(wc + n0 * kb, (uint32_t)(rows_here * kb));
-  const auto sr = make_rsrc(ws + n0 * sb, (uint32_t)(rows_here * sb));
+  // descriptors over the rows the tiles span (up to the end of the matrix)
+  int64_t span = (TN - 1) * tstride + 16;
+  span = (a.N - n0) < span ? (a.N - n0) : span;
+  const auto wr = make_rsrc(wc + n0 * kb, (uint32_t)(span * kb));
+  const auto sr = make_rsrc(ws + n0 * sb, (uint32_t)(span * sb));
   uint32_t wrow[TN], srow[TN];
 #pragma unroll
   for (int t = 0; t < TN; t++) {
-    const bool ok = 16 * t + nl < rows_here;
-    wrow[t] = ok ? (uint32_t)((16 * t + nl) * kb) : kOOB;
-    srow[t] = ok ? (uint32_t)((16 * t + nl) * sb) : kOOB;
+    const bool ok = nl < lim[t];
+    wrow[t] = ok ? (uint32_t)((t * tstride + nl) * kb) : kOOB;
+    srow[t] = ok ? (uint32_t)((t * tstride + nl) * sb) : kOOB;
   }
   __amdgpu_buffer_rsrc_t xr, xsr;
   if (ACT == 0) {
@@ -253,14 +257,26 @@ __device__ __forceinline__ void pass4(const StreamArgs& a, const uint8_t* wc, co
   // the copy is waited on, so the two latencies overlap.
   constexpr int kScaleRegs = 4;  // 16-byte scale chunks per thread held in flight
   u32x4 sreg[kScaleRegs];
-  const uint32_t s_chunks = (uint32_t)((rows_here * sb + 15) >> 4);
   const uint32_t chunks_per_row = sb >> 4;  // SLDS requires K % 256 == 0
+  const uint32_t s_chunks = 16u * TN * chunks_per_row;  // 16 LDS rows per tile
+  // chunk c: tile c / (16 * chunks_per_row), row (c / chunks_per_row) % 16
+  auto chunk_src = [&](uint32_t cidx) -> uint32_t {
+    const uint32_t lrow = cidx / chunks_per_row, col = (cidx % chunks_per_row) * 16;
+    const int t = (int)(lrow >> 4), row = (int)(lrow & 15);
+    bool ok = cidx < s_chunks;
+    uint32_t off = 0;
+#pragma unroll
+    for (int tt = 0; tt < TN; tt++)
+      if (tt == t) {
+        ok = ok && row < lim[tt];
+        off = (uint32_t)((tt * tstride + row) * sb) + col;
+      }
+    return ok ? off : kOOB;
+  };
   if (SLDS) {
 #pragma unroll
-    for (int qq = 0; qq < kScaleRegs; qq++) {
-      const uint32_t cidx = threadIdx.x + qq * blockDim.x;
-      sreg[qq] = __builtin_amdgcn_raw_buffer_load_b128(sr, cidx < s_chunks ? cidx * 16u : kOOB, 0, 0);
-    }
+    for (int qq = 0; qq < kScaleRegs; qq++)
+      sreg[qq] = __builtin_amdgcn_raw_buffer_load_b128(sr, chunk_src(threadIdx.x + qq * blockDim.x), 0, 0);
   }
   StepBuf<TN, R, ACT> buf[kDepth];
 #pragma unroll
@@ -269,7 +285,7 @@ __device__ __forceinline__ void pass4(const StreamArgs& a, const uint8_t* wc, co
     load_scales(j, j);
   }
   if (SLDS) {
-    // Chunks past the tile go to the spare 16 bytes after the scale rows, so the stores
+    // Chunks past the tiles go to the spare 16 bytes after the scale rows, so the stores
     // need no branch (a branch would make the wave wait for every load in flight).
     const uint32_t spare = 16u * TN * sls;
     auto put = [&](uint32_t cidx, u32x4 v) {
@@ -285,7 +301,7 @@ __device__ __forceinline__ void pass4(const StreamArgs& a, const uint8_t* wc, co
     for (int qq = 0; qq < kScaleRegs; qq++) put(threadIdx.x + qq * blockDim.x, sreg[qq]);
     // tiles with more chunks than the prefetch holds copy the rest directly
     for (uint32_t cidx = threadIdx.x + kScaleRegs * blockDim.x; cidx < s_chunks; cidx += blockDim.x)
-      put(cidx, __builtin_amdgcn_raw_buffer_load_b128(sr, cidx * 16u, 0, 0));
+      put(cidx, __builtin_amdgcn_raw_buffer_load_b128(sr, chunk_src(cidx), 0, 0));
     __syncthreads();
   }
   // Rounds of kDepth steps; every round but the last refills the ring, the last one only
@@ -357,8 +373,14 @@ __global__ __launch_bounds__(256) void stream_dense(StreamArgs a) {
       rm.soff[r] = ok ? (uint32_t)(m * (a.K >> 4)) : kOOB;
     }
   }
+  int lim[TN];
+#pragma unroll
+  for (int t = 0; t < TN; t++) {
+    const int64_t left = a.N - n0 - 16 * t;
+    lim[t] = left < 0 ? 0 : (left > 16 ? 16 : (int)left);
+  }
   f32x4 acc[TN][R];
-  pass4<TN, R, ACT, SLDS>(a, a.w_codes, a.w_scales, n0, rm, lds, acc);
+  pass4<TN, R, ACT, SLDS>(a, a.w_codes, a.w_scales, n0, 16, lim, rm, lds, acc);
   const float ts = a.apply_ts ? a.w_ts[0] : 1.0f;
   reduce_store<TN, R>(acc, red, n0, [&](int m, int64_t n, float s) {
     if (m < a.M && n < a.N) {
@@ -399,7 +421,8 @@ __global__ __launch_bounds__(256) void stream_grouped(StreamArgs a) {
       }
     }
     f32x4 acc[1][R];
-    pass4<1, R, ACT, SLDS>(a, wc, ws, n0, rm, lds, acc);
+    const int lim[1] = {(int)((a.N - n0) < 16 ? (a.N - n0) : 16)};
+    pass4<1, R, ACT, SLDS>(a, wc, ws, n0, 16, lim, rm, lds, acc);
     reduce_store<1, R>(acc, red, n0, [&](int m, int64_t n, float s) {
       if (m < rows && n < a.N) {
         const int rr = a.sorted[c0 + m];
@@ -412,6 +435,99 @@ __global__ __launch_bounds__(256) void stream_grouped(StreamArgs a) {
       }
     });
   }
+}
+
+// Grouped gate_up with the SwiGLU epilogue: the workgroup streams gate rows n0 + [0, 16)
+// and the matching up rows N/2 + n0 + [0, 16) of its expert as two tiles, reduces both in
+// the same fixed order as reduce_store, and writes a = bf16_rne(silu(g) * u) where g and
+// u are exactly the per-route rows' fp32 values (sum times the same scale factor) and
+// silu(g) = g / (1 + expf(-g)).
+template <int R, int ACT, bool SLDS>
+__global__ __launch_bounds__(256) void stream_grouped_swiglu(StreamArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  float* red = reinterpret_cast<float*>(lds);
+  const int slot = blockIdx.y;
+  if (slot >= *a.n_active) return;  // uniform over the workgroup
+  const int e = a.active[slot];
+  const int beg = a.offsets[e], end = a.offsets[e + 1];
+  const uint8_t* wc = a.w_codes + (int64_t)e * a.N * (a.K >> 1);
+  const uint8_t* ws = a.w_scales + (int64_t)e * a.N * (a.K >> 4);
+  const float ts = a.w_ts[e];
+  const int64_t half = a.N >> 1;
+  const int64_t n0 = (int64_t)blockIdx.x * 16;
+  const int vr = (int)((half - n0) < 16 ? (half - n0) : 16);
+  const int lim[2] = {vr, vr};
+  const int i = (threadIdx.x >> 4) & 3;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int W = blockDim.x >> 6;
+  for (int c0 = beg; c0 < end; c0 += 4 * R) {
+    const int rows = min(4 * R, end - c0);
+    RowMap rm;
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+      const int m = 4 * r + i;
+      const bool ok = r < R && m < rows;
+      const int route = a.sorted[c0 + (ok ? m : 0)];
+      const int64_t xrow = a.rows_per_token ? route / a.top_k : route;
+      if (ACT == 0) {
+        rm.off[r] = ok ? (uint32_t)(xrow * a.ldx * 2) : kOOB;
+        rm.soff[r] = kOOB;
+      } else {
+        rm.off[r] = ok ? (uint32_t)(xrow * (a.K >> 1)) : kOOB;
+        rm.soff[r] = ok ? (uint32_t)(xrow * (a.K >> 4)) : kOOB;
+      }
+    }
+    f32x4 acc[2][R];
+    pass4<2, R, ACT, SLDS>(a, wc, ws, n0, half, lim, rm, lds, acc);
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < 2; t++)
+#pragma unroll
+      for (int r = 0; r < R; r++)
+        *reinterpret_cast<f32x4*>(red + (((wave * 2 + t) * R + r) * 64 + lane) * 4) = acc[t][r];
+    __syncthreads();
+    for (int o = threadIdx.x; o < R * 64; o += blockDim.x) {
+      const int nl = o & 15, q = (o >> 4) & 3, r = o >> 6;
+      const int lane0 = 4 * (nl >> 2) + (nl & 3);
+      float sg = 0.f, su = 0.f;
+      for (int w = 0; w < W; w++)
+#pragma unroll
+        for (int gg = 0; gg < 4; gg++) {
+          sg += red[(((w * 2 + 0) * R + r) * 64 + lane0 + 16 * gg) * 4 + q];
+          su += red[(((w * 2 + 1) * R + r) * 64 + lane0 + 16 * gg) * 4 + q];
+        }
+      const int m = 4 * r + q;
+      const int64_t n = n0 + nl;
+      if (m < rows && n < half) {
+        const int rr = a.sorted[c0 + m];
+        float f = ts;
+        if (ACT != 0) {
+          const int64_t xrr = a.rows_per_token ? rr / a.top_k : rr;
+          f = a.x_ts[xrr] * ts;
+        }
+        const float g = sg * f;
+        const float u = su * f;
+        const float silu = g / (1.0f + expf(-g));
+        a.a_out[(int64_t)rr * half + n] = (uint16_t)f32_to_bf16_rne(silu * u);
+      }
+    }
+    __syncthreads();
+  }
+}
+
+template <int R, int ACT>
+hipError_t launch_grouped_swiglu(const StreamArgs& a, int max_active, int W, bool slds,
+                                 hipStream_t stream) {
+  const size_t lds = lds_bytes(2, R, W, a.K, slds);
+  const int64_t groups = ((a.N >> 1) + 15) / 16;
+  if (slds)
+    hipLaunchKernelGGL((stream_grouped_swiglu<R, ACT, true>),
+                       dim3((uint32_t)groups, (uint32_t)max_active), dim3(64 * W), lds, stream, a);
+  else
+    hipLaunchKernelGGL((stream_grouped_swiglu<R, ACT, false>),
+                       dim3((uint32_t)groups, (uint32_t)max_active), dim3(64 * W), lds, stream, a);
+  return hipGetLastError();
 }
 
 template <int TN, int R, int ACT>
@@ -492,6 +608,18 @@ int pick_tn(int64_t N) {
 hipError_t launch_stream_cfg(const StreamArgs& a, int act_kind, bool grouped, int max_active,
                              int tn, int W, hipStream_t stream) {
   if (W < 1 || W > 4) return hipErrorInvalidValue;
+  if (grouped && a.a_out) {
+    const bool slds = use_lds_scales(a, 2);
+    const int R = a.M > 0 ? (a.M + 3) / 4 : 1;
+    switch (R) {
+      case 1: return act_kind == 0 ? launch_grouped_swiglu<1, 0>(a, max_active, W, slds, stream)
+                                   : launch_grouped_swiglu<1, 1>(a, max_active, W, slds, stream);
+      case 2: return act_kind == 0 ? launch_grouped_swiglu<2, 0>(a, max_active, W, slds, stream)
+                                   : launch_grouped_swiglu<2, 1>(a, max_active, W, slds, stream);
+      default: return act_kind == 0 ? launch_grouped_swiglu<4, 0>(a, max_active, W, slds, stream)
+                                    : launch_grouped_swiglu<4, 1>(a, max_active, W, slds, stream);
+    }
+  }
   const bool slds = use_lds_scales(a, grouped ? 1 : tn);
   if (grouped) {
     // rows of one expert pass in sets of four: one set covers decode-sized loads

@@ -84,6 +84,10 @@ def test_moe_swiglu_bf16(dev, o, moe):
     assert np.all(diff <= 1), np.argwhere(diff > 1)[:5]
     assert exact >= 0.999, exact
     _say(f"SwiGLU BF16 bit-exact fraction {exact:.6f}")
+    for _ in range(2):  # deterministic
+        a2 = nv.grouped_linear(moe["x_d"], moe["gc"], moe["gs"], moe["gt"], moe["ids_d"],
+                               out_mode=nv.OUT_SWIGLU_BF16)
+        assert torch.equal(a2.view(torch.int16), a.view(torch.int16))
 
 
 def test_moe_down_combine_and_end_to_end(dev, o, moe):
@@ -155,6 +159,21 @@ def test_grouped_bad_routes_flagged_and_dropped(dev, o):
                 e = ids[t, j]
                 yr, b = o.linear(xb[t:t + 1], ws[e][1][0], ws[e][1][1], ws[e][1][2])
                 assert_within(h[r:r + 1], yr, b, f"route {t},{j}")
+    # the SwiGLU form: dropped routes give zero rows too (the output buffer starts dirty)
+    a = torch.full((T * k, N // 2), 0x7F7F, dtype=torch.int16, device=dev).view(torch.bfloat16)
+    nv.grouped_linear(to_dev_bf16(xb, dev), wc, wsc, wts, torch.from_numpy(ids).to(dev),
+                      out_mode=nv.OUT_SWIGLU_BF16, out=a)
+    a_bits = a.view(torch.int16).cpu().numpy().view(np.uint16)
+    ref = o.swiglu(h.astype(np.float64))
+    ref_bits = np.array([o.bf16_round(v) for v in ref.ravel()], np.uint16).reshape(ref.shape)
+    for t in range(T):
+        for j in range(k):
+            r = t * k + j
+            if (t, j) in dropped:
+                assert np.all(a_bits[r] == 0), (t, j)
+            else:
+                d = np.abs(a_bits[r].astype(np.int32) - ref_bits[r].astype(np.int32))
+                assert np.all(d <= 1), (t, j)
 
 
 def test_grouped_w4a4_and_many_routes_per_expert(dev, o):
