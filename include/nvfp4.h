@@ -132,9 +132,8 @@ nvfp4_status nvfp4_quantize_act(int32_t in_type, const void* x, int64_t ldx, int
  *          NVFP4_OUT_SWIGLU_BF16: N even; y is BF16 bits [T*top_k][N/2], row r =
  *            bf16_rne(silu(g) * u) with g = h[0:N/2], u = h[N/2:N] of the route's fp32
  *            row h (SwiGLU rounded once to BF16, as the pages keep the down input in
- *            BF16 rounded to nearest even: issue #565 section 4, PR #914); h is never
- *            stored (the SwiGLU is the streaming kernel's epilogue) and bit-equals the
- *            NVFP4_OUT_ROUTES row.
+ *            BF16 rounded to nearest even: issue #565 section 4, PR #914); h
+ *            bit-equals the NVFP4_OUT_ROUTES row of the same call shape.
  *          NVFP4_OUT_COMBINE: needs topk_w [T][top_k] fp32; y is fp32 [T][N],
  *            y[t] = sum over t's routes in ascending expert id of
  *            (topk_w[t][j] * ts_e) * (x_row(r) w_e^T), accumulated in fp32 in that order
@@ -142,8 +141,13 @@ nvfp4_status nvfp4_quantize_act(int32_t in_type, const void* x, int64_t ldx, int
  *            Rocket log entry "The expert split decodes the same tokens; ...", section
  *            "Why rows and not partial sums").
  * topk_w is ignored unless out_mode is NVFP4_OUT_COMBINE.
- * workspace: device scratch (route grouping; for NVFP4_OUT_COMBINE also the fp32
- *   per-route rows); pass workspace = NULL to receive the needed size in
+ * Decode-sized batches stream each active expert's weight once for all its routes;
+ *   prompt-sized ones (routes averaging >= 32 per active expert) run MFMA tiles of one
+ *   expert's routes (the pages' expert-grouped prompt GEMM, each expert read once per
+ *   batch: issue #565 section 4, PR #740).
+ * workspace: device scratch (route grouping; the fp32 per-route rows for
+ *   NVFP4_OUT_COMBINE, and for NVFP4_OUT_SWIGLU_BF16 on prompt-sized batches); pass
+ *   workspace = NULL to receive the needed size in
  *   *workspace_bytes (nothing is enqueued); otherwise *workspace_bytes is its size.
  * Sizes: one expert's codes (N * K/2 bytes) must fit 32-bit offsets.
  * Expert ids out of range or repeated within a token set NVFP4_FAULT_BAD_ROUTE; such

@@ -49,9 +49,20 @@ nvfp4_status check_k(int64_t K) {
   return NVFP4_OK;
 }
 
+// The grouped call takes the MFMA GEMM path when its routes average at least this many per
+// active expert (prompt-sized batches); below it, the weight-streaming kernel.
+constexpr int64_t kGroupedGemmRoutes = 32;
+
+bool grouped_uses_gemm(int64_t T, int top_k, int E) {
+  const int64_t R = T * top_k;
+  const int64_t active = R < E ? R : E;
+  return R >= kGroupedGemmRoutes * active;
+}
+
 // grouped-call workspace layout: 256-byte aligned regions
 struct Layout {
-  size_t offsets, active, n_active, route_expert, sorted, order, rows, total;
+  size_t offsets, active, n_active, route_expert, sorted, order, rows, tiles, n_tiles, total;
+  int64_t max_tiles;
 };
 
 size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -59,6 +70,9 @@ size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
 Layout grouped_layout(int64_t T, int top_k, int E, int64_t N, int32_t out_mode) {
   Layout L;
   const size_t R = (size_t)T * (size_t)top_k;
+  const bool gemm = grouped_uses_gemm(T, top_k, E);
+  const int64_t tr = gemm_grouped_tile_rows();
+  L.max_tiles = gemm ? ((int64_t)R + tr - 1) / tr + E : 0;  // one partial tile per expert
   size_t o = 0;
   L.offsets = o; o = up256(o + sizeof(int32_t) * ((size_t)E + 1));
   L.active = o; o = up256(o + sizeof(int32_t) * (size_t)E);
@@ -66,8 +80,11 @@ Layout grouped_layout(int64_t T, int top_k, int E, int64_t N, int32_t out_mode) 
   L.route_expert = o; o = up256(o + sizeof(int32_t) * R);
   L.sorted = o; o = up256(o + sizeof(int32_t) * R);
   L.order = o; o = up256(o + sizeof(int32_t) * R);
+  L.tiles = o; o = up256(o + sizeof(int32_t) * 2 * (size_t)L.max_tiles);
+  L.n_tiles = o; o = up256(o + sizeof(int32_t));
   L.rows = o;
-  if (out_mode == NVFP4_OUT_COMBINE) o = up256(o + sizeof(float) * R * (size_t)N);
+  if (out_mode == NVFP4_OUT_COMBINE || (gemm && out_mode == NVFP4_OUT_SWIGLU_BF16))
+    o = up256(o + sizeof(float) * R * (size_t)N);
   L.total = o;
   return L;
 }
@@ -192,6 +209,10 @@ nvfp4_status nvfp4_grouped_linear(int32_t act_kind, const void* x, const uint8_t
   ws.sorted = reinterpret_cast<int32_t*>(base + L.sorted);
   ws.order = reinterpret_cast<int32_t*>(base + L.order);
   ws.rows = reinterpret_cast<float*>(base + L.rows);
+  ws.tiles = reinterpret_cast<int32_t*>(base + L.tiles);
+  ws.n_tiles = reinterpret_cast<int32_t*>(base + L.n_tiles);
+  const bool gemm = L.max_tiles > 0;
+  ws.tile_rows = gemm ? gemm_grouped_tile_rows() : 0;
 
   // dropped routes read as zero rows in the per-route output forms; the grouping kernel
   // clears them
@@ -202,6 +223,31 @@ nvfp4_status nvfp4_grouped_linear(int32_t act_kind, const void* x, const uint8_t
   if (e != hipSuccess) return NVFP4_ERR_LAUNCH;
 
   const int64_t R = T * top_k;
+  if (gemm) {
+    // prompt-sized: MFMA tiles of one expert's routes
+    GemmArgs g{};
+    g.x = x; g.x_scales = x_scales; g.x_ts = x_ts; g.ldx = ldx;
+    g.w_codes = w_codes; g.w_scales = w_scales; g.w_ts = w_ts;
+    g.N = N; g.K = K;
+    g.tiles = ws.tiles; g.n_tiles = ws.n_tiles; g.offsets = ws.offsets; g.sorted = ws.sorted;
+    g.x_rows = rows_mode == NVFP4_ROWS_PER_TOKEN ? T : T * top_k;
+    g.rows_per_token = rows_mode == NVFP4_ROWS_PER_TOKEN ? 1 : 0;
+    g.top_k = top_k;
+    if (out_mode == NVFP4_OUT_ROUTES) {
+      g.y = static_cast<float*>(y); g.ldy = N; g.apply_ts = 1;
+    } else {
+      g.y = ws.rows; g.ldy = N; g.apply_ts = out_mode == NVFP4_OUT_SWIGLU_BF16 ? 1 : 0;
+    }
+    e = launch_gemm_grouped(g, act_kind, L.max_tiles, s);
+    if (e != hipSuccess) return NVFP4_ERR_LAUNCH;
+    if (out_mode == NVFP4_OUT_SWIGLU_BF16) {
+      e = launch_swiglu_rows(ws.rows, ws.route_expert, R, N, static_cast<uint16_t*>(y), s);
+    } else if (out_mode == NVFP4_OUT_COMBINE) {
+      e = launch_combine(ws.rows, ws.route_expert, ws.order, topk_w, w_ts, T, top_k, N,
+                         static_cast<float*>(y), s);
+    }
+    return launch_status(e);
+  }
   StreamArgs a{};
   a.x = x; a.x_scales = x_scales; a.x_ts = x_ts; a.ldx = ldx;
   a.w_codes = w_codes; a.w_scales = w_scales; a.w_ts = w_ts;

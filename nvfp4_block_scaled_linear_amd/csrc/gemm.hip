@@ -57,43 +57,84 @@ struct RegB {  // one K step of this lane's weight loads (two 32-column subtiles
   uint32_t s[2];
 };
 
-template <int MT, int ACT>
+// GROUPED: the expert-grouped form. A workgroup takes tile blockIdx.x / nbn of the route
+// grouping's tile list (tile_rows = BM routes of one expert), gathers those routes'
+// activation rows through a row table in LDS, multiplies them by that expert's weight and
+// writes each result to its route's output row; the per-row arithmetic (k order, MFMA
+// shape, epilogue) is the dense form's, so a route's row equals the dense product of its
+// activation row with the expert's weight.
+template <int MT, int ACT, bool GROUPED = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_kernel(GemmArgs a) {
   constexpr int BM = 32 * MT;
   extern __shared__ __attribute__((aligned(16))) uint16_t lds_a[];  // [2][BM * LDA]
+  __shared__ int32_t row_x[GROUPED ? BM : 1];      // x row of each tile row (-1: none)
+  __shared__ int32_t row_route[GROUPED ? BM : 1];  // route of each tile row
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int64_t M = a.M, N = a.N, K = a.K;
   const uint32_t Ku = (uint32_t)K;
+  const int64_t nbn = (N + BN - 1) / BN;
 
-  // XCD-aware tile order: consecutive tiles of one XCD share the same M rows.
-  const int64_t nbm = (M + BM - 1) / BM, nbn = (N + BN - 1) / BN;
-  const int64_t total = nbm * nbn;
-  const int64_t bid = blockIdx.x;
-  int64_t lin = bid;
-  if (total % 8 == 0) lin = (bid % 8) * (total / 8) + bid / 8;
-  const int64_t m0 = (lin / nbn) * BM;
-  const int64_t n0 = (lin % nbn) * BN;
-  const int64_t rows_m = (M - m0) < BM ? (M - m0) : BM;
+  int64_t m0 = 0, n0, rows_m;
+  const uint8_t* wcodes = a.w_codes;
+  const uint8_t* wscales = a.w_scales;
+  float ts = a.w_ts[0];
+  if (GROUPED) {
+    const int64_t tile = blockIdx.x / nbn;
+    if (tile >= *a.n_tiles) return;  // uniform over the workgroup
+    const int e = a.tiles[2 * tile];
+    const int32_t beg = a.tiles[2 * tile + 1];
+    const int32_t end = a.offsets[e + 1];
+    rows_m = (end - beg) < BM ? (end - beg) : BM;
+    n0 = (blockIdx.x % nbn) * BN;
+    wcodes += (int64_t)e * N * (K >> 1);
+    wscales += (int64_t)e * N * (K >> 4);
+    ts = a.apply_ts ? a.w_ts[e] : 1.0f;
+    for (int i = tid; i < BM; i += 256) {
+      const int32_t route = i < rows_m ? a.sorted[beg + i] : -1;
+      row_route[i] = route;
+      row_x[i] = route < 0 ? -1 : (a.rows_per_token ? route / a.top_k : route);
+    }
+    __syncthreads();
+  } else {
+    // XCD-aware tile order: consecutive tiles of one XCD share the same M rows.
+    const int64_t nbm = (M + BM - 1) / BM;
+    const int64_t total = nbm * nbn;
+    const int64_t bid = blockIdx.x;
+    int64_t lin = bid;
+    if (total % 8 == 0) lin = (bid % 8) * (total / 8) + bid / 8;
+    m0 = (lin / nbn) * BM;
+    n0 = (lin % nbn) * BN;
+    rows_m = (M - m0) < BM ? (M - m0) : BM;
+  }
   const int64_t rows_n = (N - n0) < BN ? (N - n0) : BN;
 
-  // activation descriptors over this tile's rows
+  // activation descriptors: this tile's rows (dense) or all of x (grouped)
   __amdgpu_buffer_rsrc_t xr, xsr;
-  if (ACT == 0) {
-    xr = rsrc(static_cast<const uint16_t*>(a.x) + m0 * a.ldx, ((rows_m - 1) * a.ldx + K) * 2);
-    xsr = xr;
-  } else {
-    xr = rsrc(static_cast<const uint8_t*>(a.x) + m0 * (K >> 1), rows_m * (K >> 1));
-    xsr = rsrc(a.x_scales + m0 * (K >> 4), rows_m * (K >> 4));
+  {
+    const int64_t xrow0 = GROUPED ? 0 : m0;
+    const int64_t nrows = GROUPED ? a.x_rows : rows_m;
+    if (ACT == 0) {
+      xr = rsrc(static_cast<const uint16_t*>(a.x) + xrow0 * a.ldx, ((nrows - 1) * a.ldx + K) * 2);
+      xsr = xr;
+    } else {
+      xr = rsrc(static_cast<const uint8_t*>(a.x) + xrow0 * (K >> 1), nrows * (K >> 1));
+      xsr = rsrc(a.x_scales + xrow0 * (K >> 4), nrows * (K >> 4));
+    }
   }
+  // x row read for tile row `row` (relative to the descriptor), or -1
+  auto xrow_of = [&](int row) -> int64_t {
+    if (GROUPED) return row_x[row];
+    return row < rows_m ? row : -1;
+  };
   // weight descriptors over this tile's columns; lane (col, h): two 32-column subtiles,
   // K half h of each 64-k step
   const int col = lane & 31;
   const int h = lane >> 5;
-  const auto wr = rsrc(a.w_codes + n0 * (K >> 1), rows_n * (K >> 1));
-  const auto sr = rsrc(a.w_scales + n0 * (K >> 4), rows_n * (K >> 4));
+  const auto wr = rsrc(wcodes + n0 * (K >> 1), rows_n * (K >> 1));
+  const auto sr = rsrc(wscales + n0 * (K >> 4), rows_n * (K >> 4));
   uint32_t woff[2], soff[2];
 #pragma unroll
   for (int st = 0; st < 2; st++) {
@@ -113,7 +154,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const int c = tid + 256 * q;
         const int row = c >> 3, ch = c & 7;
         const uint32_t k = k0 + 8u * ch;
-        const uint32_t off = (uint32_t)(row * a.ldx * 2) + 2u * k;
+        const int64_t xrow = xrow_of(row);
+        const uint32_t off = xrow < 0 ? kOOB : (uint32_t)(xrow * a.ldx * 2) + 2u * k;
         ra.v[q] = __builtin_amdgcn_raw_buffer_load_b128(xr, off | past(Ku, k), 0, 0);
       }
     } else {
@@ -122,10 +164,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const int p = tid + 256 * q;
         const int row = p >> 3, j = p & 7;
         const uint32_t k = k0 + 8u * j;
-        ra.c[q] = __builtin_amdgcn_raw_buffer_load_b32(
-            xr, ((uint32_t)(row * (K >> 1)) + (k >> 1)) | past(Ku, k), 0, 0);
-        ra.s[q] = __builtin_amdgcn_raw_buffer_load_b8(
-            xsr, ((uint32_t)(row * (K >> 4)) + (k >> 4)) | past(Ku, k), 0, 0);
+        const int64_t xrow = xrow_of(row);
+        const uint32_t oc = xrow < 0 ? kOOB : (uint32_t)(xrow * (K >> 1)) + (k >> 1);
+        const uint32_t os = xrow < 0 ? kOOB : (uint32_t)(xrow * (K >> 4)) + (k >> 4);
+        ra.c[q] = __builtin_amdgcn_raw_buffer_load_b32(xr, oc | past(Ku, k), 0, 0);
+        ra.s[q] = __builtin_amdgcn_raw_buffer_load_b8(xsr, os | past(Ku, k), 0, 0);
       }
     }
     const uint32_t kh = k0 + 32u * h;
@@ -218,14 +261,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     body(kt + 1, ra1, rb1, ra0, rb0, Bd1, Bd0);
   }
 
-  const float ts = a.w_ts[0];
 #pragma unroll
   for (int mt = 0; mt < MT; mt++) {
 #pragma unroll
     for (int r = 0; r < 16; r++) {
-      const int64_t row = m0 + 32 * mt + 8 * (r >> 2) + 4 * h + (r & 3);
-      if (row >= M) continue;
-      const float f = (ACT == 0) ? ts : a.x_ts[row] * ts;
+      const int lrow = 32 * mt + 8 * (r >> 2) + 4 * h + (r & 3);
+      int64_t row, xrow;
+      if (GROUPED) {
+        row = row_route[lrow];
+        xrow = row_x[lrow];
+        if (row < 0) continue;
+      } else {
+        row = m0 + lrow;
+        xrow = row;
+        if (row >= M) continue;
+      }
+      const float f = (ACT == 0) ? ts : a.x_ts[xrow] * ts;
 #pragma unroll
       for (int st = 0; st < 2; st++) {
         const int64_t n = n0 + 64 * wave + 32 * st + col;
@@ -429,7 +480,28 @@ bool use_wide(int64_t M, int64_t N) {
   return ((M + kWideBM - 1) / kWideBM) * ((N + BN - 1) / BN) >= 256;
 }
 
+// grouped form: 128-route tiles, two workgroups per CU
+constexpr int kGroupedMT = 4;
+
+template <int ACT>
+hipError_t launch_grouped_mt(const GemmArgs& a, int64_t max_tiles, hipStream_t stream) {
+  constexpr int BM = 32 * kGroupedMT;
+  const int64_t blocks = max_tiles * ((a.N + BN - 1) / BN);
+  const size_t lds = 2 * (size_t)BM * LDA * sizeof(uint16_t);
+  hipLaunchKernelGGL((gemm_kernel<kGroupedMT, ACT, true>), dim3((uint32_t)blocks), dim3(256), lds,
+                     stream, a);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+int gemm_grouped_tile_rows() { return 32 * kGroupedMT; }
+
+hipError_t launch_gemm_grouped(const GemmArgs& a, int act_kind, int64_t max_tiles,
+                               hipStream_t stream) {
+  return act_kind == 0 ? launch_grouped_mt<0>(a, max_tiles, stream)
+                       : launch_grouped_mt<1>(a, max_tiles, stream);
+}
 
 // Largest activation row pitch (elements) the GEMM's 32-bit buffer offsets can address
 // for a 256-row tile.

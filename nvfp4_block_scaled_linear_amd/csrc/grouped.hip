@@ -29,106 +29,16 @@ __device__ __forceinline__ void zero_route_row(void* out, int64_t bytes, int64_t
   }
 }
 
-// Single workgroup. E <= max_experts fits the LDS arrays sized at launch.
-__global__ __launch_bounds__(kSortThreads) void route_sort(const int32_t* ids, int64_t T,
-                                                           int top_k, int E, RouteWorkspace ws,
-                                                           uint32_t* faults, void* zero_out,
-                                                           int64_t zero_row_bytes) {
-  extern __shared__ int32_t sh[];
-  int32_t* cnt = sh;             // [E]  route count per expert, later the running cursor
-  int32_t* scan = sh + E;        // [E+1]
-  int32_t* chunk_e = sh + 2 * E + 1;  // [kSortThreads] experts of the current chunk
-  const int64_t R = T * top_k;
-  const int tid = threadIdx.x;
-
-  // (1) validate: id in range and not repeated earlier in its token; dropped -> -1
-  bool bad = false;
-  for (int64_t r = tid; r < R; r += kSortThreads) {
-    const int32_t e = ids[r];
-    bool ok = (e >= 0 && e < E);
-    const int64_t t = r / top_k;
-    const int j = (int)(r - t * top_k);
-    for (int jj = 0; jj < j && ok; jj++)
-      if (ids[t * top_k + jj] == e) ok = false;
-    ws.route_expert[r] = ok ? e : -1;
-    if (!ok) zero_route_row(zero_out, zero_row_bytes, r);
-    bad = bad || !ok;
-  }
-  if (bad && faults) atomicOr(faults, (uint32_t)NVFP4_FAULT_BAD_ROUTE);
-  for (int e = tid; e < E; e += kSortThreads) cnt[e] = 0;
-  __syncthreads();
-
-  // (2) histogram (integer atomics: order-independent)
-  for (int64_t r = tid; r < R; r += kSortThreads) {
-    const int32_t e = ws.route_expert[r];
-    if (e >= 0) atomicAdd(&cnt[e], 1);
-  }
-  __syncthreads();
-
-  // (3) exclusive scan of counts and of the active flags (thread 0: E is small)
-  if (tid == 0) {
-    int32_t run = 0, act = 0;
-    for (int e = 0; e < E; e++) {
-      scan[e] = run;
-      ws.offsets[e] = run;
-      run += cnt[e];
-      if (cnt[e] > 0) ws.active[act++] = e;
-    }
-    scan[E] = run;
-    ws.offsets[E] = run;
-    *ws.n_active = act;
-  }
-  __syncthreads();
-  for (int e = tid; e < E; e += kSortThreads) cnt[e] = scan[e];  // cursors
-  __syncthreads();
-
-  // (4) stable scatter, chunk by chunk in route order
-  for (int64_t c0 = 0; c0 < R; c0 += kSortThreads) {
-    const int64_t r = c0 + tid;
-    const int32_t e = (r < R) ? ws.route_expert[r] : -1;
-    chunk_e[tid] = e;
-    __syncthreads();
-    int rank = 0;
-    bool last = true;
-    if (e >= 0) {
-      for (int i = 0; i < tid; i++) rank += (chunk_e[i] == e);
-      const int lim = (int)((R - c0) < kSortThreads ? (R - c0) : kSortThreads);
-      for (int i = tid + 1; i < lim && last; i++) last = (chunk_e[i] != e);
-      ws.sorted[cnt[e] + rank] = (int32_t)r;
-    }
-    __syncthreads();  // every cursor read of this chunk is done
-    if (e >= 0 && last) cnt[e] += rank + 1;  // one writer per expert: its last route
-    __syncthreads();
-  }
-
-  // (5) per token: its route slots in ascending expert id, dropped routes last (-1)
-  for (int64_t t = tid; t < T; t += kSortThreads) {
-    int32_t* o = ws.order + t * top_k;
-    int n = 0;
-    for (int j = 0; j < top_k; j++)
-      if (ws.route_expert[t * top_k + j] >= 0) o[n++] = j;
-    for (int i = 1; i < n; i++) {  // insertion sort by expert id
-      const int32_t v = o[i];
-      const int32_t ev = ws.route_expert[t * top_k + v];
-      int p = i - 1;
-      while (p >= 0 && ws.route_expert[t * top_k + o[p]] > ev) {
-        o[p + 1] = o[p];
-        p--;
-      }
-      o[p + 1] = v;
-    }
-    for (int j = n; j < top_k; j++) o[j] = -1;
+// Tile list of the GEMM path: expert e's routes sorted[off, off + cnt) split into tiles
+// of ws.tile_rows routes; tile_off is e's first tile.
+__device__ __forceinline__ void write_tiles(const RouteWorkspace& ws, int e, int32_t off,
+                                            int32_t cnt, int32_t tile_off) {
+  const int32_t nt = (cnt + ws.tile_rows - 1) / ws.tile_rows;
+  for (int32_t i = 0; i < nt; i++) {
+    ws.tiles[2 * (tile_off + i)] = e;
+    ws.tiles[2 * (tile_off + i) + 1] = off + i * ws.tile_rows;
   }
 }
-
-// Decode-sized route sets (R <= kFastRoutes): the same result as route_sort, computed in
-// LDS with no dependent global-memory round trips. One route per thread (the block is
-// sized to R); the expert offsets and the active-expert list come from block-wide scans;
-// a route's place among its expert's routes is the number of earlier routes with the
-// same expert (stable, counted with 16-byte LDS reads); its slot within its token is the
-// number of the token's valid routes with a smaller expert id (valid ids are distinct
-// within a token); the slots after them hold -1, as in route_sort.
-constexpr int kFastRoutes = kSortThreads;
 
 // Exclusive prefix sum over the block: a shuffle scan inside each wave, then the wave
 // totals through LDS (two barriers). `wsum` holds blockDim.x / 64 entries.
@@ -153,6 +63,96 @@ __device__ __forceinline__ int32_t block_exclusive_scan(int32_t v, int32_t* wsum
   __syncthreads();  // wsum is reused by the next scan
   return base + x - v;
 }
+
+// Offsets, the active list and the tile list from the per-expert counts in cnt[E] (LDS);
+// afterwards cnt[e] holds expert e's first slot in `sorted`.
+__device__ __forceinline__ void expert_scans(const RouteWorkspace& ws, int E, int32_t* cnt,
+                                             int32_t* wsum) {
+  const int tid = threadIdx.x, nt = blockDim.x;
+  int32_t run = 0, act_run = 0, tile_run = 0;
+  for (int e0 = 0; e0 < E; e0 += nt) {
+    const int e = e0 + tid;
+    const int32_t c = e < E ? cnt[e] : 0;
+    const int32_t ntile = ws.tile_rows > 0 ? (c + ws.tile_rows - 1) / ws.tile_rows : 0;
+    int32_t tot, tot_a, tot_t;
+    const int32_t o = block_exclusive_scan(c, wsum, &tot) + run;
+    const int32_t a = block_exclusive_scan(c > 0 ? 1 : 0, wsum, &tot_a) + act_run;
+    const int32_t to = block_exclusive_scan(ntile, wsum, &tot_t) + tile_run;
+    if (e < E) {
+      ws.offsets[e] = o;
+      if (c > 0) ws.active[a] = e;
+      if (ntile > 0) write_tiles(ws, e, o, c, to);
+      cnt[e] = o;
+    }
+    run += tot;
+    act_run += tot_a;
+    tile_run += tot_t;
+  }
+  if (tid == 0) {
+    ws.offsets[E] = run;
+    *ws.n_active = act_run;
+    if (ws.tile_rows > 0) *ws.n_tiles = tile_run;
+  }
+  __syncthreads();
+}
+
+// Single workgroup, any number of routes. The same offsets, active list, tile list and
+// per-token order as route_sort_fast; the order of routes within one expert's group is
+// unspecified here (atomic cursors), which no output depends on: every route's row is
+// computed from its own activation row and its expert alone.
+__global__ __launch_bounds__(kSortThreads) void route_sort(const int32_t* ids, int64_t T,
+                                                           int top_k, int E, RouteWorkspace ws,
+                                                           uint32_t* faults, void* zero_out,
+                                                           int64_t zero_row_bytes) {
+  extern __shared__ int32_t sh[];
+  int32_t* wsum = sh;       // [16]
+  int32_t* cnt = sh + 16;   // [E] routes per expert, then the scatter cursors
+  const int64_t R = T * top_k;
+  const int tid = threadIdx.x;
+  for (int e = tid; e < E; e += kSortThreads) cnt[e] = 0;
+  __syncthreads();
+
+  // (1) validate: id in range and not repeated earlier in its token; dropped -> -1
+  bool bad = false;
+  for (int64_t r = tid; r < R; r += kSortThreads) {
+    const int32_t e = ids[r];
+    bool ok = (e >= 0 && e < E);
+    const int64_t t0 = (r / top_k) * top_k;
+    for (int64_t rr = t0; rr < r; rr++) ok = ok && (ids[rr] != e);
+    ws.route_expert[r] = ok ? e : -1;
+    if (!ok) zero_route_row(zero_out, zero_row_bytes, r);
+    if (ok) atomicAdd(&cnt[e], 1);  // integer count: order-independent
+    bad = bad || !ok;
+  }
+  if (bad && faults) atomicOr(faults, (uint32_t)NVFP4_FAULT_BAD_ROUTE);
+  __threadfence();  // route_expert is read back below by other threads
+  __syncthreads();
+
+  // (2) offsets, active list, tile list; cnt becomes the scatter cursors
+  expert_scans(ws, E, cnt, wsum);
+
+  // (3) scatter and (4) each route's slot within its token
+  for (int64_t r = tid; r < R; r += kSortThreads) {
+    const int32_t e = ws.route_expert[r];
+    if (e >= 0) ws.sorted[atomicAdd(&cnt[e], 1)] = (int32_t)r;
+    const int64_t t0 = (r / top_k) * top_k;
+    int slot = 0;
+    for (int64_t rr = t0; rr < t0 + top_k; rr++) {
+      const int32_t er = ws.route_expert[rr];
+      slot += (e >= 0) ? (er >= 0 && er < e) : ((er >= 0) || (rr < r));
+    }
+    ws.order[t0 + slot] = e >= 0 ? (int32_t)(r - t0) : -1;
+  }
+}
+
+// Decode-sized route sets (R <= kFastRoutes): the same result as route_sort, computed in
+// LDS with no dependent global-memory round trips. One route per thread (the block is
+// sized to R); the expert offsets and the active-expert list come from block-wide scans;
+// a route's place among its expert's routes is the number of earlier routes with the
+// same expert (stable, counted with 16-byte LDS reads); its slot within its token is the
+// number of the token's valid routes with a smaller expert id (valid ids are distinct
+// within a token); the slots after them hold -1, as in route_sort.
+constexpr int kFastRoutes = kSortThreads;
 
 __global__ __launch_bounds__(kSortThreads) void route_sort_fast(const int32_t* ids, int64_t T,
                                                                 int top_k, int E,
@@ -188,28 +188,8 @@ __global__ __launch_bounds__(kSortThreads) void route_sort_fast(const int32_t* i
   rexp[tid] = my_e;
   __syncthreads();
 
-  // offsets and the active list: exclusive scans over the experts, one per thread per
-  // chunk of nt experts
-  int32_t run = 0, act_run = 0, my_off = 0;
-  for (int e0 = 0; e0 < E; e0 += nt) {
-    const int e = e0 + tid;
-    const int32_t c = e < E ? cnt[e] : 0;
-    int32_t tot, tot_a;
-    const int32_t o = block_exclusive_scan(c, wsum, &tot) + run;
-    const int32_t a = block_exclusive_scan(c > 0 ? 1 : 0, wsum, &tot_a) + act_run;
-    if (e < E) {
-      ws.offsets[e] = o;
-      if (c > 0) ws.active[a] = e;
-      cnt[e] = o;  // now the expert's first sorted slot
-    }
-    run += tot;
-    act_run += tot_a;
-  }
-  if (tid == 0) {
-    ws.offsets[E] = run;
-    *ws.n_active = act_run;
-  }
-  __syncthreads();
+  // offsets, active list, tile list; cnt becomes each expert's first slot
+  expert_scans(ws, E, cnt, wsum);
 
   if (tid < R) {
     const int t0 = (tid / top_k) * top_k;
@@ -233,6 +213,27 @@ __global__ __launch_bounds__(kSortThreads) void route_sort_fast(const int32_t* i
       for (int r = t0; r < tid; r++) slot += (rexp[r] < 0);
     }
     ws.order[t0 + slot] = my_e >= 0 ? tid - t0 : -1;
+  }
+}
+
+// GEMM path of the SwiGLU form: a[r][n] = bf16_rne(silu(h[r][n]) * h[r][n + N/2]) from the
+// fp32 per-route rows h, silu(g) = g / (1 + expf(-g)); dropped routes give zero rows.
+__global__ __launch_bounds__(256) void swiglu_rows_kernel(const float* rows,
+                                                          const int32_t* route_expert,
+                                                          int64_t R, int64_t N, uint16_t* out) {
+  const int64_t half = N >> 1;
+  const int64_t total = R * half;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = i / half, n = i - r * half;
+    uint32_t bits = 0u;
+    if (route_expert[r] >= 0) {
+      const float g = rows[r * N + n];
+      const float u = rows[r * N + half + n];
+      const float silu = g / (1.0f + expf(-g));
+      bits = f32_to_bf16_rne(silu * u);
+    }
+    out[i] = (uint16_t)bits;
   }
 }
 
@@ -275,9 +276,16 @@ hipError_t launch_route_sort(const int32_t* topk_ids, int64_t T, int top_k, int 
                        ws, faults, zero_out, zero_row_bytes);
     return hipGetLastError();
   }
-  const size_t lds = sizeof(int32_t) * ((size_t)2 * E + 1 + kSortThreads);
+  const size_t lds = sizeof(int32_t) * (16 + (size_t)E);
   hipLaunchKernelGGL(route_sort, dim3(1), dim3(kSortThreads), lds, stream, topk_ids, T, top_k, E,
                      ws, faults, zero_out, zero_row_bytes);
+  return hipGetLastError();
+}
+
+hipError_t launch_swiglu_rows(const float* rows, const int32_t* route_expert, int64_t R,
+                              int64_t N, uint16_t* out, hipStream_t stream) {
+  hipLaunchKernelGGL(swiglu_rows_kernel, dim3((uint32_t)grid_for(R * (N / 2))), dim3(256), 0,
+                     stream, rows, route_expert, R, N, out);
   return hipGetLastError();
 }
 

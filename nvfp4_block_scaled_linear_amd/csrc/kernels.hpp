@@ -55,9 +55,24 @@ struct GemmArgs {
   int64_t M, N, K;
   float* y;
   int64_t ldy;
+  // grouped form (NULL tiles for dense): tiles of tile_rows routes of one expert, rows
+  // gathered from x by route, written to y row = route; w_* point at expert 0
+  const int32_t* tiles;      // [n_tiles][2] (expert, first slot in sorted)
+  const int32_t* n_tiles;    // [1]
+  const int32_t* offsets;    // [E+1]
+  const int32_t* sorted;     // route ids grouped by expert
+  int64_t x_rows;            // rows in x
+  int32_t rows_per_token;    // x row of route r: r / top_k (1) or r (0)
+  int32_t top_k;
+  int32_t apply_ts;          // multiply by the expert's tensor scale
 };
 
 hipError_t launch_gemm(const GemmArgs& a, int act_kind, hipStream_t stream);
+// grouped form: max_tiles bounds the tile list the route grouping writes
+hipError_t launch_gemm_grouped(const GemmArgs& a, int act_kind, int64_t max_tiles,
+                               hipStream_t stream);
+// routes per tile of the grouped GEMM
+int gemm_grouped_tile_rows();
 // largest BF16 activation row pitch (elements) the GEMM's buffer offsets address
 int64_t gemm_max_ldx();
 
@@ -73,7 +88,10 @@ struct RouteWorkspace {
   int32_t* route_expert;  // [R] expert of route r, or -1 when dropped
   int32_t* sorted;        // [R]
   int32_t* order;         // [T][top_k] token's route slots in ascending expert id (-1 last)
-  float* rows;            // [R][N] fp32 per-route rows (SwiGLU / combine forms)
+  float* rows;            // [R][N] fp32 per-route rows (combine form; SwiGLU on the GEMM path)
+  int32_t* tiles;         // GEMM path: [n_tiles][2] (expert, first slot in `sorted`)
+  int32_t* n_tiles;       // [1]
+  int32_t tile_rows;      // GEMM path: routes per tile (0: no tile list)
 };
 
 // also zeroes output row r (zero_row_bytes bytes of zero_out, when not NULL) of every
@@ -81,6 +99,8 @@ struct RouteWorkspace {
 hipError_t launch_route_sort(const int32_t* topk_ids, int64_t T, int top_k, int E,
                              const RouteWorkspace& ws, uint32_t* faults, void* zero_out,
                              int64_t zero_row_bytes, hipStream_t stream);
+hipError_t launch_swiglu_rows(const float* rows, const int32_t* route_expert, int64_t R,
+                              int64_t N, uint16_t* out, hipStream_t stream);
 hipError_t launch_combine(const float* rows, const int32_t* route_expert, const int32_t* order,
                           const float* topk_w, const float* w_ts, int64_t T, int top_k,
                           int64_t N, float* y, hipStream_t stream);

@@ -258,3 +258,73 @@ def test_grouped_many_routes_general_sort(dev, o):
         e = int(ids[t, j])
         yr, b = o.linear(xb[t:t + 1], oc[e], os_[e], ot[e:e + 1])
         assert_within(h[r:r + 1], yr, b, f"many routes: route {t},{j}")
+
+
+def _prefill_case(dev, o, E, N, K, T, k, seed):
+    wc, wsc, wts, oc, os_, ot = _small_experts(o, dev, E, N, K, seed)
+    ids, rw = moe_routes(seed + 1, T, E, k)
+    ids = ids.astype(np.int32)
+    xb = act_bf16(seed + 2, T, K)
+    return wc, wsc, wts, oc, os_, ot, ids, rw.astype(np.float32), xb
+
+
+def test_grouped_prefill_gemm(dev, o):
+    """Prompt-sized batches (routes average >= 32 per expert) take the MFMA GEMM path:
+    per-route rows vs the oracle, one route per token = the dense linear bit for bit,
+    SwiGLU from those rows, the ordered combine, determinism."""
+    E, N, K, T, k = 8, 96, 256, 512, 2
+    wc, wsc, wts, oc, os_, ot, ids, rw, xb = _prefill_case(dev, o, E, N, K, T, k, 101)
+    x = to_dev_bf16(xb, dev)
+    ids_d = torch.from_numpy(ids).to(dev)
+    h = nv.grouped_linear(x, wc, wsc, wts, ids_d)
+    hn = h.cpu().numpy()
+    for r in np.r_[0, 1, 511, 512, 1023, np.random.default_rng(7).choice(T * k, 40, replace=False)]:
+        t, j = divmod(int(r), k)
+        e = int(ids[t, j])
+        yr, b = o.linear(xb[t:t + 1], oc[e], os_[e], ot[e:e + 1])
+        assert_within(hn[r:r + 1], yr, b, f"prefill route {t},{j}")
+    assert torch.equal(nv.grouped_linear(x, wc, wsc, wts, ids_d), h)
+    # one route per token: each expert's rows equal the dense product
+    ids1 = ids_d[:, :1].contiguous()
+    h1 = nv.grouped_linear(x, wc, wsc, wts, ids1)
+    for e in range(E):
+        toks = np.nonzero(ids[:, 0] == e)[0]
+        if len(toks) <= 16:
+            continue
+        dense = nv.linear(x[torch.from_numpy(toks).to(dev)].contiguous(), wc[e], wsc[e], wts[e:e + 1])
+        assert torch.equal(h1[torch.from_numpy(toks).to(dev)], dense), e
+    # SwiGLU from the same rows
+    a = nv.grouped_linear(x, wc, wsc, wts, ids_d, out_mode=nv.OUT_SWIGLU_BF16)
+    a_bits = a.view(torch.int16).cpu().numpy().view(np.uint16)
+    ref = o.swiglu(hn.astype(np.float64))
+    ref_bits = np.array([o.bf16_round(v) for v in ref.ravel()], np.uint16).reshape(ref.shape)
+    assert np.all(np.abs(a_bits.astype(np.int32) - ref_bits.astype(np.int32)) <= 1)
+    # ordered combine
+    y = nv.grouped_linear(x, wc, wsc, wts, ids_d, topk_w=torch.from_numpy(rw).to(dev),
+                          out_mode=nv.OUT_COMBINE).cpu().numpy()
+    yr, b = o.moe_down_combine(np.repeat(xb, k, axis=0), ids, rw, oc, os_, ot)
+    assert_within(y, yr, b, "prefill combine")
+
+
+def test_grouped_prefill_gemm_many_routes(dev, o):
+    """More than 1024 routes: the general grouping (order inside an expert's group is not
+    fixed there) still gives bit-identical outputs run to run."""
+    E, N, K, T, k = 16, 64, 128, 1024, 4
+    wc, wsc, wts, oc, os_, ot, ids, rw, xb = _prefill_case(dev, o, E, N, K, T, k, 111)
+    x = to_dev_bf16(xb, dev)
+    ids_d = torch.from_numpy(ids).to(dev)
+    h = nv.grouped_linear(x, wc, wsc, wts, ids_d)
+    for _ in range(3):
+        assert torch.equal(nv.grouped_linear(x, wc, wsc, wts, ids_d), h)
+    hn = h.cpu().numpy()
+    for r in np.r_[0, 4095, np.random.default_rng(8).choice(T * k, 40, replace=False)]:
+        t, j = divmod(int(r), k)
+        e = int(ids[t, j])
+        yr, b = o.linear(xb[t:t + 1], oc[e], os_[e], ot[e:e + 1])
+        assert_within(hn[r:r + 1], yr, b, f"many-route prefill {t},{j}")
+    rw_d = torch.from_numpy(rw).to(dev)
+    y = nv.grouped_linear(x, wc, wsc, wts, ids_d, topk_w=rw_d, out_mode=nv.OUT_COMBINE)
+    assert torch.equal(nv.grouped_linear(x, wc, wsc, wts, ids_d, topk_w=rw_d,
+                                         out_mode=nv.OUT_COMBINE), y)
+    yr, b = o.moe_down_combine(np.repeat(xb, k, axis=0), ids, rw, oc, os_, ot)
+    assert_within(y.cpu().numpy(), yr, b, "many-route prefill combine")
