@@ -278,6 +278,47 @@ def bench_moe(nv, dev):
             "bytes": b}
 
 
+def bench_moe_prefill(nv, dev):
+    """The MoE layer at prompt size: 4096 tokens over the same 128 experts, top-8 (the
+    grouped GEMM path: each routed expert read once per batch)."""
+    from synth import WORKLOADS, act_bf16, moe_expert_weights, moe_routes
+    cfg = WORKLOADS["moe_decode"]
+    E, k = cfg["E"], cfg["top_k"]
+    T = 4096
+    gc, gs, gt, dc, ds, dt = [], [], [], [], [], []
+    for e in range(E):
+        gu, dn = moe_expert_weights(cfg["w_seed"], e, cfg["N_gu"], cfg["K_gu"], cfg["N_d"], cfg["K_d"])
+        c, s, t = quantize_weight(nv, gu, dev); gc.append(c); gs.append(s); gt.append(t)
+        c, s, t = quantize_weight(nv, dn, dev); dc.append(c); ds.append(s); dt.append(t)
+    st = (torch.stack(gc), torch.stack(gs), torch.cat(gt), torch.stack(dc), torch.stack(ds), torch.cat(dt))
+    ids, rw = moe_routes(cfg["route_seed"] + 1, T, E, k)
+    ids_d = torch.from_numpy(ids).to(dev)
+    rw_d = torch.from_numpy(rw).to(dev)
+    x = to_bf16(act_bf16(cfg["x_seed"] + 1, T, cfg["K_gu"]), dev)
+    a = torch.empty((T * k, cfg["N_gu"] // 2), dtype=torch.bfloat16, device=dev)
+    y = torch.empty((T, cfg["N_d"]), dtype=torch.float32, device=dev)
+    w1 = torch.empty(nv.grouped_workspace_size(T, k, cfg["N_gu"], cfg["K_gu"], E, nv.OUT_SWIGLU_BF16),
+                     dtype=torch.uint8, device=dev)
+    w2 = torch.empty(nv.grouped_workspace_size(T, k, cfg["N_d"], cfg["K_d"], E, nv.OUT_COMBINE),
+                     dtype=torch.uint8, device=dev)
+
+    def run():
+        nv.grouped_linear(x, st[0], st[1], st[2], ids_d, out_mode=nv.OUT_SWIGLU_BF16, out=a,
+                          workspace=w1)
+        nv.grouped_linear(a, st[3], st[4], st[5], ids_d, topk_w=rw_d, out_mode=nv.OUT_COMBINE,
+                          rows_per_route=True, out=y, workspace=w2)
+    g = capture(run)
+    timer = Timer()
+    warm_until(g.replay, 0.15)
+    ms = timer.time(g.replay, 10)
+    R = T * k
+    flops = 2.0 * R * (cfg["N_gu"] * cfg["K_gu"] + cfg["N_d"] * cfg["K_d"])
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"workload": f"{T} tokens, 128 experts, top-8, gate_up 2048->1536 + down 768->2048",
+            "us_layer": round(ms * 1e3, 2), "TFLOPs": round(tf, 1),
+            "frac_bf16_mfma": round(tf / BF16_PEAK_TFLOPS, 4), "flop": flops}
+
+
 def hbm_copy_probe(dev):
     """Device-to-device copy of 1 GiB: measured read+write bandwidth of a plain copy."""
     n = 1 << 29  # int16 elements = 1 GiB
@@ -410,7 +451,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--only", choices=["all", "decode", "single", "prefill", "w4a4", "moe"],
+    ap.add_argument("--only", choices=["all", "decode", "single", "prefill", "w4a4", "moe",
+                                       "moe_prefill"],
                     default="all", help="run the decode sweep plus one other workload (all: every one)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--copy-probe", action="store_true", help="also time a 1 GiB device copy")
@@ -477,6 +519,9 @@ def main():
     if want("moe"):
         log("moe ...")
         rec["moe"] = bench_moe(nv, dev)
+    if want("moe_prefill"):
+        log("moe prefill ...")
+        rec["moe_prefill"] = bench_moe_prefill(nv, dev)
     if args.copy_probe or args.only == "all":
         rec["hbm_copy_GBps"] = hbm_copy_probe(dev)
     if not args.no_cpu:

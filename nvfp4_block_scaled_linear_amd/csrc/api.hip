@@ -83,8 +83,7 @@ Layout grouped_layout(int64_t T, int top_k, int E, int64_t N, int32_t out_mode) 
   L.tiles = o; o = up256(o + sizeof(int32_t) * 2 * (size_t)L.max_tiles);
   L.n_tiles = o; o = up256(o + sizeof(int32_t));
   L.rows = o;
-  if (out_mode == NVFP4_OUT_COMBINE || (gemm && out_mode == NVFP4_OUT_SWIGLU_BF16))
-    o = up256(o + sizeof(float) * R * (size_t)N);
+  if (out_mode == NVFP4_OUT_COMBINE) o = up256(o + sizeof(float) * R * (size_t)N);
   L.total = o;
   return L;
 }
@@ -235,14 +234,14 @@ nvfp4_status nvfp4_grouped_linear(int32_t act_kind, const void* x, const uint8_t
     g.top_k = top_k;
     if (out_mode == NVFP4_OUT_ROUTES) {
       g.y = static_cast<float*>(y); g.ldy = N; g.apply_ts = 1;
+    } else if (out_mode == NVFP4_OUT_SWIGLU_BF16) {
+      g.a_out = static_cast<uint16_t*>(y); g.apply_ts = 1;  // the GEMM's epilogue
     } else {
-      g.y = ws.rows; g.ldy = N; g.apply_ts = out_mode == NVFP4_OUT_SWIGLU_BF16 ? 1 : 0;
+      g.y = ws.rows; g.ldy = N; g.apply_ts = 0;
     }
     e = launch_gemm_grouped(g, act_kind, L.max_tiles, s);
     if (e != hipSuccess) return NVFP4_ERR_LAUNCH;
-    if (out_mode == NVFP4_OUT_SWIGLU_BF16) {
-      e = launch_swiglu_rows(ws.rows, ws.route_expert, R, N, static_cast<uint16_t*>(y), s);
-    } else if (out_mode == NVFP4_OUT_COMBINE) {
+    if (out_mode == NVFP4_OUT_COMBINE) {
       e = launch_combine(ws.rows, ws.route_expert, ws.order, topk_w, w_ts, T, top_k, N,
                          static_cast<float*>(y), s);
     }

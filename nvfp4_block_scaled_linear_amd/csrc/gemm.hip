@@ -63,7 +63,12 @@ struct RegB {  // one K step of this lane's weight loads (two 32-column subtiles
 // writes each result to its route's output row; the per-row arithmetic (k order, MFMA
 // shape, epilogue) is the dense form's, so a route's row equals the dense product of its
 // activation row with the expert's weight.
-template <int MT, int ACT, bool GROUPED = false>
+//
+// SWIGLU (grouped only): the tile's 256 columns are 128 gate columns (waves 0, 1) and the
+// matching 128 up columns N/2 + ... (waves 2, 3); the up waves hand their scaled results
+// to the gate waves through LDS in the same register layout, and the gate waves write
+// bf16_rne(silu(g) * u) to a_out, g and u being exactly the per-route rows' values.
+template <int MT, int ACT, bool GROUPED = false, bool SWIGLU = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_kernel(GemmArgs a) {
   constexpr int BM = 32 * MT;
   extern __shared__ __attribute__((aligned(16))) uint16_t lds_a[];  // [2][BM * LDA]
@@ -75,7 +80,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int wave = tid >> 6;
   const int64_t M = a.M, N = a.N, K = a.K;
   const uint32_t Ku = (uint32_t)K;
-  const int64_t nbn = (N + BN - 1) / BN;
+  const int64_t half = N >> 1;
+  const int64_t nbn = SWIGLU ? (half + BN / 2 - 1) / (BN / 2) : (N + BN - 1) / BN;
 
   int64_t m0 = 0, n0, rows_m;
   const uint8_t* wcodes = a.w_codes;
@@ -110,6 +116,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     rows_m = (M - m0) < BM ? (M - m0) : BM;
   }
   const int64_t rows_n = (N - n0) < BN ? (N - n0) : BN;
+  // this wave's first weight column: n0 + 64 * wave, or for SwiGLU the gate half (waves
+  // 0, 1: n0 = tile * 128) and the matching up half (waves 2, 3)
+  const int64_t wcol0 = SWIGLU ? (wave < 2 ? 0 : half) + (blockIdx.x % nbn) * (BN / 2) + 64 * (wave & 1)
+                               : n0 + 64 * wave;
+  const int64_t col_end = SWIGLU ? (wave < 2 ? half : N) : N;
 
   // activation descriptors: this tile's rows (dense) or all of x (grouped)
   __amdgpu_buffer_rsrc_t xr, xsr;
@@ -133,14 +144,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // K half h of each 64-k step
   const int col = lane & 31;
   const int h = lane >> 5;
-  const auto wr = rsrc(wcodes + n0 * (K >> 1), rows_n * (K >> 1));
-  const auto sr = rsrc(wscales + n0 * (K >> 4), rows_n * (K >> 4));
+  // descriptors over this tile's columns (dense) or the whole expert (grouped: its codes
+  // fit 32-bit offsets)
+  const int64_t wbase = GROUPED ? 0 : n0;
+  const int64_t wrows = GROUPED ? N : rows_n;
+  const auto wr = rsrc(wcodes + wbase * (K >> 1), wrows * (K >> 1));
+  const auto sr = rsrc(wscales + wbase * (K >> 4), wrows * (K >> 4));
   uint32_t woff[2], soff[2];
 #pragma unroll
   for (int st = 0; st < 2; st++) {
-    const int nl = 64 * wave + 32 * st + col;
-    woff[st] = nl < rows_n ? (uint32_t)(nl * (K >> 1)) : kOOB;
-    soff[st] = nl < rows_n ? (uint32_t)(nl * (K >> 4)) : kOOB;
+    const int64_t n = wcol0 + 32 * st + col;
+    const int64_t nl = n - wbase;
+    woff[st] = n < col_end ? (uint32_t)(nl * (K >> 1)) : kOOB;
+    soff[st] = n < col_end ? (uint32_t)(nl * (K >> 4)) : kOOB;
   }
 
   const int KT = (int)((K + BK - 1) / BK);
@@ -261,6 +277,47 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     body(kt + 1, ra1, rb1, ra0, rb0, Bd1, Bd0);
   }
 
+  if (SWIGLU) {
+    // up waves -> LDS (their own register layout) -> gate waves
+    float* xch = reinterpret_cast<float*>(lds_a);  // [2 waves][MT][2][16][64 lanes]
+    __syncthreads();
+    if (wave >= 2) {
+#pragma unroll
+      for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) {
+          const int lrow = 32 * mt + 8 * (r >> 2) + 4 * h + (r & 3);
+          const int64_t xrow = row_x[lrow];
+          const float f = (ACT == 0 || xrow < 0) ? ts : a.x_ts[xrow] * ts;
+#pragma unroll
+          for (int st = 0; st < 2; st++)
+            xch[((((wave - 2) * MT + mt) * 2 + st) * 16 + r) * 64 + lane] = acc[mt][st][r] * f;
+        }
+    }
+    __syncthreads();
+    if (wave < 2) {
+#pragma unroll
+      for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) {
+          const int lrow = 32 * mt + 8 * (r >> 2) + 4 * h + (r & 3);
+          const int64_t route = row_route[lrow];
+          if (route < 0) continue;
+          const int64_t xrow = row_x[lrow];
+          const float f = (ACT == 0) ? ts : a.x_ts[xrow] * ts;
+#pragma unroll
+          for (int st = 0; st < 2; st++) {
+            const int64_t n = wcol0 + 32 * st + col;
+            if (n >= half) continue;
+            const float g = acc[mt][st][r] * f;
+            const float u = xch[(((wave * MT + mt) * 2 + st) * 16 + r) * 64 + lane];
+            const float silu = g / (1.0f + expf(-g));
+            a.a_out[route * half + n] = (uint16_t)f32_to_bf16_rne(silu * u);
+          }
+        }
+    }
+    return;
+  }
 #pragma unroll
   for (int mt = 0; mt < MT; mt++) {
 #pragma unroll
@@ -486,10 +543,17 @@ constexpr int kGroupedMT = 4;
 template <int ACT>
 hipError_t launch_grouped_mt(const GemmArgs& a, int64_t max_tiles, hipStream_t stream) {
   constexpr int BM = 32 * kGroupedMT;
-  const int64_t blocks = max_tiles * ((a.N + BN - 1) / BN);
   const size_t lds = 2 * (size_t)BM * LDA * sizeof(uint16_t);
-  hipLaunchKernelGGL((gemm_kernel<kGroupedMT, ACT, true>), dim3((uint32_t)blocks), dim3(256), lds,
-                     stream, a);
+  if (a.a_out) {
+    const int64_t blocks = max_tiles * (((a.N >> 1) + BN / 2 - 1) / (BN / 2));
+    const size_t xch = (size_t)2 * kGroupedMT * 2 * 16 * 64 * sizeof(float);
+    hipLaunchKernelGGL((gemm_kernel<kGroupedMT, ACT, true, true>), dim3((uint32_t)blocks),
+                       dim3(256), lds > xch ? lds : xch, stream, a);
+  } else {
+    const int64_t blocks = max_tiles * ((a.N + BN - 1) / BN);
+    hipLaunchKernelGGL((gemm_kernel<kGroupedMT, ACT, true>), dim3((uint32_t)blocks), dim3(256),
+                       lds, stream, a);
+  }
   return hipGetLastError();
 }
 

@@ -145,6 +145,90 @@ __global__ __launch_bounds__(kSortThreads) void route_sort(const int32_t* ids, i
   }
 }
 
+// Any number of routes with top_k <= kRegTopK: each thread takes whole tokens, their ids
+// loaded together and validated, counted and placed in registers (no loop of dependent
+// global loads); the ids are re-read after the scans rather than kept across them. Same
+// outputs as route_sort (order inside an expert's group unspecified).
+constexpr int kRegTopK = 16;
+
+// KREG: the exact top_k (fully unrolled), or kRegTopK with top_k <= kRegTopK read at run time
+template <int KREG>
+__global__ __launch_bounds__(kSortThreads) void route_sort_tokens(const int32_t* ids, int64_t T,
+                                                                  int top_k_rt, int E,
+                                                                  RouteWorkspace ws,
+                                                                  uint32_t* faults,
+                                                                  void* zero_out,
+                                                                  int64_t zero_row_bytes) {
+  const int top_k = KREG == kRegTopK ? top_k_rt : KREG;
+  extern __shared__ int32_t sh[];
+  int32_t* wsum = sh;       // [16]
+  int32_t* cnt = sh + 16;   // [E] routes per expert, then the scatter cursors
+  const int tid = threadIdx.x;
+  for (int e = tid; e < E; e += kSortThreads) cnt[e] = 0;
+  __syncthreads();
+
+  // a token's ids and validity, in registers
+  auto load_token = [&](int64_t t, int32_t (&e)[KREG], bool (&ok)[KREG]) {
+#pragma unroll
+    for (int j = 0; j < KREG; j++) e[j] = j < top_k ? ids[t * top_k + j] : -1;
+#pragma unroll
+    for (int j = 0; j < KREG; j++) {
+      bool v = j < top_k && e[j] >= 0 && e[j] < E;
+#pragma unroll
+      for (int jj = 0; jj < j; jj++) v = v && e[jj] != e[j];
+      ok[j] = v;
+    }
+  };
+
+  bool bad = false;
+  for (int64_t t = tid; t < T; t += kSortThreads) {
+    int32_t e[KREG];
+    bool ok[KREG];
+    load_token(t, e, ok);
+#pragma unroll
+    for (int j = 0; j < KREG; j++) {
+      if (j >= top_k) break;
+      const int64_t r = t * top_k + j;
+      ws.route_expert[r] = ok[j] ? e[j] : -1;
+      if (ok[j]) {
+        atomicAdd(&cnt[e[j]], 1);  // integer count: order-independent
+      } else {
+        zero_route_row(zero_out, zero_row_bytes, r);
+        bad = true;
+      }
+    }
+  }
+  if (bad && faults) atomicOr(faults, (uint32_t)NVFP4_FAULT_BAD_ROUTE);
+  __syncthreads();
+
+  expert_scans(ws, E, cnt, wsum);
+
+  for (int64_t t = tid; t < T; t += kSortThreads) {
+    int32_t e[KREG];
+    bool ok[KREG];
+    load_token(t, e, ok);
+    int nvalid = 0;
+#pragma unroll
+    for (int j = 0; j < KREG; j++) nvalid += ok[j];
+    int ninvalid = 0;
+#pragma unroll
+    for (int j = 0; j < KREG; j++) {
+      if (j >= top_k) break;
+      const int64_t r = t * top_k + j;
+      int slot;
+      if (ok[j]) {
+        ws.sorted[atomicAdd(&cnt[e[j]], 1)] = (int32_t)r;
+        slot = 0;
+#pragma unroll
+        for (int jj = 0; jj < KREG; jj++) slot += (ok[jj] && e[jj] < e[j]);
+      } else {
+        slot = nvalid + ninvalid++;
+      }
+      ws.order[t * top_k + slot] = ok[j] ? j : -1;
+    }
+  }
+}
+
 // Decode-sized route sets (R <= kFastRoutes): the same result as route_sort, computed in
 // LDS with no dependent global-memory round trips. One route per thread (the block is
 // sized to R); the expert offsets and the active-expert list come from block-wide scans;
@@ -216,46 +300,71 @@ __global__ __launch_bounds__(kSortThreads) void route_sort_fast(const int32_t* i
   }
 }
 
-// GEMM path of the SwiGLU form: a[r][n] = bf16_rne(silu(h[r][n]) * h[r][n + N/2]) from the
-// fp32 per-route rows h, silu(g) = g / (1 + expf(-g)); dropped routes give zero rows.
-__global__ __launch_bounds__(256) void swiglu_rows_kernel(const float* rows,
-                                                          const int32_t* route_expert,
-                                                          int64_t R, int64_t N, uint16_t* out) {
-  const int64_t half = N >> 1;
-  const int64_t total = R * half;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
-       i += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t r = i / half, n = i - r * half;
-    uint32_t bits = 0u;
-    if (route_expert[r] >= 0) {
-      const float g = rows[r * N + n];
-      const float u = rows[r * N + half + n];
-      const float silu = g / (1.0f + expf(-g));
-      bits = f32_to_bf16_rne(silu * u);
-    }
-    out[i] = (uint16_t)bits;
-  }
-}
-
 // y[t][n] = sum over the token's routes in ascending expert id of (w * ts_e) * row[n]
+// One workgroup per (token, 1024 columns): the token's routes in ascending expert id and
+// their weights r * ts_e are staged in LDS once; each thread loads its four columns of
+// every route row before summing them with fmaf in that order, starting from zero.
+constexpr int kCombineMaxK = 64;
+
 __global__ __launch_bounds__(256) void combine_kernel(const float* rows,
                                                       const int32_t* route_expert,
                                                       const int32_t* order, const float* topk_w,
                                                       const float* w_ts, int64_t T, int top_k,
                                                       int64_t N, float* y) {
-  const int64_t total = T * N;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
-       i += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t t = i / N, n = i - t * N;
-    float acc = 0.0f;
+  __shared__ int32_t rr[kCombineMaxK];
+  __shared__ float wr[kCombineMaxK];
+  __shared__ int nr;
+  const int64_t t = blockIdx.x;
+  if (threadIdx.x == 0) {
+    int n = 0;
     for (int jj = 0; jj < top_k; jj++) {
       const int j = order[t * top_k + jj];
       if (j < 0) break;
       const int64_t r = t * top_k + j;
-      const float wr = topk_w[r] * w_ts[route_expert[r]];
-      acc = __builtin_fmaf(wr, rows[r * N + n], acc);
+      rr[n] = (int32_t)r;
+      wr[n] = topk_w[r] * w_ts[route_expert[r]];
+      n++;
     }
-    y[i] = acc;
+    nr = n;
+  }
+  __syncthreads();
+  const int n_routes = nr;
+  const int64_t n0 = (int64_t)blockIdx.y * 1024 + 4 * threadIdx.x;
+  if (n0 >= N) return;
+  const bool vec = n0 + 4 <= N && (N & 3) == 0;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  constexpr int kBatch = 8;  // route rows in flight per thread
+  for (int q0 = 0; q0 < n_routes; q0 += kBatch) {
+    float v[kBatch][4];
+#pragma unroll
+    for (int q = 0; q < kBatch; q++) {
+      if (q0 + q < n_routes) {
+        const float* src = rows + (int64_t)rr[q0 + q] * N + n0;
+        if (vec) {
+          const float4 f = *reinterpret_cast<const float4*>(src);
+          v[q][0] = f.x; v[q][1] = f.y; v[q][2] = f.z; v[q][3] = f.w;
+        } else {
+#pragma unroll
+          for (int c = 0; c < 4; c++) v[q][c] = n0 + c < N ? src[c] : 0.f;
+        }
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < kBatch; q++) {
+      if (q0 + q < n_routes) {
+        const float w = wr[q0 + q];
+#pragma unroll
+        for (int c = 0; c < 4; c++) acc[c] = __builtin_fmaf(w, v[q][c], acc[c]);
+      }
+    }
+  }
+  float* dst = y + t * N + n0;
+  if (vec) {
+    *reinterpret_cast<float4*>(dst) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+  } else {
+#pragma unroll
+    for (int c = 0; c < 4; c++)
+      if (n0 + c < N) dst[c] = acc[c];
   }
 }
 
@@ -277,23 +386,26 @@ hipError_t launch_route_sort(const int32_t* topk_ids, int64_t T, int top_k, int 
     return hipGetLastError();
   }
   const size_t lds = sizeof(int32_t) * (16 + (size_t)E);
+  if (top_k <= kRegTopK) {
+    auto k = top_k == 1 ? route_sort_tokens<1>
+           : top_k == 2 ? route_sort_tokens<2>
+           : top_k == 4 ? route_sort_tokens<4>
+           : top_k == 8 ? route_sort_tokens<8>
+                        : route_sort_tokens<kRegTopK>;
+    hipLaunchKernelGGL(k, dim3(1), dim3(kSortThreads), lds, stream, topk_ids, T, top_k, E, ws,
+                       faults, zero_out, zero_row_bytes);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(route_sort, dim3(1), dim3(kSortThreads), lds, stream, topk_ids, T, top_k, E,
                      ws, faults, zero_out, zero_row_bytes);
-  return hipGetLastError();
-}
-
-hipError_t launch_swiglu_rows(const float* rows, const int32_t* route_expert, int64_t R,
-                              int64_t N, uint16_t* out, hipStream_t stream) {
-  hipLaunchKernelGGL(swiglu_rows_kernel, dim3((uint32_t)grid_for(R * (N / 2))), dim3(256), 0,
-                     stream, rows, route_expert, R, N, out);
   return hipGetLastError();
 }
 
 hipError_t launch_combine(const float* rows, const int32_t* route_expert, const int32_t* order,
                           const float* topk_w, const float* w_ts, int64_t T, int top_k,
                           int64_t N, float* y, hipStream_t stream) {
-  hipLaunchKernelGGL(combine_kernel, dim3((uint32_t)grid_for(T * N)), dim3(256), 0, stream, rows,
-                     route_expert, order, topk_w, w_ts, T, top_k, N, y);
+  hipLaunchKernelGGL(combine_kernel, dim3((uint32_t)T, (uint32_t)((N + 1023) / 1024)), dim3(256),
+                     0, stream, rows, route_expert, order, topk_w, w_ts, T, top_k, N, y);
   return hipGetLastError();
 }
 

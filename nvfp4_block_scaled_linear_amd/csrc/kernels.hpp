@@ -65,6 +65,9 @@ struct GemmArgs {
   int32_t rows_per_token;    // x row of route r: r / top_k (1) or r (0)
   int32_t top_k;
   int32_t apply_ts;          // multiply by the expert's tensor scale
+  // grouped SwiGLU form (NULL otherwise): BF16 rows [routes][N/2] of
+  // bf16(silu(h[n]) * h[n + N/2])
+  uint16_t* a_out;
 };
 
 hipError_t launch_gemm(const GemmArgs& a, int act_kind, hipStream_t stream);
@@ -99,8 +102,6 @@ struct RouteWorkspace {
 hipError_t launch_route_sort(const int32_t* topk_ids, int64_t T, int top_k, int E,
                              const RouteWorkspace& ws, uint32_t* faults, void* zero_out,
                              int64_t zero_row_bytes, hipStream_t stream);
-hipError_t launch_swiglu_rows(const float* rows, const int32_t* route_expert, int64_t R,
-                              int64_t N, uint16_t* out, hipStream_t stream);
 hipError_t launch_combine(const float* rows, const int32_t* route_expert, const int32_t* order,
                           const float* topk_w, const float* w_ts, int64_t T, int top_k,
                           int64_t N, float* y, hipStream_t stream);
