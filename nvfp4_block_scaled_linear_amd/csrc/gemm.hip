@@ -25,6 +25,8 @@
 //    tiles that share activation rows (A-stationary), keeping the reused operand in its
 //    own L2.
 // The fp32 accumulator is scaled once by the tensor scale(s) in the epilogue.
+#include <type_traits>
+
 #include "device.hpp"
 #include "kernels.hpp"
 
@@ -513,6 +515,212 @@ __global__ __launch_bounds__(512) void gemm_wide(GemmArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------------------
+// gemm_splitk: problems whose 64 x 256 tiles leave most CUs idle (e.g. M = 512, N = 4096:
+// 128 tiles). A 64 (M) x 128 (N) tile on sixteen waves: four groups of four waves take
+// the four quarters of K, each wave computing 64 x 32 (two 32x32x16 subtiles) with its
+// own 32 weight columns decoded in registers, and each group staging its quarter's
+// activations through its own LDS buffers. The groups' partial tiles meet in LDS and are
+// added in a fixed order (quarter 0 + 1 + 2 + 3) before the one store. One workgroup per
+// CU and four waves per SIMD, so one wave's MFMAs overlap the others' decode work; no
+// workspace and no atomics.
+// ---------------------------------------------------------------------------------------
+constexpr int kSkBM = 64, kSkBN = 128, kSkSplit = 4;
+
+template <int ACT>
+struct SkRegA {  // one K step of this thread's activation loads (two 16-byte pieces)
+  u32x4 v[ACT == 0 ? 2 : 1];
+  uint32_t c[ACT == 0 ? 1 : 2];
+  uint32_t s[ACT == 0 ? 1 : 2];
+};
+struct SkRegB {  // one K step of this lane's weight column: 32 codes and their 2 scales
+  u32x4 c;
+  uint32_t s;
+};
+
+template <int ACT>
+__global__ __launch_bounds__(1024) void gemm_splitk(GemmArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t lds_k[];  // [4][2][BM * LDA]
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ks = wave >> 2, wn = wave & 3;  // K quarter, 32-column group
+  const int gt = tid & 255;                 // thread within the quarter's group
+  const int64_t M = a.M, N = a.N, K = a.K;
+  const uint32_t Ku = (uint32_t)K;
+
+  const int64_t nbm = (M + kSkBM - 1) / kSkBM, nbn = (N + kSkBN - 1) / kSkBN;
+  const int64_t total = nbm * nbn;
+  int64_t lin = blockIdx.x;
+  if (total % 8 == 0) lin = (lin % 8) * (total / 8) + lin / 8;  // XCD runs share rows
+  const int64_t m0 = (int64_t)__builtin_amdgcn_readfirstlane((int)(lin / nbn)) * kSkBM;
+  const int64_t n0 = (int64_t)__builtin_amdgcn_readfirstlane((int)(lin % nbn)) * kSkBN;
+  const int64_t rows_m = (M - m0) < kSkBM ? (M - m0) : kSkBM;
+  const int64_t rows_n = (N - n0) < kSkBN ? (N - n0) : kSkBN;
+
+  // this quarter's steps: kbeg .. kbeg + KTs - 1, run in whole rounds of four (padding
+  // steps and steps past K read zeros)
+  const int KT = (int)((K + BK - 1) / BK);
+  const int KTs = (KT + kSkSplit - 1) / kSkSplit;
+  const int kbeg = ks * KTs;
+  const int KT4 = (KTs + 3) & ~3;
+
+  __amdgpu_buffer_rsrc_t xr, xsr;
+  if (ACT == 0) {
+    xr = rsrc(static_cast<const uint16_t*>(a.x) + m0 * a.ldx, ((rows_m - 1) * a.ldx + K) * 2);
+    xsr = xr;
+  } else {
+    xr = rsrc(static_cast<const uint8_t*>(a.x) + m0 * (K >> 1), rows_m * (K >> 1));
+    xsr = rsrc(a.x_scales + m0 * (K >> 4), rows_m * (K >> 4));
+  }
+  // weights: lane (col, h) holds column n0 + 32 wn + col, K half h of each 64-k step
+  const int col = lane & 31;
+  const int h = lane >> 5;
+  const auto wr = rsrc(a.w_codes + n0 * (K >> 1), rows_n * (K >> 1));
+  const auto sr = rsrc(a.w_scales + n0 * (K >> 4), rows_n * (K >> 4));
+  const int nl = 32 * wn + col;
+  const uint32_t woff = nl < rows_n ? (uint32_t)(nl * (K >> 1)) : kOOB;
+  const uint32_t soff = nl < rows_n ? (uint32_t)(nl * (K >> 4)) : kOOB;
+  uint16_t* as = lds_k + ks * 2 * (kSkBM * LDA);  // this quarter's two buffers
+
+  auto issue = [&](int kt, SkRegA<ACT>& ra, SkRegB& rb) {
+    const uint32_t k0 = (uint32_t)(kbeg + kt) * BK;
+    const uint32_t out = kt < KTs ? 0u : kOOB;  // padding steps (uniform)
+#pragma unroll
+    for (int q = 0; q < 2; q++) {
+      const int c = gt + 256 * q;
+      const int row = c >> 3, ch = c & 7;
+      const uint32_t k = k0 + 8u * ch;
+      const uint32_t rowok = row < rows_m ? 0u : kOOB;
+      if (ACT == 0) {
+        const uint32_t off = (uint32_t)(row * a.ldx * 2) + 2u * k;
+        ra.v[q] = __builtin_amdgcn_raw_buffer_load_b128(xr, off | rowok | out | past(Ku, k), 0, 0);
+      } else {
+        // the step's four scale bytes of the row as one dword (K % 64 == 0 keeps it inside
+        // the row); the piece's byte is picked at staging
+        const uint32_t oc = (uint32_t)(row * (K >> 1)) + (k >> 1);
+        const uint32_t os = (uint32_t)(row * (K >> 4)) + (k0 >> 4);
+        ra.c[q] = __builtin_amdgcn_raw_buffer_load_b32(xr, oc | rowok | out | past(Ku, k), 0, 0);
+        ra.s[q] = __builtin_amdgcn_raw_buffer_load_b32(xsr, os | rowok | out | past(Ku, k0), 0, 0);
+      }
+    }
+    const uint32_t kh = k0 + 32u * h;
+    rb.c = __builtin_amdgcn_raw_buffer_load_b128(wr, (woff + (kh >> 1)) | out | past(Ku, kh), 0, 0);
+    // the step's four scale bytes (both halves) as one dword; this half's two are picked
+    // at decode (a 16-bit load here would leave a zero-extension that the compiler hoists
+    // to the loop head, waiting there for every load in flight)
+    rb.s = __builtin_amdgcn_raw_buffer_load_b32(sr, (soff + (k0 >> 4)) | out | past(Ku, k0), 0, 0);
+  };
+  auto write_a = [&](const SkRegA<ACT>& ra, int buf) {
+    uint16_t* dst = as + buf * (kSkBM * LDA);
+#pragma unroll
+    for (int q = 0; q < 2; q++) {
+      const int c = gt + 256 * q;
+      const int row = c >> 3, ch = c & 7;
+      u32x4 v;
+      if (ACT == 0) v = ra.v[q];
+      else v = decode8(ra.c[q], e4m3_to_f32<0>(ra.s[q] >> (8 * (ch >> 1))));  // exact BF16
+      *reinterpret_cast<u32x4*>(dst + row * LDA + 8 * ch) = v;
+    }
+  };
+  auto decode = [&](const SkRegB& rb, u32x4 (&bd)[4]) {
+    const uint32_t sw = rb.s >> (16 * h);
+    const float s0 = e4m3_to_f32<0>(sw), s1 = e4m3_to_f32<1>(sw);
+#pragma unroll
+    for (int j = 0; j < 4; j++) bd[j] = decode8(rb.c[j], j < 2 ? s0 : s1);
+  };
+
+  f32x16 acc[2];
+#pragma unroll
+  for (int mt = 0; mt < 2; mt++)
+#pragma unroll
+    for (int r = 0; r < 16; r++) acc[mt][r] = 0.f;
+
+  // Loads run four steps ahead in a ring of four register sets (the steps are short: a
+  // wave's step is eight MFMAs). Step kt multiplies LDS buffer kt & 1 with its decoded
+  // weights while decoding step kt + 1's weights and staging its activations into the
+  // other buffer, then refills the set it freed with step kt + 4.
+  SkRegA<ACT> ra[4];
+  SkRegB rb[4];
+  u32x4 bd[2][4];
+  auto step = [&](auto ic, int kt) {
+    constexpr int I = decltype(ic)::value;
+    constexpr int J = (I + 1) & 3;
+    const uint16_t* src = as + (kt & 1) * (kSkBM * LDA);
+    u32x4 af[8];
+#pragma unroll
+    for (int i = 0; i < 8; i++)
+      af[i] = *reinterpret_cast<const u32x4*>(src + (32 * (i & 1) + col) * LDA + 32 * h + 8 * (i >> 1));
+#pragma unroll
+    for (int i = 0; i < 8; i++) acc[i & 1] = mfma32(af[i], bd[I & 1][i >> 1], acc[i & 1]);
+    decode(rb[J], bd[J & 1]);
+    // interleave: operand reads two ahead of their MFMA, the next step's decode between
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                 // one MFMA
+      if (i < 6) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);      // one LDS read
+      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);                 // VALU
+    }
+    write_a(ra[J], (kt + 1) & 1);
+    __builtin_amdgcn_sched_barrier(0);
+    issue(kt + 4, ra[I], rb[I]);
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+  };
+
+#pragma unroll
+  for (int i = 0; i < 4; i++) issue(i, ra[i], rb[i]);
+  decode(rb[0], bd[0]);
+  write_a(ra[0], 0);
+  __syncthreads();
+  for (int kt = 0; kt < KT4; kt += 4) {
+    step(std::integral_constant<int, 0>{}, kt);
+    step(std::integral_constant<int, 1>{}, kt + 1);
+    step(std::integral_constant<int, 2>{}, kt + 2);
+    step(std::integral_constant<int, 3>{}, kt + 3);
+  }
+
+  // quarters 1..3 hand their partial tiles to quarter 0 through LDS (over the staging
+  // buffers: the loop ended with a barrier), which adds them in order
+  float* red = reinterpret_cast<float*>(lds_k);  // [3][4 wn][2 mt][16][64 lanes]
+  if (ks > 0) {
+#pragma unroll
+    for (int mt = 0; mt < 2; mt++)
+#pragma unroll
+      for (int r = 0; r < 16; r++)
+        red[((((ks - 1) * 4 + wn) * 2 + mt) * 16 + r) * 64 + lane] = acc[mt][r];
+  }
+  __syncthreads();
+  if (ks == 0) {
+    const float ts = a.w_ts[0];
+#pragma unroll
+    for (int mt = 0; mt < 2; mt++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) {
+        float v = acc[mt][r];
+#pragma unroll
+        for (int q = 0; q < kSkSplit - 1; q++) v += red[(((q * 4 + wn) * 2 + mt) * 16 + r) * 64 + lane];
+        const int64_t row = m0 + 32 * mt + 8 * (r >> 2) + 4 * h + (r & 3);
+        const int64_t n = n0 + nl;
+        if (row < M && n < N) {
+          const float f = (ACT == 0) ? ts : a.x_ts[row] * ts;
+          a.y[row * a.ldy + n] = v * f;
+        }
+      }
+  }
+}
+
+template <int ACT>
+hipError_t launch_splitk(const GemmArgs& a, hipStream_t stream) {
+  const int64_t blocks = ((a.M + kSkBM - 1) / kSkBM) * ((a.N + kSkBN - 1) / kSkBN);
+  const size_t stage = (size_t)kSkSplit * 2 * kSkBM * LDA * sizeof(uint16_t);
+  const size_t red = (size_t)(kSkSplit - 1) * 4 * 2 * 16 * 64 * sizeof(float);
+  hipLaunchKernelGGL((gemm_splitk<ACT>), dim3((uint32_t)blocks), dim3(1024),
+                     stage > red ? stage : red, stream, a);
+  return hipGetLastError();
+}
+
 template <int MT, int ACT>
 hipError_t launch_mt(const GemmArgs& a, hipStream_t stream) {
   constexpr int BM = 32 * MT;
@@ -571,9 +779,17 @@ hipError_t launch_gemm_grouped(const GemmArgs& a, int act_kind, int64_t max_tile
 // for a 256-row tile.
 int64_t gemm_max_ldx() { return ((int64_t)1 << 31) / (2 * 256) - 1; }
 
+// K split four ways when the 64 x 256 tiles would not give every CU a workgroup, the K
+// quarters stay at least four steps long and K is whole 64-k steps
+bool use_splitk(int64_t M, int64_t N, int64_t K) {
+  return ((M + 63) / 64) * ((N + BN - 1) / BN) < 256 && K >= 4 * kSkSplit * BK && K % BK == 0;
+}
+
 hipError_t launch_gemm(const GemmArgs& a, int act_kind, hipStream_t stream) {
   if (use_wide(a.M, a.N))
     return act_kind == 0 ? launch_wide<0>(a, stream) : launch_wide<1>(a, stream);
+  if (use_splitk(a.M, a.N, a.K))
+    return act_kind == 0 ? launch_splitk<0>(a, stream) : launch_splitk<1>(a, stream);
   return act_kind == 0 ? launch_mt<2, 0>(a, stream) : launch_mt<2, 1>(a, stream);
 }
 

@@ -183,6 +183,50 @@ def test_linear_wide_tiles_ragged(dev, o):
     assert_within(y4[torch.from_numpy(rows).to(dev)].cpu().numpy(), yr4, b4, "wide ragged w4a4")
 
 
+def test_linear_wide_tiles_padded_rows(dev, o):
+    """The 256 x 256-tile GEMM on ragged M, N and K with an odd number of 64-k steps and
+    padded activation and output rows; sampled rows, including every row of the last,
+    partial row tile, with BF16 and with NVFP4 activations."""
+    M, N, K = 1100, 29 * 512 + 152, 544
+    _say(f"wide-tile gemm, padded rows, M={M} N={N} K={K} (sampled rows)")
+    w = weight_f32(73, N, K)
+    (c, s, t), oq = quantize_both(o, w, dev)
+    xb = act_bf16(74, M, K + 24)
+    xd = to_dev_bf16(xb, dev)[:, :K]
+    out = torch.full((M, N + 8), float("nan"), device=dev)[:, :N]
+    y = nv.linear(xd, c, s, t, out=out)
+    rows = np.unique(np.r_[0, 127, 128, 1023, np.arange(1024, M), np.arange(5, 1024, 37)])
+    wdq = o.dequant(*oq, per_row=False)
+    yr, b = o.linear_f64(o.bf16_to_f64(xb[rows, :K]), wdq)
+    assert_within(y[torch.from_numpy(rows).to(dev)].cpu().numpy(), yr, b, "wide padded rows")
+    assert bool(torch.isfinite(y).all())
+    xc, xs, xt = nv.quantize_act(xd.contiguous())
+    oc, os_, ot = o.quantize_bf16(np.ascontiguousarray(xb[:, :K]), per_row=True)
+    assert np.array_equal(xc.cpu().numpy(), oc) and np.array_equal(xs.cpu().numpy(), os_)
+    y4 = nv.linear(xc, c, s, t, x_scales=xs, x_ts=xt)
+    yr4, b4 = o.linear_w4a4(oc[rows], os_[rows], ot[rows], *oq)
+    assert_within(y4[torch.from_numpy(rows).to(dev)].cpu().numpy(), yr4, b4, "wide padded w4a4")
+
+
+def test_linear_splitk_ragged(dev, o):
+    """The K-split GEMM (chosen when 64 x 256 tiles would leave CUs idle) on ragged M and
+    N with 33 K steps, so that the last K quarter runs past K and its last steps read
+    zeros; padded activation and output rows; BF16 and NVFP4 activations, every output."""
+    M, N, K = 300, 1000, 2112
+    _say(f"split-K gemm M={M} N={N} K={K}")
+    y, yr, b = _linear_case(dev, o, M, N, K, seed=91, pad_x=40, pad_y=24)
+    assert_within(y, yr, b, "split-K bf16")
+    w = weight_f32(92, N, K)
+    (c, s, t), oq = quantize_both(o, w, dev)
+    xb = act_bf16(93, M, K)
+    xc, xs, xt = nv.quantize_act(to_dev_bf16(xb, dev))
+    oc, os_, ot = o.quantize_bf16(xb, per_row=True)
+    assert np.array_equal(xc.cpu().numpy(), oc) and np.array_equal(xs.cpu().numpy(), os_)
+    y4 = nv.linear(xc, c, s, t, x_scales=xs, x_ts=xt)
+    yr4, b4 = o.linear_w4a4(oc, os_, ot, *oq)
+    assert_within(y4.cpu().numpy(), yr4, b4, "split-K w4a4")
+
+
 def test_linear_leading_dimensions(dev, o):
     _say("linear with padded x and y rows")
     for M in (4, 40):
@@ -264,10 +308,18 @@ def test_prefill_full_sampled_rows(dev, o):
     wdq = o.dequant(*oq, per_row=False)
     yr, b = o.linear_f64(o.bf16_to_f64(xb[rows]), wdq)
     assert_within(y[torch.from_numpy(rows).to(dev)].cpu().numpy(), yr, b, "prefill rows")
-    # rows do not depend on M (the tile they fall in is computed the same way)
-    y_small = nv.linear(to_dev_bf16(xb[:130], dev), c, s, t)
-    assert torch.equal(y_small, y[:130])
+    # rows do not depend on M while the kernel keeps the same k order: M = 320 runs the
+    # 64 x 256 tiles, M = 2048 the 256 x 256 tiles
+    y_small = nv.linear(to_dev_bf16(xb[:320], dev), c, s, t)
+    assert torch.equal(y_small, y[:320])
     assert bool(torch.isfinite(y).all())
+    # M = 130 runs the K-split kernel (K summed in quarters): within the bound, and
+    # identical from run to run
+    y_k = nv.linear(to_dev_bf16(xb[:130], dev), c, s, t)
+    kr = np.array([0, 1, 63, 64, 127, 128, 129])
+    yr_k, b_k = o.linear_f64(o.bf16_to_f64(xb[kr]), wdq)
+    assert_within(y_k[torch.from_numpy(kr).to(dev)].cpu().numpy(), yr_k, b_k, "prefill rows, K split")
+    assert torch.equal(y_k, nv.linear(to_dev_bf16(xb[:130], dev), c, s, t))
 
 
 @pytest.mark.parametrize("M", WORKLOADS["w4a4"]["Ms"])
