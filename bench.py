@@ -254,17 +254,17 @@ def bench_moe(nv, dev):
     x = to_bf16(act_bf16(cfg["x_seed"], T, cfg["K_gu"]), dev)
     a = torch.empty((T * k, cfg["N_gu"] // 2), dtype=torch.bfloat16, device=dev)
     y = torch.empty((T, cfg["N_d"]), dtype=torch.float32, device=dev)
-    w1 = torch.empty(nv.grouped_workspace_size(T, k, cfg["N_gu"], cfg["K_gu"], E, nv.OUT_SWIGLU_BF16),
-                     dtype=torch.uint8, device=dev)
-    w2 = torch.empty(nv.grouped_workspace_size(T, k, cfg["N_d"], cfg["K_d"], E, nv.OUT_COMBINE),
+    # one workspace for the layer: the down call reuses the gate_up call's route grouping
+    ws = torch.empty(max(nv.grouped_workspace_size(T, k, cfg["N_gu"], cfg["K_gu"], E, nv.OUT_SWIGLU_BF16),
+                         nv.grouped_workspace_size(T, k, cfg["N_d"], cfg["K_d"], E, nv.OUT_COMBINE)),
                      dtype=torch.uint8, device=dev)
 
     def run():
         for st in sets:
             nv.grouped_linear(x, st[0], st[1], st[2], ids_d, out_mode=nv.OUT_SWIGLU_BF16, out=a,
-                              workspace=w1)
+                              workspace=ws)
             nv.grouped_linear(a, st[3], st[4], st[5], ids_d, topk_w=rw_d, out_mode=nv.OUT_COMBINE,
-                              rows_per_route=True, out=y, workspace=w2)
+                              rows_per_route=True, out=y, workspace=ws, reuse_grouping=True)
     g = capture(run)
     timer = Timer()
     timer.time(g.replay, 1)
@@ -297,16 +297,15 @@ def bench_moe_prefill(nv, dev):
     x = to_bf16(act_bf16(cfg["x_seed"] + 1, T, cfg["K_gu"]), dev)
     a = torch.empty((T * k, cfg["N_gu"] // 2), dtype=torch.bfloat16, device=dev)
     y = torch.empty((T, cfg["N_d"]), dtype=torch.float32, device=dev)
-    w1 = torch.empty(nv.grouped_workspace_size(T, k, cfg["N_gu"], cfg["K_gu"], E, nv.OUT_SWIGLU_BF16),
-                     dtype=torch.uint8, device=dev)
-    w2 = torch.empty(nv.grouped_workspace_size(T, k, cfg["N_d"], cfg["K_d"], E, nv.OUT_COMBINE),
+    ws = torch.empty(max(nv.grouped_workspace_size(T, k, cfg["N_gu"], cfg["K_gu"], E, nv.OUT_SWIGLU_BF16),
+                         nv.grouped_workspace_size(T, k, cfg["N_d"], cfg["K_d"], E, nv.OUT_COMBINE)),
                      dtype=torch.uint8, device=dev)
 
     def run():
         nv.grouped_linear(x, st[0], st[1], st[2], ids_d, out_mode=nv.OUT_SWIGLU_BF16, out=a,
-                          workspace=w1)
+                          workspace=ws)
         nv.grouped_linear(a, st[3], st[4], st[5], ids_d, topk_w=rw_d, out_mode=nv.OUT_COMBINE,
-                          rows_per_route=True, out=y, workspace=w2)
+                          rows_per_route=True, out=y, workspace=ws, reuse_grouping=True)
     g = capture(run)
     timer = Timer()
     warm_until(g.replay, 0.15)

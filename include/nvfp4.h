@@ -67,6 +67,8 @@ enum { NVFP4_TS_PER_ROW = 0, NVFP4_TS_PER_TENSOR = 1 };
 /* grouped call: which x row a route reads, and what is written */
 enum { NVFP4_ROWS_PER_TOKEN = 0, NVFP4_ROWS_PER_ROUTE = 1 };
 enum { NVFP4_OUT_ROUTES = 0, NVFP4_OUT_SWIGLU_BF16 = 1, NVFP4_OUT_COMBINE = 2 };
+/* OR'ed into out_mode of a grouped call: reuse the route grouping already in the workspace */
+enum { NVFP4_OUT_REUSE_GROUPING = 0x100 };
 /* fault bits */
 enum { NVFP4_FAULT_NONFINITE = 1u, NVFP4_FAULT_BAD_ROUTE = 2u };
 
@@ -141,6 +143,14 @@ nvfp4_status nvfp4_quantize_act(int32_t in_type, const void* x, int64_t ldx, int
  *            Rocket log entry "The expert split decodes the same tokens; ...", section
  *            "Why rows and not partial sums").
  * topk_w is ignored unless out_mode is NVFP4_OUT_COMBINE.
+ * NVFP4_OUT_REUSE_GROUPING (OR'ed into NVFP4_OUT_COMBINE only): the workspace already
+ *   holds the route grouping of these topk_ids, left there by an earlier grouped call
+ *   on the same stream with the same topk_ids, T, top_k and num_experts (the gate_up
+ *   call of the same layer); the grouping is not recomputed. The grouping occupies the
+ *   same leading bytes of the workspace in every output form, so one workspace sized
+ *   for the combine serves both calls. Bad routes were reported by the earlier call.
+ *   Passing stale topk_ids or a different workspace gives unspecified (but in-bounds)
+ *   results. Any other out_mode with this bit is NVFP4_ERR_ARG.
  * Decode-sized batches stream each active expert's weight once for all its routes;
  *   prompt-sized ones (routes averaging >= 32 per active expert) run MFMA tiles of one
  *   expert's routes (the pages' expert-grouped prompt GEMM, each expert read once per

@@ -12,6 +12,7 @@ from ._binding import (  # noqa: F401
     LIB_PATH,
     NVFP4Error,
     OUT_COMBINE,
+    OUT_REUSE_GROUPING,
     OUT_ROUTES,
     OUT_SWIGLU_BF16,
     grouped_linear,

@@ -17,6 +17,7 @@ IN_BF16, IN_F32 = 0, 1
 TS_PER_ROW, TS_PER_TENSOR = 0, 1
 ROWS_PER_TOKEN, ROWS_PER_ROUTE = 0, 1
 OUT_ROUTES, OUT_SWIGLU_BF16, OUT_COMBINE = 0, 1, 2
+OUT_REUSE_GROUPING = 0x100
 FAULT_NONFINITE, FAULT_BAD_ROUTE = 1, 2
 
 EXPORTS = ("nvfp4_status_string", "nvfp4_linear", "nvfp4_quantize_act", "nvfp4_grouped_linear")
@@ -131,9 +132,13 @@ def grouped_workspace_size(T: int, top_k: int, N: int, K: int, num_experts: int,
 
 def grouped_linear(x, w_codes, w_scales, w_ts, topk_ids, *, topk_w=None, out_mode=OUT_ROUTES,
                    rows_per_route=False, x_scales=None, x_ts=None, out=None, workspace=None,
-                   faults=None):
+                   faults=None, reuse_grouping=False):
     """Expert-grouped NVFP4 linear. w_codes [E][N][K/2], w_scales [E][N][K/16], w_ts [E];
-    topk_ids [T][top_k] int32. See include/nvfp4.h for the output forms."""
+    topk_ids [T][top_k] int32. See include/nvfp4.h for the output forms. reuse_grouping
+    (OUT_COMBINE with the workspace of the layer's earlier call on the same topk_ids)
+    skips the route grouping."""
+    if reuse_grouping and workspace is None:
+        raise ValueError("reuse_grouping needs the workspace that holds the grouping")
     E, N, half = w_codes.shape
     K = 2 * half
     T, top_k = topk_ids.shape
@@ -154,7 +159,8 @@ def grouped_linear(x, w_codes, w_scales, w_ts, topk_ids, *, topk_w=None, out_mod
     nbytes = ctypes.c_size_t(workspace.numel())
     st = load_library().nvfp4_grouped_linear(
         act, _p(x), _p(x_scales), _p(x_ts), ldx, ROWS_PER_ROUTE if rows_per_route else ROWS_PER_TOKEN,
-        T, top_k, N, K, E, _p(w_codes), _p(w_scales), _p(w_ts), _p(topk_ids), _p(topk_w), out_mode,
+        T, top_k, N, K, E, _p(w_codes), _p(w_scales), _p(w_ts), _p(topk_ids), _p(topk_w),
+        out_mode | (OUT_REUSE_GROUPING if reuse_grouping else 0),
         _p(out), _p(workspace), ctypes.byref(nbytes), _p(faults), _stream())
     _check(st, "nvfp4_grouped_linear")
     return out

@@ -167,6 +167,10 @@ nvfp4_status nvfp4_grouped_linear(int32_t act_kind, const void* x, const uint8_t
                                   size_t* workspace_bytes, uint32_t* faults, void* stream) {
   nvfp4_status st;
   if (!workspace_bytes) return NVFP4_ERR_NULL;
+  // the grouping left in the workspace by the layer's earlier call (combine only)
+  const bool reuse = (out_mode & NVFP4_OUT_REUSE_GROUPING) != 0;
+  out_mode &= ~(int32_t)NVFP4_OUT_REUSE_GROUPING;
+  if (reuse && out_mode != NVFP4_OUT_COMBINE) return NVFP4_ERR_ARG;
   if ((st = check_k(K)) != NVFP4_OK) return st;
   if (num_experts <= 0 || num_experts > kMaxExperts) return NVFP4_ERR_ARG;
   if (top_k <= 0 || top_k > num_experts || top_k > 64) return NVFP4_ERR_ARG;
@@ -217,9 +221,11 @@ nvfp4_status nvfp4_grouped_linear(int32_t act_kind, const void* x, const uint8_t
   // clears them
   void* zero_out = out_mode == NVFP4_OUT_COMBINE ? nullptr : y;
   const int64_t zero_row_bytes = out_mode == NVFP4_OUT_ROUTES ? N * 4 : N;  // fp32 / BF16 N/2
-  hipError_t e = launch_route_sort(topk_ids, T, top_k, num_experts, ws, faults, zero_out,
-                                   zero_row_bytes, s);
-  if (e != hipSuccess) return NVFP4_ERR_LAUNCH;
+  hipError_t e = hipSuccess;
+  if (!reuse) {
+    e = launch_route_sort(topk_ids, T, top_k, num_experts, ws, faults, zero_out, zero_row_bytes, s);
+    if (e != hipSuccess) return NVFP4_ERR_LAUNCH;
+  }
 
   const int64_t R = T * top_k;
   if (gemm) {

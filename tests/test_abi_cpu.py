@@ -107,12 +107,16 @@ def test_grouped_workspace_query(lib):
     assert need_swiglu == need_routes
     assert need_combine - need_routes >= 16 * 8 * 1536 * 4
     assert nv.grouped_workspace_size(16, 8, 1536, 2048, 128, nv.OUT_SWIGLU_BF16) == need_swiglu
+    # reusing a grouping needs the same workspace as the combine itself
+    st, need_reuse = grouped(lib, work=None, nbytes=0, out_mode=2 | 0x100)
+    assert st == OK and need_reuse == need_combine
 
 
 @pytest.mark.parametrize("kw,status", [
     (dict(pass_nbytes=False), ERR_NULL), (dict(E=0), ERR_ARG), (dict(E=5000), ERR_ARG),
     (dict(k=0), ERR_ARG), (dict(k=129), ERR_ARG), (dict(rows_mode=2), ERR_ARG),
-    (dict(out_mode=3), ERR_ARG), (dict(T=0), ERR_SHAPE), (dict(K=2047), ERR_SHAPE),
+    (dict(out_mode=3), ERR_ARG), (dict(out_mode=0x100), ERR_ARG), (dict(out_mode=0x101), ERR_ARG),
+    (dict(out_mode=0x200), ERR_ARG), (dict(T=0), ERR_SHAPE), (dict(K=2047), ERR_SHAPE),
     (dict(out_mode=1, N=1535), ERR_SHAPE), (dict(nbytes=1000), ERR_WORKSPACE),
     (dict(work=P + 16), ERR_ALIGN), (dict(x=None), ERR_NULL), (dict(ids=None), ERR_NULL),
     (dict(y=None), ERR_NULL), (dict(out_mode=2, tw=None), ERR_NULL), (dict(ids=P + 2), ERR_ALIGN),

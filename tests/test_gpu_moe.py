@@ -328,3 +328,42 @@ def test_grouped_prefill_gemm_many_routes(dev, o):
                                          out_mode=nv.OUT_COMBINE), y)
     yr, b = o.moe_down_combine(np.repeat(xb, k, axis=0), ids, rw, oc, os_, ot)
     assert_within(y.cpu().numpy(), yr, b, "many-route prefill combine")
+
+
+def _reuse_check(dev, x, g, d, ids_d, rw_d, tag):
+    """gate_up (SwiGLU) then down + combine: the down call reusing the grouping the
+    gate_up call left in a shared workspace equals the down call that regroups, bit for
+    bit."""
+    gc, gs, gt = g
+    dc, ds, dt = d
+    T, k = ids_d.shape
+    N_gu, K = gc.shape[1], 2 * gc.shape[2]
+    N_d, K_d = dc.shape[1], 2 * dc.shape[2]
+    E = gc.shape[0]
+    need = max(nv.grouped_workspace_size(T, k, N_gu, K, E, nv.OUT_SWIGLU_BF16),
+               nv.grouped_workspace_size(T, k, N_d, K_d, E, nv.OUT_COMBINE))
+    ws = torch.full((need,), 0x5A, dtype=torch.uint8, device=dev)
+    a = nv.grouped_linear(x, gc, gs, gt, ids_d, out_mode=nv.OUT_SWIGLU_BF16, workspace=ws)
+    y_reuse = nv.grouped_linear(a, dc, ds, dt, ids_d, topk_w=rw_d, out_mode=nv.OUT_COMBINE,
+                                rows_per_route=True, workspace=ws, reuse_grouping=True)
+    y = nv.grouped_linear(a, dc, ds, dt, ids_d, topk_w=rw_d, out_mode=nv.OUT_COMBINE,
+                          rows_per_route=True)
+    assert torch.equal(y_reuse, y), tag
+    with pytest.raises(ValueError):
+        nv.grouped_linear(a, dc, ds, dt, ids_d, topk_w=rw_d, out_mode=nv.OUT_COMBINE,
+                          rows_per_route=True, reuse_grouping=True)
+
+
+def test_grouped_reuse_grouping_decode(dev, moe):
+    _say("MoE decode layer: down + combine reusing the gate_up call's grouping")
+    _reuse_check(dev, moe["x_d"], (moe["gc"], moe["gs"], moe["gt"]),
+                 (moe["dc"], moe["ds"], moe["dt"]), moe["ids_d"], moe["rw_d"], "decode")
+
+
+def test_grouped_reuse_grouping_prefill(dev, o):
+    _say("MoE prefill: down + combine reusing the gate_up call's grouping (GEMM path)")
+    E, N, K, T, k = 16, 64, 128, 1024, 4
+    wc, wsc, wts, _, _, _, ids, rw, xb = _prefill_case(dev, o, E, N, K, T, k, 121)
+    dc, dsc, dts, _, _, _ = _small_experts(o, dev, E, 96, N // 2, 122)
+    _reuse_check(dev, to_dev_bf16(xb, dev), (wc, wsc, wts), (dc, dsc, dts),
+                 torch.from_numpy(ids).to(dev), torch.from_numpy(rw).to(dev), "prefill")
