@@ -61,7 +61,8 @@ bool grouped_uses_gemm(int64_t T, int top_k, int E) {
 
 // grouped-call workspace layout: 256-byte aligned regions
 struct Layout {
-  size_t offsets, active, n_active, route_expert, sorted, order, rows, tiles, n_tiles, total;
+  size_t offsets, active, n_active, route_expert, sorted, order, rows, tiles, n_tiles, chunks,
+      total;
   int64_t max_tiles;
 };
 
@@ -82,6 +83,7 @@ Layout grouped_layout(int64_t T, int top_k, int E, int64_t N, int32_t out_mode) 
   L.order = o; o = up256(o + sizeof(int32_t) * R);
   L.tiles = o; o = up256(o + sizeof(int32_t) * 2 * (size_t)L.max_tiles);
   L.n_tiles = o; o = up256(o + sizeof(int32_t));
+  L.chunks = o; o = up256(o + sizeof(int32_t) * (size_t)route_chunk_ints(T, top_k, E));
   L.rows = o;
   if (out_mode == NVFP4_OUT_COMBINE) o = up256(o + sizeof(float) * R * (size_t)N);
   L.total = o;
@@ -214,6 +216,7 @@ nvfp4_status nvfp4_grouped_linear(int32_t act_kind, const void* x, const uint8_t
   ws.rows = reinterpret_cast<float*>(base + L.rows);
   ws.tiles = reinterpret_cast<int32_t*>(base + L.tiles);
   ws.n_tiles = reinterpret_cast<int32_t*>(base + L.n_tiles);
+  ws.chunk_counts = reinterpret_cast<int32_t*>(base + L.chunks);
   const bool gemm = L.max_tiles > 0;
   ws.tile_rows = gemm ? gemm_grouped_tile_rows() : 0;
 

@@ -145,46 +145,55 @@ __global__ __launch_bounds__(kSortThreads) void route_sort(const int32_t* ids, i
   }
 }
 
-// Any number of routes with top_k <= kRegTopK: each thread takes whole tokens, their ids
-// loaded together and validated, counted and placed in registers (no loop of dependent
-// global loads); the ids are re-read after the scans rather than kept across them. Same
-// outputs as route_sort (order inside an expert's group unspecified).
+// Route sets beyond one workgroup's quick reach (more than kFastRoutes routes, top_k <=
+// kRegTopK) are grouped by chunks of kChunkTokens tokens, one workgroup each, one token
+// per thread with its ids in registers:
+//  (1) route_count_chunks validates its tokens' routes and counts them per expert into
+//      chunk_counts[chunk][E];
+//  (2) route_scan_chunks (one workgroup) turns the counts into the offsets, the active
+//      list, the tile list and, in place, each chunk's first slot per expert;
+//  (3) route_scatter_chunks places its routes from those slots and writes its tokens'
+//      route order.
+// Chunks keep ascending token order within an expert's group; inside a chunk the order is
+// unspecified (LDS atomic cursors), which no output depends on: every route's row is
+// computed from its own activation row and its expert alone.
 constexpr int kRegTopK = 16;
+constexpr int kChunkTokens = 256;
+
+// a token's ids and validity (in range, not repeated earlier in the token)
+template <int KREG>
+__device__ __forceinline__ void load_token(const int32_t* ids, int64_t t, int top_k, int E,
+                                           int32_t (&e)[KREG], bool (&ok)[KREG]) {
+#pragma unroll
+  for (int j = 0; j < KREG; j++) e[j] = j < top_k ? ids[t * top_k + j] : -1;
+#pragma unroll
+  for (int j = 0; j < KREG; j++) {
+    bool v = j < top_k && e[j] >= 0 && e[j] < E;
+#pragma unroll
+    for (int jj = 0; jj < j; jj++) v = v && e[jj] != e[j];
+    ok[j] = v;
+  }
+}
 
 // KREG: the exact top_k (fully unrolled), or kRegTopK with top_k <= kRegTopK read at run time
 template <int KREG>
-__global__ __launch_bounds__(kSortThreads) void route_sort_tokens(const int32_t* ids, int64_t T,
-                                                                  int top_k_rt, int E,
-                                                                  RouteWorkspace ws,
-                                                                  uint32_t* faults,
-                                                                  void* zero_out,
-                                                                  int64_t zero_row_bytes) {
+__global__ __launch_bounds__(kChunkTokens) void route_count_chunks(const int32_t* ids, int64_t T,
+                                                                   int top_k_rt, int E,
+                                                                   RouteWorkspace ws,
+                                                                   uint32_t* faults,
+                                                                   void* zero_out,
+                                                                   int64_t zero_row_bytes) {
   const int top_k = KREG == kRegTopK ? top_k_rt : KREG;
-  extern __shared__ int32_t sh[];
-  int32_t* wsum = sh;       // [16]
-  int32_t* cnt = sh + 16;   // [E] routes per expert, then the scatter cursors
+  extern __shared__ int32_t cnt[];  // [E]
   const int tid = threadIdx.x;
-  for (int e = tid; e < E; e += kSortThreads) cnt[e] = 0;
+  for (int e = tid; e < E; e += kChunkTokens) cnt[e] = 0;
   __syncthreads();
-
-  // a token's ids and validity, in registers
-  auto load_token = [&](int64_t t, int32_t (&e)[KREG], bool (&ok)[KREG]) {
-#pragma unroll
-    for (int j = 0; j < KREG; j++) e[j] = j < top_k ? ids[t * top_k + j] : -1;
-#pragma unroll
-    for (int j = 0; j < KREG; j++) {
-      bool v = j < top_k && e[j] >= 0 && e[j] < E;
-#pragma unroll
-      for (int jj = 0; jj < j; jj++) v = v && e[jj] != e[j];
-      ok[j] = v;
-    }
-  };
-
+  const int64_t t = (int64_t)blockIdx.x * kChunkTokens + tid;
   bool bad = false;
-  for (int64_t t = tid; t < T; t += kSortThreads) {
+  if (t < T) {
     int32_t e[KREG];
     bool ok[KREG];
-    load_token(t, e, ok);
+    load_token<KREG>(ids, t, top_k, E, e, ok);
 #pragma unroll
     for (int j = 0; j < KREG; j++) {
       if (j >= top_k) break;
@@ -200,32 +209,67 @@ __global__ __launch_bounds__(kSortThreads) void route_sort_tokens(const int32_t*
   }
   if (bad && faults) atomicOr(faults, (uint32_t)NVFP4_FAULT_BAD_ROUTE);
   __syncthreads();
+  int32_t* cc = ws.chunk_counts + (int64_t)blockIdx.x * E;
+  for (int e = tid; e < E; e += kChunkTokens) cc[e] = cnt[e];
+}
 
+__global__ __launch_bounds__(kSortThreads) void route_scan_chunks(int E, int64_t nchunks,
+                                                                  RouteWorkspace ws) {
+  extern __shared__ int32_t sh[];
+  int32_t* wsum = sh;      // [16]
+  int32_t* cnt = sh + 16;  // [E] routes per expert, then each expert's first slot
+  const int tid = threadIdx.x;
+  for (int e = tid; e < E; e += kSortThreads) {
+    int32_t c = 0;
+    for (int64_t k = 0; k < nchunks; k++) c += ws.chunk_counts[k * E + e];
+    cnt[e] = c;
+  }
+  __syncthreads();
   expert_scans(ws, E, cnt, wsum);
-
-  for (int64_t t = tid; t < T; t += kSortThreads) {
-    int32_t e[KREG];
-    bool ok[KREG];
-    load_token(t, e, ok);
-    int nvalid = 0;
-#pragma unroll
-    for (int j = 0; j < KREG; j++) nvalid += ok[j];
-    int ninvalid = 0;
-#pragma unroll
-    for (int j = 0; j < KREG; j++) {
-      if (j >= top_k) break;
-      const int64_t r = t * top_k + j;
-      int slot;
-      if (ok[j]) {
-        ws.sorted[atomicAdd(&cnt[e[j]], 1)] = (int32_t)r;
-        slot = 0;
-#pragma unroll
-        for (int jj = 0; jj < KREG; jj++) slot += (ok[jj] && e[jj] < e[j]);
-      } else {
-        slot = nvalid + ninvalid++;
-      }
-      ws.order[t * top_k + slot] = ok[j] ? j : -1;
+  // chunk k's first slot for expert e: e's first slot plus the earlier chunks' counts
+  for (int e = tid; e < E; e += kSortThreads) {
+    int32_t run = cnt[e];
+    for (int64_t k = 0; k < nchunks; k++) {
+      const int32_t c = ws.chunk_counts[k * E + e];
+      ws.chunk_counts[k * E + e] = run;
+      run += c;
     }
+  }
+}
+
+template <int KREG>
+__global__ __launch_bounds__(kChunkTokens) void route_scatter_chunks(const int32_t* ids, int64_t T,
+                                                                     int top_k_rt, int E,
+                                                                     RouteWorkspace ws) {
+  const int top_k = KREG == kRegTopK ? top_k_rt : KREG;
+  extern __shared__ int32_t cur[];  // [E] this chunk's next slot per expert
+  const int tid = threadIdx.x;
+  const int32_t* cc = ws.chunk_counts + (int64_t)blockIdx.x * E;
+  for (int e = tid; e < E; e += kChunkTokens) cur[e] = cc[e];
+  __syncthreads();
+  const int64_t t = (int64_t)blockIdx.x * kChunkTokens + tid;
+  if (t >= T) return;
+  int32_t e[KREG];
+  bool ok[KREG];
+  load_token<KREG>(ids, t, top_k, E, e, ok);
+  int nvalid = 0;
+#pragma unroll
+  for (int j = 0; j < KREG; j++) nvalid += ok[j];
+  int ninvalid = 0;
+#pragma unroll
+  for (int j = 0; j < KREG; j++) {
+    if (j >= top_k) break;
+    const int64_t r = t * top_k + j;
+    int slot;
+    if (ok[j]) {
+      ws.sorted[atomicAdd(&cur[e[j]], 1)] = (int32_t)r;
+      slot = 0;
+#pragma unroll
+      for (int jj = 0; jj < KREG; jj++) slot += (ok[jj] && e[jj] < e[j]);
+    } else {
+      slot = nvalid + ninvalid++;
+    }
+    ws.order[t * top_k + slot] = ok[j] ? j : -1;
   }
 }
 
@@ -387,18 +431,37 @@ hipError_t launch_route_sort(const int32_t* topk_ids, int64_t T, int top_k, int 
   }
   const size_t lds = sizeof(int32_t) * (16 + (size_t)E);
   if (top_k <= kRegTopK) {
-    auto k = top_k == 1 ? route_sort_tokens<1>
-           : top_k == 2 ? route_sort_tokens<2>
-           : top_k == 4 ? route_sort_tokens<4>
-           : top_k == 8 ? route_sort_tokens<8>
-                        : route_sort_tokens<kRegTopK>;
-    hipLaunchKernelGGL(k, dim3(1), dim3(kSortThreads), lds, stream, topk_ids, T, top_k, E, ws,
-                       faults, zero_out, zero_row_bytes);
+    const int64_t nchunks = (T + kChunkTokens - 1) / kChunkTokens;
+    const size_t lds_c = sizeof(int32_t) * (size_t)E;
+    auto kc = top_k == 1 ? route_count_chunks<1>
+            : top_k == 2 ? route_count_chunks<2>
+            : top_k == 4 ? route_count_chunks<4>
+            : top_k == 8 ? route_count_chunks<8>
+                         : route_count_chunks<kRegTopK>;
+    auto ks = top_k == 1 ? route_scatter_chunks<1>
+            : top_k == 2 ? route_scatter_chunks<2>
+            : top_k == 4 ? route_scatter_chunks<4>
+            : top_k == 8 ? route_scatter_chunks<8>
+                         : route_scatter_chunks<kRegTopK>;
+    hipLaunchKernelGGL(kc, dim3((uint32_t)nchunks), dim3(kChunkTokens), lds_c, stream, topk_ids, T,
+                       top_k, E, ws, faults, zero_out, zero_row_bytes);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(route_scan_chunks, dim3(1), dim3(kSortThreads), lds, stream, E, nchunks, ws);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(ks, dim3((uint32_t)nchunks), dim3(kChunkTokens), lds_c, stream, topk_ids, T,
+                       top_k, E, ws);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(route_sort, dim3(1), dim3(kSortThreads), lds, stream, topk_ids, T, top_k, E,
                      ws, faults, zero_out, zero_row_bytes);
   return hipGetLastError();
+}
+
+int64_t route_chunk_ints(int64_t T, int top_k, int E) {
+  if (T * top_k <= kFastRoutes || top_k > kRegTopK) return 0;
+  return (T + kChunkTokens - 1) / kChunkTokens * (int64_t)E;
 }
 
 hipError_t launch_combine(const float* rows, const int32_t* route_expert, const int32_t* order,

@@ -95,7 +95,12 @@ struct RouteWorkspace {
   int32_t* tiles;         // GEMM path: [n_tiles][2] (expert, first slot in `sorted`)
   int32_t* n_tiles;       // [1]
   int32_t tile_rows;      // GEMM path: routes per tile (0: no tile list)
+  int32_t* chunk_counts;  // chunked grouping: [chunks][E] counts, then first slots
 };
+
+// int32 entries of the chunked grouping's count table for this route set (0 when the
+// route set is grouped by a single workgroup)
+int64_t route_chunk_ints(int64_t T, int top_k, int E);
 
 // also zeroes output row r (zero_row_bytes bytes of zero_out, when not NULL) of every
 // dropped route

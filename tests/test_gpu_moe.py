@@ -240,7 +240,8 @@ def test_grouped_combine_with_dropped_routes(dev, o):
 
 def test_grouped_many_routes_general_sort(dev, o):
     """More routes than one sorting workgroup holds at once (T * top_k > 1024): the
-    general route grouping, several 16-row passes per expert, in both output forms."""
+    chunked route grouping (one chunk here), several 16-row passes per expert, in both
+    output forms."""
     E, N, K, T, k = 16, 48, 64, 160, 8
     ids, _ = moe_routes(91, T, E, k)
     ids = ids.astype(np.int32)
@@ -258,6 +259,36 @@ def test_grouped_many_routes_general_sort(dev, o):
         e = int(ids[t, j])
         yr, b = o.linear(xb[t:t + 1], oc[e], os_[e], ot[e:e + 1])
         assert_within(h[r:r + 1], yr, b, f"many routes: route {t},{j}")
+
+
+@pytest.mark.parametrize("T,k,E", [(700, 4, 24), (64, 20, 40)])
+def test_grouped_chunked_and_wide_topk_grouping(dev, o, T, k, E):
+    """Route sets beyond one workgroup: several token chunks (T = 700: three chunks of
+    256 tokens), and top_k above 16 (the general single-workgroup grouping); dropped routes
+    (repeated, out of range, negative) in both; combine and per-route rows against the
+    oracle."""
+    N, K = 40, 64
+    _say(f"grouping T={T} top_k={k} E={E}")
+    ids, _ = moe_routes(95 + k, T, E, k)
+    ids = ids.astype(np.int32)
+    dropped = [(3, 1), (T - 2, k - 1), (T // 2, 0)]
+    ids[3, 1] = ids[3, 0]
+    ids[T - 2, k - 1] = E + 1
+    ids[T // 2, 0] = -1
+    f = _combine_check(dev, o, ids, E, N, K, 96 + k, f"grouping T={T} k={k}: combine")
+    assert f & nv.FAULT_BAD_ROUTE
+    wc, wsc, wts, oc, os_, ot = _small_experts(o, dev, E, N, K, 96 + k)
+    xb = act_bf16(97, T, K)
+    h = nv.grouped_linear(to_dev_bf16(xb, dev), wc, wsc, wts, torch.from_numpy(ids).to(dev)).cpu().numpy()
+    for t, j in dropped:
+        assert np.all(h[t * k + j] == 0), (t, j)
+    for r in np.r_[0, T * k - 1, np.random.default_rng(6).choice(T * k, 24, replace=False)]:
+        t, j = divmod(int(r), k)
+        if (t, j) in dropped:
+            continue
+        e = int(ids[t, j])
+        yr, b = o.linear(xb[t:t + 1], oc[e], os_[e], ot[e:e + 1])
+        assert_within(h[r:r + 1], yr, b, f"grouping T={T} k={k}: route {t},{j}")
 
 
 def _prefill_case(dev, o, E, N, K, T, k, seed):
