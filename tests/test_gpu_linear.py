@@ -145,7 +145,7 @@ def _linear_case(dev, o, M, N, K, seed, pad_x=0, pad_y=0):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 1, 32), (3, 17, 96), (16, 200, 544), (5, 1000, 4128),
-                                   (2, 3000, 64), (16, 48, 8192)])
+                                   (2, 3000, 64), (16, 48, 8192), (12, 777, 4096), (9, 130, 2048)])
 def test_linear_stream_ragged(dev, o, M, N, K):
     _say(f"stream linear M={M} N={N} K={K}")
     y, yr, b = _linear_case(dev, o, M, N, K, seed=M * 7 + N)
@@ -277,6 +277,8 @@ def test_decode_rows_batch_invariant_and_deterministic(dev, sweep_weight):
     for m in (0, 5, 15):
         y1 = nv.linear(xd[m:m + 1], c, s, t)
         assert torch.equal(y1[0], y16[m]), m
+    for rows in (4, 8, 12):  # other row-set counts, tile widths and ring depths
+        assert torch.equal(nv.linear(xd[:rows], c, s, t), y16[:rows]), rows
     for _ in range(3):
         assert torch.equal(nv.linear(xd, c, s, t), y16)
 
