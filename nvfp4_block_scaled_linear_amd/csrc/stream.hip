@@ -27,7 +27,7 @@
 //  - The workgroup's scale rows are one contiguous block; it is copied into LDS once
 //    with 16-byte loads and each lane reads its two scale bytes from there.
 //  - Activation rows are padded to sets of four (R sets for M <= 4R); a workgroup owns
-//    16*TN weight rows and W waves, with a ring of ring_depth(R) steps of loads in flight per
+//    16*TN weight rows and W waves, with a ring of a few steps of loads in flight per
 //    wave.
 //  - Loads are raw buffer loads: out-of-range offsets read as zero without touching
 //    memory, so bounds and predication need no branches (a branch around a load forces a
@@ -40,10 +40,17 @@
 namespace nvfp4 {
 namespace {
 
-// Steps of loads in flight per wave: four for up to two row sets; two for more, where each
-// step already holds TN + R 16-byte loads per lane and a deeper ring measured slower (M=16,
-// K=4096, N=12288: 13.9 us at depth two against 14.7 us at four).
-__host__ __device__ constexpr int ring_depth(int R) { return R >= 3 ? 2 : 4; }
+// Steps of loads in flight per wave (measured at K=4096): the dense kernel keeps eight for
+// one row set, where few loads per step leave the memory pipe short of work (M=4, N=4096
+// NVFP4 activations: 10.3 us with quantize against 10.7 us at depth four; M=1, K=N=2048:
+// 4.4 against 4.7 us); four for two row sets (M=8, N=12288: 10.3 us against 10.8 us at
+// eight); two for more, where each step already holds TN + R 16-byte loads per lane (M=16:
+// 13.9 us against 14.7 us at four). The grouped kernels stream one expert's tile per
+// workgroup and keep four (two from three row sets).
+__host__ __device__ constexpr int dense_ring_depth(int R) {
+  return R == 1 ? 8 : (R == 2 ? 4 : 2);
+}
+__host__ __device__ constexpr int grouped_ring_depth(int R) { return R >= 3 ? 2 : 4; }
 constexpr uint32_t kOOB = 0x80000000u;
 // Activation transpose buffer: one 16-byte piece per lane, rows of 16 pieces padded to
 // 288 bytes so that both the row-contiguous writes and the operand-layout reads are free
@@ -113,11 +120,10 @@ __host__ __device__ __forceinline__ size_t lds_bytes(int TN, int R, int W, int64
 
 // Tile t of the workgroup is weight rows n0 + t * tstride + [0, 16), of which the first
 // lim[t] exist (rows past them read as zero).
-template <int TN, int R, int ACT, bool SLDS>
+template <int TN, int R, int ACT, bool SLDS, int kDepth>
 __device__ __forceinline__ void pass4(const StreamArgs& a, const uint8_t* wc, const uint8_t* ws,
                                       int64_t n0, int64_t tstride, const int (&lim)[TN],
                                       const RowMap& rm, uint8_t* lds, f32x4 (&acc)[TN][R]) {
-  constexpr int kDepth = ring_depth(R);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // scalar: uniform guards
   const int W = blockDim.x >> 6;
@@ -384,7 +390,7 @@ __global__ __launch_bounds__(256) void stream_dense(StreamArgs a) {
     lim[t] = left < 0 ? 0 : (left > 16 ? 16 : (int)left);
   }
   f32x4 acc[TN][R];
-  pass4<TN, R, ACT, SLDS>(a, a.w_codes, a.w_scales, n0, 16, lim, rm, lds, acc);
+  pass4<TN, R, ACT, SLDS, dense_ring_depth(R)>(a, a.w_codes, a.w_scales, n0, 16, lim, rm, lds, acc);
   const float ts = a.apply_ts ? a.w_ts[0] : 1.0f;
   reduce_store<TN, R>(acc, red, n0, [&](int m, int64_t n, float s) {
     if (m < a.M && n < a.N) {
@@ -426,7 +432,7 @@ __global__ __launch_bounds__(256) void stream_grouped(StreamArgs a) {
     }
     f32x4 acc[1][R];
     const int lim[1] = {(int)((a.N - n0) < 16 ? (a.N - n0) : 16)};
-    pass4<1, R, ACT, SLDS>(a, wc, ws, n0, 16, lim, rm, lds, acc);
+    pass4<1, R, ACT, SLDS, grouped_ring_depth(R)>(a, wc, ws, n0, 16, lim, rm, lds, acc);
     reduce_store<1, R>(acc, red, n0, [&](int m, int64_t n, float s) {
       if (m < rows && n < a.N) {
         const int rr = a.sorted[c0 + m];
@@ -483,7 +489,7 @@ __global__ __launch_bounds__(256) void stream_grouped_swiglu(StreamArgs a) {
       }
     }
     f32x4 acc[2][R];
-    pass4<2, R, ACT, SLDS>(a, wc, ws, n0, half, lim, rm, lds, acc);
+    pass4<2, R, ACT, SLDS, grouped_ring_depth(R)>(a, wc, ws, n0, half, lim, rm, lds, acc);
     __syncthreads();
 #pragma unroll
     for (int t = 0; t < 2; t++)
