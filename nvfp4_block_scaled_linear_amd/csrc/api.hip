@@ -61,8 +61,7 @@ bool grouped_uses_gemm(int64_t T, int top_k, int E) {
 
 // grouped-call workspace layout: 256-byte aligned regions
 struct Layout {
-  size_t offsets, active, n_active, route_expert, sorted, order, rows, tiles, n_tiles, chunks,
-      total;
+  size_t offsets, active, n_active, route_expert, sorted, rows, tiles, n_tiles, chunks, total;
   int64_t max_tiles;
 };
 
@@ -80,7 +79,6 @@ Layout grouped_layout(int64_t T, int top_k, int E, int64_t N, int32_t out_mode) 
   L.n_active = o; o = up256(o + sizeof(int32_t));
   L.route_expert = o; o = up256(o + sizeof(int32_t) * R);
   L.sorted = o; o = up256(o + sizeof(int32_t) * R);
-  L.order = o; o = up256(o + sizeof(int32_t) * R);
   L.tiles = o; o = up256(o + sizeof(int32_t) * 2 * (size_t)L.max_tiles);
   L.n_tiles = o; o = up256(o + sizeof(int32_t));
   L.chunks = o; o = up256(o + sizeof(int32_t) * (size_t)route_chunk_ints(T, top_k, E));
@@ -212,7 +210,6 @@ nvfp4_status nvfp4_grouped_linear(int32_t act_kind, const void* x, const uint8_t
   ws.n_active = reinterpret_cast<int32_t*>(base + L.n_active);
   ws.route_expert = reinterpret_cast<int32_t*>(base + L.route_expert);
   ws.sorted = reinterpret_cast<int32_t*>(base + L.sorted);
-  ws.order = reinterpret_cast<int32_t*>(base + L.order);
   ws.rows = reinterpret_cast<float*>(base + L.rows);
   ws.tiles = reinterpret_cast<int32_t*>(base + L.tiles);
   ws.n_tiles = reinterpret_cast<int32_t*>(base + L.n_tiles);
@@ -251,7 +248,7 @@ nvfp4_status nvfp4_grouped_linear(int32_t act_kind, const void* x, const uint8_t
     e = launch_gemm_grouped(g, act_kind, L.max_tiles, s);
     if (e != hipSuccess) return NVFP4_ERR_LAUNCH;
     if (out_mode == NVFP4_OUT_COMBINE) {
-      e = launch_combine(ws.rows, ws.route_expert, ws.order, topk_w, w_ts, T, top_k, N,
+      e = launch_combine(ws.rows, ws.route_expert, topk_w, w_ts, T, top_k, N,
                          static_cast<float*>(y), s);
     }
     return launch_status(e);
@@ -281,7 +278,7 @@ nvfp4_status nvfp4_grouped_linear(int32_t act_kind, const void* x, const uint8_t
   e = launch_stream(a, act_kind, true, max_active, s);
   if (e != hipSuccess) return NVFP4_ERR_LAUNCH;
   if (out_mode == NVFP4_OUT_COMBINE) {
-    e = launch_combine(ws.rows, ws.route_expert, ws.order, topk_w, w_ts, T, top_k, N,
+    e = launch_combine(ws.rows, ws.route_expert, topk_w, w_ts, T, top_k, N,
                        static_cast<float*>(y), s);
   }
   return launch_status(e);

@@ -96,8 +96,8 @@ __device__ __forceinline__ void expert_scans(const RouteWorkspace& ws, int E, in
   __syncthreads();
 }
 
-// Single workgroup, any number of routes. The same offsets, active list, tile list and
-// per-token order as route_sort_fast; the order of routes within one expert's group is
+// Single workgroup, any number of routes. The same offsets, active list and tile list as
+// route_sort_fast; the order of routes within one expert's group is
 // unspecified here (atomic cursors), which no output depends on: every route's row is
 // computed from its own activation row and its expert alone.
 __global__ __launch_bounds__(kSortThreads) void route_sort(const int32_t* ids, int64_t T,
@@ -131,17 +131,10 @@ __global__ __launch_bounds__(kSortThreads) void route_sort(const int32_t* ids, i
   // (2) offsets, active list, tile list; cnt becomes the scatter cursors
   expert_scans(ws, E, cnt, wsum);
 
-  // (3) scatter and (4) each route's slot within its token
+  // (3) scatter
   for (int64_t r = tid; r < R; r += kSortThreads) {
     const int32_t e = ws.route_expert[r];
     if (e >= 0) ws.sorted[atomicAdd(&cnt[e], 1)] = (int32_t)r;
-    const int64_t t0 = (r / top_k) * top_k;
-    int slot = 0;
-    for (int64_t rr = t0; rr < t0 + top_k; rr++) {
-      const int32_t er = ws.route_expert[rr];
-      slot += (e >= 0) ? (er >= 0 && er < e) : ((er >= 0) || (rr < r));
-    }
-    ws.order[t0 + slot] = e >= 0 ? (int32_t)(r - t0) : -1;
   }
 }
 
@@ -152,8 +145,7 @@ __global__ __launch_bounds__(kSortThreads) void route_sort(const int32_t* ids, i
 //      chunk_counts[chunk][E];
 //  (2) route_scan_chunks (one workgroup) turns the counts into the offsets, the active
 //      list, the tile list and, in place, each chunk's first slot per expert;
-//  (3) route_scatter_chunks places its routes from those slots and writes its tokens'
-//      route order.
+//  (3) route_scatter_chunks places its routes from those slots.
 // Chunks keep ascending token order within an expert's group; inside a chunk the order is
 // unspecified (LDS atomic cursors), which no output depends on: every route's row is
 // computed from its own activation row and its expert alone.
@@ -252,24 +244,10 @@ __global__ __launch_bounds__(kChunkTokens) void route_scatter_chunks(const int32
   int32_t e[KREG];
   bool ok[KREG];
   load_token<KREG>(ids, t, top_k, E, e, ok);
-  int nvalid = 0;
-#pragma unroll
-  for (int j = 0; j < KREG; j++) nvalid += ok[j];
-  int ninvalid = 0;
 #pragma unroll
   for (int j = 0; j < KREG; j++) {
     if (j >= top_k) break;
-    const int64_t r = t * top_k + j;
-    int slot;
-    if (ok[j]) {
-      ws.sorted[atomicAdd(&cur[e[j]], 1)] = (int32_t)r;
-      slot = 0;
-#pragma unroll
-      for (int jj = 0; jj < KREG; jj++) slot += (ok[jj] && e[jj] < e[j]);
-    } else {
-      slot = nvalid + ninvalid++;
-    }
-    ws.order[t * top_k + slot] = ok[j] ? j : -1;
+    if (ok[j]) ws.sorted[atomicAdd(&cur[e[j]], 1)] = (int32_t)(t * top_k + j);
   }
 }
 
@@ -277,9 +255,7 @@ __global__ __launch_bounds__(kChunkTokens) void route_scatter_chunks(const int32
 // LDS with no dependent global-memory round trips. One route per thread (the block is
 // sized to R); the expert offsets and the active-expert list come from block-wide scans;
 // a route's place among its expert's routes is the number of earlier routes with the
-// same expert (stable, counted with 16-byte LDS reads); its slot within its token is the
-// number of the token's valid routes with a smaller expert id (valid ids are distinct
-// within a token); the slots after them hold -1, as in route_sort.
+// same expert (stable, counted with 16-byte LDS reads).
 constexpr int kFastRoutes = kSortThreads;
 
 __global__ __launch_bounds__(kSortThreads) void route_sort_fast(const int32_t* ids, int64_t T,
@@ -319,60 +295,55 @@ __global__ __launch_bounds__(kSortThreads) void route_sort_fast(const int32_t* i
   // offsets, active list, tile list; cnt becomes each expert's first slot
   expert_scans(ws, E, cnt, wsum);
 
-  if (tid < R) {
-    const int t0 = (tid / top_k) * top_k;
-    if (my_e >= 0) {
-      // stable place among the expert's routes
-      int rank = 0;
-      const int full = tid & ~3;
-      for (int r = 0; r < full; r += 4) {
-        const int4 v = *reinterpret_cast<const int4*>(rexp + r);
-        rank += (v.x == my_e) + (v.y == my_e) + (v.z == my_e) + (v.w == my_e);
-      }
-      for (int r = full; r < tid; r++) rank += (rexp[r] == my_e);
-      ws.sorted[cnt[my_e] + rank] = tid;
+  if (my_e >= 0) {
+    // stable place among the expert's routes
+    int rank = 0;
+    const int full = tid & ~3;
+    for (int r = 0; r < full; r += 4) {
+      const int4 v = *reinterpret_cast<const int4*>(rexp + r);
+      rank += (v.x == my_e) + (v.y == my_e) + (v.z == my_e) + (v.w == my_e);
     }
-    // slot within the token: ascending expert id, dropped routes last as -1
-    int slot = 0;
-    if (my_e >= 0) {
-      for (int r = t0; r < t0 + top_k; r++) slot += (rexp[r] >= 0 && rexp[r] < my_e);
-    } else {
-      for (int r = t0; r < t0 + top_k; r++) slot += (rexp[r] >= 0);
-      for (int r = t0; r < tid; r++) slot += (rexp[r] < 0);
-    }
-    ws.order[t0 + slot] = my_e >= 0 ? tid - t0 : -1;
+    for (int r = full; r < tid; r++) rank += (rexp[r] == my_e);
+    ws.sorted[cnt[my_e] + rank] = tid;
   }
 }
 
 // y[t][n] = sum over the token's routes in ascending expert id of (w * ts_e) * row[n]
-// One workgroup per (token, 1024 columns): the token's routes in ascending expert id and
-// their weights r * ts_e are staged in LDS once; each thread loads its four columns of
-// every route row before summing them with fmaf in that order, starting from zero.
+// One workgroup per (token, 1024 columns). The first top_k threads read their route's
+// expert and router weight together, rank the route among the token's kept routes by
+// expert id in LDS and stage its row index and weight r * ts_e at that rank; each thread
+// then loads its four columns of every route row before summing them with fmaf in that
+// order, starting from zero. (Three dependent memory round trips per workgroup: routes,
+// tensor scales, rows.)
 constexpr int kCombineMaxK = 64;
 
 __global__ __launch_bounds__(256) void combine_kernel(const float* rows,
                                                       const int32_t* route_expert,
-                                                      const int32_t* order, const float* topk_w,
+                                                      const float* topk_w,
                                                       const float* w_ts, int64_t T, int top_k,
                                                       int64_t N, float* y) {
+  __shared__ int32_t ex[kCombineMaxK];
   __shared__ int32_t rr[kCombineMaxK];
   __shared__ float wr[kCombineMaxK];
-  __shared__ int nr;
   const int64_t t = blockIdx.x;
-  if (threadIdx.x == 0) {
-    int n = 0;
-    for (int jj = 0; jj < top_k; jj++) {
-      const int j = order[t * top_k + jj];
-      if (j < 0) break;
-      const int64_t r = t * top_k + j;
-      rr[n] = (int32_t)r;
-      wr[n] = topk_w[r] * w_ts[route_expert[r]];
-      n++;
-    }
-    nr = n;
+  const int tid = threadIdx.x;
+  int32_t e = -1;
+  float w = 0.f;
+  if (tid < top_k) {
+    e = route_expert[t * top_k + tid];
+    w = topk_w[t * top_k + tid];
+    ex[tid] = e;
   }
   __syncthreads();
-  const int n_routes = nr;
+  int n_routes = 0;  // kept routes of the token (ids are distinct within a token)
+  for (int j = 0; j < top_k; j++) n_routes += ex[j] >= 0;
+  if (e >= 0) {
+    int slot = 0;
+    for (int j = 0; j < top_k; j++) slot += (ex[j] >= 0 && ex[j] < e);
+    rr[slot] = (int32_t)(t * top_k + tid);
+    wr[slot] = w * w_ts[e];
+  }
+  __syncthreads();
   const int64_t n0 = (int64_t)blockIdx.y * 1024 + 4 * threadIdx.x;
   if (n0 >= N) return;
   const bool vec = n0 + 4 <= N && (N & 3) == 0;
@@ -464,11 +435,11 @@ int64_t route_chunk_ints(int64_t T, int top_k, int E) {
   return (T + kChunkTokens - 1) / kChunkTokens * (int64_t)E;
 }
 
-hipError_t launch_combine(const float* rows, const int32_t* route_expert, const int32_t* order,
-                          const float* topk_w, const float* w_ts, int64_t T, int top_k,
-                          int64_t N, float* y, hipStream_t stream) {
+hipError_t launch_combine(const float* rows, const int32_t* route_expert, const float* topk_w,
+                          const float* w_ts, int64_t T, int top_k, int64_t N, float* y,
+                          hipStream_t stream) {
   hipLaunchKernelGGL(combine_kernel, dim3((uint32_t)T, (uint32_t)((N + 1023) / 1024)), dim3(256),
-                     0, stream, rows, route_expert, order, topk_w, w_ts, T, top_k, N, y);
+                     0, stream, rows, route_expert, topk_w, w_ts, T, top_k, N, y);
   return hipGetLastError();
 }
 

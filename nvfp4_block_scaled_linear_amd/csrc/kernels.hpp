@@ -90,7 +90,6 @@ struct RouteWorkspace {
   int32_t* n_active;      // [1]
   int32_t* route_expert;  // [R] expert of route r, or -1 when dropped
   int32_t* sorted;        // [R]
-  int32_t* order;         // [T][top_k] token's route slots in ascending expert id (-1 last)
   float* rows;            // [R][N] fp32 per-route rows (combine form; SwiGLU on the GEMM path)
   int32_t* tiles;         // GEMM path: [n_tiles][2] (expert, first slot in `sorted`)
   int32_t* n_tiles;       // [1]
@@ -107,7 +106,7 @@ int64_t route_chunk_ints(int64_t T, int top_k, int E);
 hipError_t launch_route_sort(const int32_t* topk_ids, int64_t T, int top_k, int E,
                              const RouteWorkspace& ws, uint32_t* faults, void* zero_out,
                              int64_t zero_row_bytes, hipStream_t stream);
-hipError_t launch_combine(const float* rows, const int32_t* route_expert, const int32_t* order,
+hipError_t launch_combine(const float* rows, const int32_t* route_expert,
                           const float* topk_w, const float* w_ts, int64_t T, int top_k,
                           int64_t N, float* y, hipStream_t stream);
 
