@@ -155,8 +155,37 @@ def bench_decode_sweep(nv, dev, steps, warmup):
                          "bytes": b}
         del gm
     del g
+    probe = read_probe_roof(nv, dev, linear_bytes(1, N, K), timer)
+    for M in Ms:
+        per_m[str(M)]["frac_read_probe"] = round(per_m[str(M)]["GBps"] / probe["GBps"], 4)
     return dict(N=N, K=K, Ms=Ms, R=R, ms_step=ms_step, step_bytes=step_bytes,
-                timed_steps=timed_steps, per_m=per_m, launches_per_step=len(Ms))
+                timed_steps=timed_steps, per_m=per_m, launches_per_step=len(Ms), probe=probe)
+
+
+def read_probe_roof(nv, dev, nbytes, timer):
+    """The measured single-launch read roof: the library's plain streaming-read kernel over
+    buffers of the M=1 launch's algorithmic size, rotated over >= 1 GiB like the weights,
+    timed in the same way; the best of its launch shapes."""
+    nbytes = (nbytes + 15) // 16 * 16
+    R = max(2, math.ceil(ROTATE_BYTES / nbytes))
+    bufs = [torch.full((nbytes,), 1, dtype=torch.uint8, device=dev) for _ in range(R)]
+    sink = torch.zeros((1,), dtype=torch.int32, device=dev)
+    best = None
+    for u in (1, 2, 4, 8, 16):
+        def run(u=u):
+            for b in bufs:
+                nv.read_probe(b, u, sink)
+        g = capture(run)
+        timer.time(g.replay, 1)
+        ms = min(timer.time(g.replay, 3) for _ in range(3)) / R
+        if best is None or ms < best[0]:
+            best = (ms, u)
+        del g
+    ms, u = best
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    return {"bytes": nbytes, "us": round(ms * 1e3, 3), "GBps": round(gbps, 1),
+            "frac_hbm": round(gbps / HBM_PEAK_GBPS, 4), "loads_per_thread": u,
+            "kernel": "read_probe (plain streaming read, one launch per buffer)"}
 
 
 def bench_single(nv, dev):
@@ -501,8 +530,11 @@ def main():
                      "traffic": measured_traffic(),
                      "kernel": "stream_dense (weight-streaming MFMA kernel)",
                      "avg_launch_us": round(d["ms_step"] * 1e3 / d["launches_per_step"], 3),
-                     "bytes_per_launch_avg": d["step_bytes"] // d["launches_per_step"]},
+                     "bytes_per_launch_avg": d["step_bytes"] // d["launches_per_step"],
+                     "achievable": d["probe"]["GBps"],
+                     "frac_achievable": round(achieved / d["probe"]["GBps"], 4)},
         "per_m": d["per_m"],
+        "read_probe": d["probe"],
     }
     def want(name):
         return args.only in ("all", name)

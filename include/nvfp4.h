@@ -172,6 +172,20 @@ nvfp4_status nvfp4_grouped_linear(int32_t act_kind, const void* x, const uint8_t
                                   int32_t out_mode, void* y, void* workspace,
                                   size_t* workspace_bytes, uint32_t* faults, void* stream);
 
+/* nvfp4_read_probe — measurement support, not part of the layer: one plain streaming read
+ * of `bytes` bytes at `buf` in one launch, the measured single-launch read roof that the
+ * weight-streaming calls are compared against (the pages set their decode paths beside a
+ * measured local roof as well as the nominal one: Rocket engineering log, entry on the
+ * GDN decode path on GB10, roofline table).
+ * buf: device memory, 16-byte aligned; bytes: 16 .. 2^31 - 16, a multiple of 16.
+ * loads_per_thread: 1, 2, 4, 8 or 16 sixteen-byte loads per thread (the launch shape;
+ *   each workgroup reads loads_per_thread * 4 KiB).
+ * sink: a device word the kernel may overwrite (it keeps the loads live; its value is
+ *   meaningless).
+ * Errors: NVFP4_ERR_NULL, _SHAPE, _ALIGN, _ARG, _LAUNCH. */
+nvfp4_status nvfp4_read_probe(const void* buf, int64_t bytes, int32_t loads_per_thread,
+                              uint32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

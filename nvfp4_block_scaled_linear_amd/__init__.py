@@ -20,5 +20,6 @@ from ._binding import (  # noqa: F401
     linear,
     load_library,
     quantize_act,
+    read_probe,
     status_string,
 )

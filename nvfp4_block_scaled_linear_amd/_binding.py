@@ -20,7 +20,8 @@ OUT_ROUTES, OUT_SWIGLU_BF16, OUT_COMBINE = 0, 1, 2
 OUT_REUSE_GROUPING = 0x100
 FAULT_NONFINITE, FAULT_BAD_ROUTE = 1, 2
 
-EXPORTS = ("nvfp4_status_string", "nvfp4_linear", "nvfp4_quantize_act", "nvfp4_grouped_linear")
+EXPORTS = ("nvfp4_status_string", "nvfp4_linear", "nvfp4_quantize_act", "nvfp4_grouped_linear",
+           "nvfp4_read_probe")
 
 _lib = None
 
@@ -51,6 +52,8 @@ def load_library(path: str = LIB_PATH):
     lib.nvfp4_grouped_linear.argtypes = [i32, vp, vp, vp, i64, i32, i64, i32, i64, i64, i32, vp,
                                          vp, vp, vp, vp, i32, vp, vp,
                                          ctypes.POINTER(ctypes.c_size_t), u32p, vp]
+    lib.nvfp4_read_probe.restype = i32
+    lib.nvfp4_read_probe.argtypes = [vp, i64, i32, u32p, vp]
     _lib = lib
     return lib
 
@@ -164,3 +167,12 @@ def grouped_linear(x, w_codes, w_scales, w_ts, topk_ids, *, topk_w=None, out_mod
         _p(out), _p(workspace), ctypes.byref(nbytes), _p(faults), _stream())
     _check(st, "nvfp4_grouped_linear")
     return out
+
+
+def read_probe(buf, loads_per_thread: int, sink):
+    """Measurement support: one plain streaming read of the bytes of `buf` (a contiguous
+    device tensor) in one launch; `sink` is a device int32 the kernel may overwrite."""
+    nbytes = buf.numel() * buf.element_size()
+    st = load_library().nvfp4_read_probe(_p(buf), nbytes, int(loads_per_thread), _p(sink),
+                                         _stream())
+    _check(st, "nvfp4_read_probe")

@@ -284,4 +284,16 @@ nvfp4_status nvfp4_grouped_linear(int32_t act_kind, const void* x, const uint8_t
   return launch_status(e);
 }
 
+nvfp4_status nvfp4_read_probe(const void* buf, int64_t bytes, int32_t loads_per_thread,
+                              uint32_t* sink, void* stream) {
+  if (!buf || !sink) return NVFP4_ERR_NULL;
+  if (bytes < 16 || bytes > ((int64_t)1 << 31) - 16 || bytes % 16 != 0) return NVFP4_ERR_SHAPE;
+  if (!aligned(buf, 16) || !aligned(sink, 4)) return NVFP4_ERR_ALIGN;
+  if (loads_per_thread != 1 && loads_per_thread != 2 && loads_per_thread != 4 &&
+      loads_per_thread != 8 && loads_per_thread != 16)
+    return NVFP4_ERR_ARG;
+  return launch_status(launch_read_probe(buf, bytes, loads_per_thread, sink,
+                                         static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -110,4 +110,9 @@ hipError_t launch_combine(const float* rows, const int32_t* route_expert,
                           const float* topk_w, const float* w_ts, int64_t T, int top_k,
                           int64_t N, float* y, hipStream_t stream);
 
+// measurement support: one streaming read of `bytes` bytes (loads_per_thread 16-byte loads
+// per thread, 1/2/4/8/16)
+hipError_t launch_read_probe(const void* buf, int64_t bytes, int loads_per_thread, uint32_t* sink,
+                             hipStream_t stream);
+
 }  // namespace nvfp4

@@ -126,6 +126,15 @@ def test_grouped_refusals(lib, kw, status):
     assert grouped(lib, **kw)[0] == status
 
 
+@pytest.mark.parametrize("args,status", [
+    ((None, 4096, 4, P), ERR_NULL), ((P, 4096, 4, None), ERR_NULL), ((P, 0, 4, P), ERR_SHAPE),
+    ((P, 4100, 4, P), ERR_SHAPE), ((P, 1 << 31, 4, P), ERR_SHAPE), ((P + 8, 4096, 4, P), ERR_ALIGN),
+    ((P, 4096, 4, P + 2), ERR_ALIGN), ((P, 4096, 3, P), ERR_ARG), ((P, 4096, 32, P), ERR_ARG),
+])
+def test_read_probe_refusals(lib, args, status):
+    assert lib.nvfp4_read_probe(*args, None) == status
+
+
 def test_binding_fails_loudly_without_library(tmp_path):
     from nvfp4_block_scaled_linear_amd import _binding
     saved = _binding._lib

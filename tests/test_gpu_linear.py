@@ -356,3 +356,21 @@ def test_w4a4_equals_w4a16_on_decoded_rows(dev, o):
     y16 = nv.linear(torch.from_numpy(xhat.astype(np.float32)).to(dev).to(torch.bfloat16), c, s, t)
     want = y16 / t * (xt[:, None] * t)
     assert torch.allclose(y4, want, rtol=1e-6, atol=1e-30)
+
+
+def test_read_probe_reads_every_byte(dev):
+    """The measurement probe's loads cover the buffer: a fold mark placed at the start of
+    one thread's run (and nowhere else) reaches the sink, a zero buffer leaves it alone."""
+    mark = 0x9E3779B9
+    for u in (1, 2, 4, 8, 16):
+        nbytes = 3 * u * 4096 + 4096 + 32  # ragged last workgroup
+        for where in (0, nbytes - 16 - (nbytes - 16) % (u * 4096)):  # first / last workgroup
+            buf = torch.zeros((nbytes,), dtype=torch.uint8, device=dev)
+            sink = torch.zeros((1,), dtype=torch.int32, device=dev)
+            nv.read_probe(buf, u, sink)
+            torch.cuda.synchronize()
+            assert sink.item() == 0
+            buf.view(torch.int32)[where // 4] = int(np.array(mark, dtype=np.uint32).view(np.int32))
+            nv.read_probe(buf, u, sink)
+            torch.cuda.synchronize()
+            assert sink.cpu().view(torch.int32).numpy().view(np.uint32)[0] == mark, (u, where)
