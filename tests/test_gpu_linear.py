@@ -152,6 +152,45 @@ def test_linear_stream_ragged(dev, o, M, N, K):
     assert_within(y, yr, b, f"M={M} N={N} K={K}")
 
 
+# decode-sweep-sized N with ragged N (the last workgroup's tiles partly or wholly empty),
+# ragged K (the last wave's K range shorter than the others; K % 256 != 0 takes the scales
+# from memory), 48-row tiles (M=12, 16) and a long K
+@pytest.mark.parametrize("M,N,K", [(5, 12300, 4128), (12, 12320, 2048), (1, 12288, 8192),
+                                   (16, 12256, 544)])
+def test_linear_stream_large_n_ragged(dev, o, M, N, K):
+    _say(f"stream linear M={M} N={N} K={K}")
+    y, yr, b = _linear_case(dev, o, M, N, K, seed=M * 11 + N)
+    assert_within(y, yr, b, f"M={M} N={N} K={K}")
+
+
+def test_column_subsets_bit_identical(dev, o):
+    """Columns of the full decode-sized product equal, bit for bit, the same columns
+    computed from a slice of the weight (a different grid and, at M=16, tile width): a
+    row's arithmetic does not depend on the workgroup shape."""
+    K = 4096
+    w = weight_f32(31, 12288, K)
+    (c, s, t), _ = quantize_both(o, w, dev)
+    for M in (1, 4, 8, 16):
+        xd = to_dev_bf16(act_bf16(900 + M, M, K), dev)
+        y_all = nv.linear(xd, c, s, t)
+        for lo in (0, 4096, 12288 - 1024):
+            y_part = nv.linear(xd, c[lo:lo + 1024].contiguous(), s[lo:lo + 1024].contiguous(), t)
+            assert torch.equal(y_part, y_all[:, lo:lo + 1024]), (M, lo)
+
+
+def test_w4a4_large_n(dev, o):
+    K, N, M = 4096, 12288, 6
+    w = weight_f32(33, N, K)
+    (c, s, t), oq = quantize_both(o, w, dev)
+    xb = act_bf16(34, M, K)
+    xc, xs, xt = nv.quantize_act(to_dev_bf16(xb, dev))
+    oc, os_, ot = o.quantize_bf16(xb, per_row=True)
+    assert np.array_equal(xc.cpu().numpy(), oc) and np.array_equal(xs.cpu().numpy(), os_)
+    y = nv.linear(xc, c, s, t, x_scales=xs, x_ts=xt).cpu().numpy()
+    yr, b = o.linear_w4a4(oc, os_, ot, *oq)
+    assert_within(y, yr, b, "w4a4 N=12288")
+
+
 @pytest.mark.parametrize("M,N,K", [(17, 255, 64), (130, 600, 1056), (300, 130, 96), (64, 256, 32)])
 def test_linear_gemm_ragged(dev, o, M, N, K):
     _say(f"gemm linear M={M} N={N} K={K}")
