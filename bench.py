@@ -264,6 +264,41 @@ def bench_w4a4(nv, dev):
     return out
 
 
+def bench_w4a4_in_call(nv, dev):
+    """W4A4 for decode-sized batches two ways on the W4A4 weight (K = N = 4096): the
+    quantizer launch followed by the NVFP4-activation linear, and the one-launch form that
+    quantizes each row inside the weight-streaming kernel (bit for bit the same result)."""
+    from synth import WORKLOADS, act_bf16, weight_f32
+    cfg = WORKLOADS["w4a4"]
+    N, K = cfg["N"], cfg["K"]
+    c, s, t = quantize_weight(nv, weight_f32(cfg["w_seed"], N, K), dev)
+    R = math.ceil(ROTATE_BYTES / weight_bytes(N, K))
+    W = copies(c, s, R)
+    out = {}
+    timer = Timer()
+    for M in (1, 2, 4):
+        x = to_bf16(act_bf16(cfg["x_seed_base"] + M, M, K), dev)
+        xc, xs_, xt = nv.quantize_act(x)
+        y = torch.empty((M, N), dtype=torch.float32, device=dev)
+
+        def two_calls():
+            for j in range(R):
+                nv.quantize_act(x, codes=xc, scales=xs_, ts=xt)
+                nv.linear(xc, W[j][0], W[j][1], t, x_scales=xs_, x_ts=xt, out=y)
+
+        def in_call():
+            for j in range(R):
+                nv.linear(x, W[j][0], W[j][1], t, out=y, quantize_x=True)
+        rec = {}
+        for name, fn in (("us_two_calls", two_calls), ("us_in_call", in_call)):
+            g = capture(fn)
+            warm_until(g.replay, 0.05)
+            rec[name] = round(timer.time(g.replay, 5) / R * 1e3, 3)
+            del g
+        out[str(M)] = rec
+    return out
+
+
 def bench_moe(nv, dev):
     from synth import WORKLOADS, act_bf16, moe_expert_weights, moe_routes
     cfg = WORKLOADS["moe_decode"]
@@ -547,6 +582,7 @@ def main():
     if want("w4a4"):
         log("w4a4 ...")
         rec["w4a4"] = bench_w4a4(nv, dev)
+        rec["w4a4_in_call_quantize"] = bench_w4a4_in_call(nv, dev)
     if want("moe"):
         log("moe ...")
         rec["moe"] = bench_moe(nv, dev)

@@ -5,6 +5,7 @@ include/nvfp4.h); this package is its thin Python binding over torch tensors.
 """
 from ._binding import (  # noqa: F401
     ACT_BF16,
+    ACT_BF16_QUANTIZE,
     ACT_NVFP4,
     EXPORTS,
     FAULT_BAD_ROUTE,

@@ -12,7 +12,7 @@ import torch
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libnvfp4.so")
 
-ACT_BF16, ACT_NVFP4 = 0, 1
+ACT_BF16, ACT_NVFP4, ACT_BF16_QUANTIZE = 0, 1, 2
 IN_BF16, IN_F32 = 0, 1
 TS_PER_ROW, TS_PER_TENSOR = 0, 1
 ROWS_PER_TOKEN, ROWS_PER_ROUTE = 0, 1
@@ -89,13 +89,15 @@ def _check(status: int, what: str):
         raise NVFP4Error(status, what)
 
 
-def linear(x, w_codes, w_scales, w_ts, *, x_scales=None, x_ts=None, out=None):
+def linear(x, w_codes, w_scales, w_ts, *, x_scales=None, x_ts=None, out=None,
+           quantize_x=False):
     """y = x W^T for an NVFP4 weight (codes [N][K/2] u8, scales [N][K/16] u8, ts [1] f32).
-    x is BF16 [M][K] (W4A16), or NVFP4 codes [M][K/2] u8 with x_scales/x_ts (W4A4)."""
+    x is BF16 [M][K] (W4A16), or NVFP4 codes [M][K/2] u8 with x_scales/x_ts (W4A4).
+    quantize_x=True (BF16 x, M <= 4): W4A4 with x quantized per row inside the call."""
     N = w_codes.shape[0]
     K = 2 * w_codes.shape[1]
     if x_scales is None:
-        act, M, ldx = ACT_BF16, x.shape[0], _ld(x)
+        act, M, ldx = (ACT_BF16_QUANTIZE if quantize_x else ACT_BF16), x.shape[0], _ld(x)
     else:
         act, M, ldx = ACT_NVFP4, x.shape[0], K
     if out is None:

@@ -24,10 +24,12 @@ nvfp4_status launch_status(hipError_t e) { return e == hipSuccess ? NVFP4_OK : N
 // checks shared by the weight operand and the activation operand of linear/grouped calls
 nvfp4_status check_act(int32_t act_kind, const void* x, const uint8_t* x_scales,
                        const float* x_ts, int64_t ldx, int64_t K) {
-  if (act_kind != NVFP4_ACT_BF16 && act_kind != NVFP4_ACT_NVFP4) return NVFP4_ERR_ARG;
+  if (act_kind != NVFP4_ACT_BF16 && act_kind != NVFP4_ACT_NVFP4 &&
+      act_kind != NVFP4_ACT_BF16_QUANTIZE)
+    return NVFP4_ERR_ARG;
   if (!x) return NVFP4_ERR_NULL;
   if (!aligned(x, 16)) return NVFP4_ERR_ALIGN;
-  if (act_kind == NVFP4_ACT_BF16) {
+  if (act_kind != NVFP4_ACT_NVFP4) {
     if (x_scales || x_ts) return NVFP4_ERR_ARG;
     if (ldx < K || ldx > kMaxDim) return NVFP4_ERR_SHAPE;
     if (ldx % 8 != 0) return NVFP4_ERR_ALIGN;
@@ -113,13 +115,14 @@ nvfp4_status nvfp4_linear(int32_t act_kind, const void* x, const uint8_t* x_scal
   if ((st = check_k(K)) != NVFP4_OK) return st;
   if (M <= 0 || N <= 0 || M > kMaxDim || N > kMaxDim) return NVFP4_ERR_SHAPE;
   if ((st = check_act(act_kind, x, x_scales, x_ts, ldx, K)) != NVFP4_OK) return st;
+  if (act_kind == NVFP4_ACT_BF16_QUANTIZE && (M > 4 || K > 8192)) return NVFP4_ERR_SHAPE;
   if ((st = check_weight(w_codes, w_scales, w_ts)) != NVFP4_OK) return st;
   if (!y) return NVFP4_ERR_NULL;
   if (ldy < N || ldy > kMaxDim) return NVFP4_ERR_SHAPE;
   if (!aligned(y, 4)) return NVFP4_ERR_ALIGN;
   hipStream_t s = static_cast<hipStream_t>(stream);
   // the kernels address activation rows with 32-bit buffer offsets
-  if (act_kind == NVFP4_ACT_BF16 &&
+  if (act_kind != NVFP4_ACT_NVFP4 &&
       (M <= kStreamMaxRows ? M * ldx * 2 > kMaxBufferBytes : ldx > gemm_max_ldx()))
     return NVFP4_ERR_SHAPE;
   if (act_kind == NVFP4_ACT_NVFP4 && M * (K / 2) > kMaxBufferBytes) return NVFP4_ERR_SHAPE;

@@ -118,6 +118,34 @@ __device__ __forceinline__ bool is_finite(float v) {
   return (__float_as_uint(v) & 0x7F800000u) != 0x7F800000u;
 }
 
+// One 16-block of a row under tensor scale t, by the quantization rule, each step one
+// correctly rounded fp32 operation in the stated order:
+//   ratio = (amax_b / 6) / t (0 when t == 0);  s = E4M3_RNE(ratio);
+//   q_k = x_k / (e4m3(s) * t) (+-0 when that is 0);  code_k = E2M1_RNE(q_k).
+// Returns the scale byte; lo / hi receive codes 0..7 / 8..15, low nibble first. Shared by
+// the quantizer and the weight-streaming kernel's in-call activation quantization, so
+// the two agree bit for bit.
+__device__ __forceinline__ uint32_t quantize16(const float v[16], float t, uint32_t& lo,
+                                               uint32_t& hi) {
+#pragma clang fp contract(off)
+  float amax_b = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; i++) amax_b = fmaxf(amax_b, __builtin_fabsf(v[i]));
+  const float ratio = (t == 0.0f) ? 0.0f : (amax_b / 6.0f) / t;
+  const uint32_t s = e4m3_rne(ratio);
+  const float den = e4m3_value(s) * t;
+  lo = 0u;
+  hi = 0u;
+#pragma unroll
+  for (int i = 0; i < 16; i++) {
+    const float q = (den == 0.0f) ? __builtin_copysignf(0.0f, v[i]) : v[i] / den;
+    const uint32_t c = e2m1_rne(q);
+    if (i < 8) lo |= c << (4 * i);
+    else hi |= c << (4 * (i - 8));
+  }
+  return s;
+}
+
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
   return __uint_as_float(bits16 << 16);
 }

@@ -50,19 +50,8 @@ __device__ __forceinline__ float amax16(const float v[16], bool& finite) {
 // one 16-block with tensor scale t -> 8 code bytes + 1 scale byte
 __device__ __forceinline__ void quantize_block(const float v[16], float t, uint8_t* codes8,
                                                uint8_t* scale1) {
-  bool dummy = true;
-  const float amax_b = amax16(v, dummy);
-  const float ratio = (t == 0.0f) ? 0.0f : (amax_b / 6.0f) / t;
-  const uint32_t s = e4m3_rne(ratio);
-  const float den = e4m3_value(s) * t;
-  uint32_t lo = 0, hi = 0;
-#pragma unroll
-  for (int i = 0; i < 16; i++) {
-    const float q = (den == 0.0f) ? __builtin_copysignf(0.0f, v[i]) : v[i] / den;
-    const uint32_t c = e2m1_rne(q);
-    if (i < 8) lo |= c << (4 * i);
-    else hi |= c << (4 * (i - 8));
-  }
+  uint32_t lo, hi;
+  const uint32_t s = quantize16(v, t, lo, hi);
   *reinterpret_cast<uint2*>(codes8) = make_uint2(lo, hi);
   *scale1 = (uint8_t)s;
 }

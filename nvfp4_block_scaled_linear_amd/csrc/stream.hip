@@ -110,12 +110,155 @@ __host__ __device__ __forceinline__ uint32_t lds_scale_bytes(int TN, int64_t K, 
   return slds ? ((16u * TN * lds_scale_stride(K) + 31u) & ~15u) : 0u;
 }
 
-// LDS layout of a workgroup: [scales | transpose buffers of the W waves] during the
-// stream, then the reduction buffer over the same bytes.
-__host__ __device__ __forceinline__ size_t lds_bytes(int TN, int R, int W, int64_t K, bool slds) {
-  const size_t stream = lds_scale_bytes(TN, K, slds) + (size_t)W * R * kXSet;
+// In-call quantized activations (ACT == 2): the four rows' exact BF16 values stay in LDS
+// for the whole stream, rows padded to whole 128-k steps plus 32 bytes (no bank
+// conflicts between the four rows of an operand read); then the rows' amax bits, a
+// non-finite flag per row and the rows' tensor scales.
+__host__ __device__ __forceinline__ uint32_t xq_row_bytes(int64_t K) {
+  return (uint32_t)(((K + 127) / 128) * 256 + 32);
+}
+__host__ __device__ __forceinline__ uint32_t xq_bytes(int64_t K) {
+  return 4u * xq_row_bytes(K) + 48u;
+}
+
+// LDS layout of a workgroup: [scales | transpose buffers of the W waves, or the quantized
+// rows] during the stream, then the reduction buffer over the same bytes.
+__host__ __device__ __forceinline__ size_t lds_bytes(int TN, int R, int W, int64_t K, bool slds,
+                                                     int act = 0) {
+  const size_t stream =
+      lds_scale_bytes(TN, K, slds) + (act == 2 ? (size_t)xq_bytes(K) : (size_t)W * R * kXSet);
   const size_t red = (size_t)W * TN * R * 64 * 4 * sizeof(float);
   return stream > red ? stream : red;
+}
+
+// Waves splitting K: about eight 128-k steps per wave, one to four waves. The in-call
+// quantization sizes its loops from this rule rather than from blockDim, whose read from
+// the dispatch packet after the weight ring is issued would wait for the whole ring.
+__host__ __device__ constexpr int waves_for_k(int64_t K) {
+  const int64_t w = ((K + 127) / 128 + 7) / 8;
+  return w < 1 ? 1 : (w > 4 ? 4 : (int)w);
+}
+
+// In-call activation quantization (ACT == 2): the workgroup quantizes the a.M <= 4 BF16
+// rows by the per-row rule (row amax -> ts_row = amax / 2688 -> per 16-block E4M3 scale
+// and E2M1 codes, the quantizer's own quantize16) and keeps their exact decoded BF16
+// values e2m1 * e4m3 in LDS (rows past a.M and k past K are zero), so the stream
+// multiplies exactly what nvfp4_quantize_act followed by the W4A4 call would. A row with
+// a NaN or Inf gets a NaN tensor scale (its outputs are NaN). LDS: rows at xq, then
+// amax bits [4], non-finite flags [4], ts_row [4].
+//
+// The rows' BF16 values are loaded first (xq_issue, before the weight ring, so that
+// waiting for them does not wait for the ring), kQBlocks 16-blocks per thread: K <= 8192
+// keeps a.M * K/16 within kQBlocks * 64 * waves_for_k(K) for every K.
+constexpr int kQBlocks = 8;
+constexpr int64_t kQMaxK = 8192;
+
+struct XqRegs {
+  u32x4 v[kQBlocks][2];
+};
+
+__device__ __forceinline__ void xq_issue(const StreamArgs& a, XqRegs& r) {
+  const int nthr = 64 * waves_for_k(a.K);
+  const int nb = (int)(a.K >> 4);
+  const auto xr = make_rsrc(a.x, (uint32_t)(((a.x_rows - 1) * a.ldx + a.K) * 2));
+#pragma unroll
+  for (int u = 0; u < kQBlocks; u++) {
+    const int j = threadIdx.x + u * nthr;
+    const int m = j / nb, b = j % nb;
+    const uint32_t off = j < a.M * nb ? (uint32_t)((m * a.ldx + 16 * b) * 2) : kOOB;
+    r.v[u][0] = __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0);
+    r.v[u][1] = __builtin_amdgcn_raw_buffer_load_b128(xr, off + 16u, 0, 0);
+  }
+}
+
+__device__ __forceinline__ void unpack16(const u32x4& lo, const u32x4& hi, float v[16]) {
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    v[2 * i] = __uint_as_float(lo[i] << 16);
+    v[2 * i + 1] = __uint_as_float(lo[i] & 0xFFFF0000u);
+    v[8 + 2 * i] = __uint_as_float(hi[i] << 16);
+    v[8 + 2 * i + 1] = __uint_as_float(hi[i] & 0xFFFF0000u);
+  }
+}
+
+__device__ __forceinline__ void xq_finish(const StreamArgs& a, const XqRegs& r, uint8_t* xq) {
+  const int nthr = 64 * waves_for_k(a.K);
+  const uint32_t rb = xq_row_bytes(a.K);
+  uint32_t* amax_bits = reinterpret_cast<uint32_t*>(xq + 4 * rb);
+  uint32_t* bad = amax_bits + 4;
+  float* ts_row = reinterpret_cast<float*>(bad + 4);
+  const int nb = (int)(a.K >> 4);         // 16-blocks per row
+  const int nbp = (int)(rb - 32u) >> 5;  // 16-blocks per padded row
+  if (threadIdx.x < 8) amax_bits[threadIdx.x] = 0u;  // amax bits and flags
+  // rows and padding past the data are zero (stores after the barrier below fill the rest)
+  for (int j = threadIdx.x; j < 4 * nbp; j += nthr) {
+    const int m = j / nbp, b = j % nbp;
+    if (m >= a.M || b >= nb) {
+      u32x4* d = reinterpret_cast<u32x4*>(xq + m * rb + 32u * b);
+      d[0] = u32x4{0u, 0u, 0u, 0u};
+      d[1] = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  __syncthreads();
+  // (1) row amax: per thread, then per wave (max is exact in any order), then one LDS
+  // atomic max per wave and row on the bits of the non-negative float
+  float pm[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  uint32_t badm = 0u;  // bit m: row m holds a NaN or Inf
+#pragma unroll
+  for (int u = 0; u < kQBlocks; u++) {
+    const int j = threadIdx.x + u * nthr;
+    if (j < a.M * nb) {
+      float v[16];
+      unpack16(r.v[u][0], r.v[u][1], v);
+      float mx = 0.0f;
+      bool fin = true;
+#pragma unroll
+      for (int i = 0; i < 16; i++) {
+        fin = fin && is_finite(v[i]);
+        mx = fmaxf(mx, __builtin_fabsf(v[i]));
+      }
+      const int m = j / nb;
+#pragma unroll
+      for (int rr = 0; rr < 4; rr++) pm[rr] = (m == rr) ? fmaxf(pm[rr], mx) : pm[rr];
+      if (!fin) badm |= 1u << m;
+    }
+  }
+#pragma unroll
+  for (int rr = 0; rr < 4; rr++) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) pm[rr] = fmaxf(pm[rr], __shfl_xor(pm[rr], off, 64));
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) badm |= (uint32_t)__shfl_xor((int)badm, off, 64);
+  if ((threadIdx.x & 63) == 0) {
+#pragma unroll
+    for (int rr = 0; rr < 4; rr++) {
+      if (rr < a.M) atomicMax(&amax_bits[rr], __float_as_uint(pm[rr]));
+      if ((badm >> rr) & 1u) bad[rr] = 1u;
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < 4) {
+    const float t = __uint_as_float(amax_bits[threadIdx.x]) / 2688.0f;
+    ts_row[threadIdx.x] = bad[threadIdx.x] ? __builtin_nanf("") : t;
+  }
+  // (2) blocks: codes and scale (quantize16, the quantizer's own arithmetic), then their
+  // exact BF16 values (decode8, as the W4A4 stream decodes stored codes)
+#pragma unroll
+  for (int u = 0; u < kQBlocks; u++) {
+    const int j = threadIdx.x + u * nthr;
+    if (j < a.M * nb) {
+      const int m = j / nb, b = j % nb;
+      float v[16];
+      unpack16(r.v[u][0], r.v[u][1], v);
+      uint32_t lo, hi;
+      const uint32_t sc = quantize16(v, __uint_as_float(amax_bits[m]) / 2688.0f, lo, hi);
+      const float sd = e4m3_value(sc);
+      u32x4* d = reinterpret_cast<u32x4*>(xq + m * rb + 32u * b);
+      d[0] = decode8(lo, sd);
+      d[1] = decode8(hi, sd);
+    }
+  }
 }
 
 // Tile t of the workgroup is weight rows n0 + t * tstride + [0, 16), of which the first
@@ -156,7 +299,7 @@ __device__ __forceinline__ void pass4(const StreamArgs& a, const uint8_t* wc, co
     srow[t] = ok ? (uint32_t)((t * tstride + nl) * sb) : kOOB;
   }
   __amdgpu_buffer_rsrc_t xr, xsr;
-  if (ACT == 0) {
+  if (ACT != 1) {
     xr = make_rsrc(a.x, (uint32_t)(((a.x_rows - 1) * a.ldx + a.K) * 2));  // last row: K values
     xsr = xr;
   } else {
@@ -164,8 +307,9 @@ __device__ __forceinline__ void pass4(const StreamArgs& a, const uint8_t* wc, co
     xsr = make_rsrc(a.x_scales, (uint32_t)(a.x_rows * sb));
   }
 
+  static_assert(ACT != 2 || (TN == 1 && R == 1), "in-call quantization: one row set, one tile");
   uint8_t* lds_s = lds;
-  uint8_t* xbuf = lds + lds_scale_bytes(TN, a.K, SLDS) + (uint32_t)wave * R * kXSet;
+  uint8_t* xbuf = lds + lds_scale_bytes(TN, a.K, SLDS) + (ACT == 2 ? 0u : (uint32_t)wave * R * kXSet);
   const uint32_t sls = lds_scale_stride(a.K);
   const uint32_t xw = kXRow * g + 16u * q;                 // this lane's piece (write)
   const uint32_t xrd = kXRow * (lane & 3) + 16u * (4 * g + bp);  // operand piece (read)
@@ -187,7 +331,9 @@ __device__ __forceinline__ void pass4(const StreamArgs& a, const uint8_t* wc, co
     const uint32_t out_p = step_out | past(K, kp);
 #pragma unroll
     for (int r = 0; r < R; r++) {
-      if (ACT == 0) {
+      if (ACT == 2) {
+        // in-call quantized activations are read from LDS at compute time
+      } else if (ACT == 0) {
         b.x[r] = __builtin_amdgcn_raw_buffer_load_b128(xr, (rm.off[r] + 2u * kp) | out_p, 0, 0);
       } else {
         b.x[r][0] = __builtin_amdgcn_raw_buffer_load_b32(xr, (rm.off[r] + (kp >> 1)) | out_p, 0, 0);
@@ -212,14 +358,21 @@ __device__ __forceinline__ void pass4(const StreamArgs& a, const uint8_t* wc, co
   auto compute = [&](StepBuf<TN, R, ACT>& b, uint32_t kg, int slot) {
     // activations: row-contiguous pieces -> LDS -> operand layout
     u32x4 A[R];
+    if (ACT == 2) {
+      // the quantized rows in LDS: row lane & 3, 8 k at k0 + 8 * (4g + bp)
+      const uint32_t k0 = kg - 32u * g;
+      A[0] = *reinterpret_cast<const u32x4*>(xbuf + (lane & 3) * xq_row_bytes(a.K) +
+                                             2u * (k0 + 8u * (4 * g + bp)));
+    } else {
 #pragma unroll
-    for (int r = 0; r < R; r++) {
-      u32x4 v = b.x[r];
-      if (ACT != 0) v = decode8(b.x[r][0], e4m3_to_f32<0>(b.x[r][1]));  // exact BF16
-      *reinterpret_cast<u32x4*>(xbuf + r * kXSet + xw) = v;
+      for (int r = 0; r < R; r++) {
+        u32x4 v = b.x[r];
+        if (ACT != 0) v = decode8(b.x[r][0], e4m3_to_f32<0>(b.x[r][1]));  // exact BF16
+        *reinterpret_cast<u32x4*>(xbuf + r * kXSet + xw) = v;
+      }
+#pragma unroll
+      for (int r = 0; r < R; r++) A[r] = *reinterpret_cast<const u32x4*>(xbuf + r * kXSet + xrd);
     }
-#pragma unroll
-    for (int r = 0; r < R; r++) A[r] = *reinterpret_cast<const u32x4*>(xbuf + r * kXSet + xrd);
 #pragma unroll
     for (int t = 0; t < TN; t++) {
       uint32_t sc;
@@ -288,11 +441,22 @@ __device__ __forceinline__ void pass4(const StreamArgs& a, const uint8_t* wc, co
     for (int qq = 0; qq < kScaleRegs; qq++)
       sreg[qq] = __builtin_amdgcn_raw_buffer_load_b128(sr, chunk_src(threadIdx.x + qq * blockDim.x), 0, 0);
   }
+  XqRegs xq_regs;
+  if constexpr (ACT == 2) {
+    xq_issue(a, xq_regs);  // before the ring, so that waiting for them does not wait for it
+    __builtin_amdgcn_sched_barrier(0);
+  }
   StepBuf<TN, R, ACT> buf[kDepth];
 #pragma unroll
   for (int j = 0; j < kDepth; j++) {
     load(j, buf[j], kstep[j]);
     load_scales(j, j);
+  }
+  // In-call quantization of the (up to four) BF16 rows while the weight ring is in flight;
+  // the barrier after the scale copy below (or its own) publishes the rows.
+  if constexpr (ACT == 2) {
+    xq_finish(a, xq_regs, xbuf);
+    if (!SLDS) __syncthreads();
   }
   if (SLDS) {
     // Chunks past the tiles go to the spare 16 bytes after the scale rows, so the stores
@@ -392,9 +556,16 @@ __global__ __launch_bounds__(256) void stream_dense(StreamArgs a) {
   f32x4 acc[TN][R];
   pass4<TN, R, ACT, SLDS, dense_ring_depth(R)>(a, a.w_codes, a.w_scales, n0, 16, lim, rm, lds, acc);
   const float ts = a.apply_ts ? a.w_ts[0] : 1.0f;
+  float ts_q[4] = {0.f, 0.f, 0.f, 0.f};  // in-call quantized rows' tensor scales
+  if (ACT == 2) {
+    const float* tq = reinterpret_cast<const float*>(lds + lds_scale_bytes(TN, a.K, SLDS) +
+                                                     4 * xq_row_bytes(a.K) + 32);
+#pragma unroll
+    for (int m = 0; m < 4; m++) ts_q[m] = tq[m];  // before the reduction reuses the bytes
+  }
   reduce_store<TN, R>(acc, red, n0, [&](int m, int64_t n, float s) {
     if (m < a.M && n < a.N) {
-      const float f = (ACT == 0) ? ts : a.x_ts[m] * ts;
+      const float f = (ACT == 0) ? ts : (ACT == 2 ? ts_q[m & 3] * ts : a.x_ts[m] * ts);
       a.y[(int64_t)m * a.ldy + n] = s * f;
     }
   });
@@ -542,7 +713,7 @@ hipError_t launch_grouped_swiglu(const StreamArgs& a, int max_active, int W, boo
 
 template <int TN, int R, int ACT>
 hipError_t launch_dense(const StreamArgs& a, int W, bool slds, hipStream_t stream) {
-  const size_t lds = lds_bytes(TN, R, W, a.K, slds);
+  const size_t lds = lds_bytes(TN, R, W, a.K, slds, ACT);
   const int64_t groups = (a.N + 16 * TN - 1) / (16 * TN);
   if (slds)
     hipLaunchKernelGGL((stream_dense<TN, R, ACT, true>), dim3((uint32_t)groups), dim3(64 * W), lds,
@@ -644,15 +815,17 @@ hipError_t launch_stream_cfg(const StreamArgs& a, int act_kind, bool grouped, in
     }
   }
   const int R = (a.M + 3) / 4;
+  if (act_kind == 2) {  // in-call quantized activations: one row set, 16-row tiles
+    if (R != 1 || tn != 1 || W != waves_for_k(a.K)) return hipErrorInvalidValue;
+    return launch_dense<1, 1, 2>(a, W, slds, stream);
+  }
   return act_kind == 0 ? dense_tn<0>(a, tn, R, W, slds, stream)
                        : dense_tn<1>(a, tn, R, W, slds, stream);
 }
 
 hipError_t launch_stream(const StreamArgs& a, int act_kind, bool grouped, int max_active,
                          hipStream_t stream) {
-  const int64_t NS = (a.K + 127) / 128;  // 128-k steps per row
-  int W = (int)((NS + 7) / 8);           // about 8 steps per wave
-  W = W < 1 ? 1 : (W > 4 ? 4 : W);
+  const int W = waves_for_k(a.K);
   // up to two row sets: 16-row tiles keep the most workgroups in flight (M=8 at K=4096,
   // N=12288: 10.2 us against 10.6 us with 48-row tiles); more row sets: wider tiles share
   // each activation load among more weight rows

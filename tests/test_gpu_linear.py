@@ -413,3 +413,58 @@ def test_read_probe_reads_every_byte(dev):
             nv.read_probe(buf, u, sink)
             torch.cuda.synchronize()
             assert sink.cpu().view(torch.int32).numpy().view(np.uint32)[0] == mark, (u, where)
+
+
+# W4A4 with the activation quantization inside the call (decode-sized: M <= 4)
+@pytest.mark.parametrize("M,N,K,pad", [(1, 4096, 4096, 0), (4, 4096, 4096, 0), (3, 1000, 4128, 24),
+                                       (4, 777, 544, 8), (2, 12288, 8192, 0), (4, 64, 32, 0)])
+def test_w4a4_in_call_quantization(dev, o, M, N, K, pad):
+    """Bit for bit the two-call W4A4 (quantize_act, then the NVFP4-activation linear), and
+    within the bound of the oracle's W4A4 on the oracle's own quantization."""
+    _say(f"w4a4 in-call quantization M={M} N={N} K={K}")
+    w = weight_f32(40 + M, N, K)
+    (c, s, t), oq = quantize_both(o, w, dev)
+    xb = act_bf16(41 + M, M, K + pad)
+    xd = to_dev_bf16(xb, dev)[:, :K]
+    y = nv.linear(xd, c, s, t, quantize_x=True)
+    xc, xs, xt = nv.quantize_act(xd)
+    y2 = nv.linear(xc, c, s, t, x_scales=xs, x_ts=xt)
+    assert torch.equal(y, y2)
+    oc, os_, ot = o.quantize_bf16(np.ascontiguousarray(xb[:, :K]), per_row=True)
+    yr, b = o.linear_w4a4(oc, os_, ot, *oq)
+    assert_within(y.cpu().numpy(), yr, b, f"w4a4 in-call M={M} N={N} K={K}")
+
+
+def test_w4a4_in_call_quantization_ties(dev, o):
+    """Rows whose quotients land exactly on every E2M1 decision point (the hand-checked
+    block: amax 6 gives a scale of 448 and a denominator of exactly 1), on E2M1 values,
+    and just beside them: bit for bit the two-call result."""
+    K, N = 1024, 256
+    w = weight_f32(47, N, K)
+    (c, s, t), _ = quantize_both(o, w, dev)
+    blk = np.array([1, -0.5, 0.25, 0.75, 3, 6, -6, 0.1, -0.1, 1.25, 1.75, 2.5, 3.5, 5, -5, 0],
+                   np.float32)
+    rows = np.tile(blk, (4, K // 16))
+    rows[1] *= np.float32(1.0 + 2.0 ** -7)  # one BF16 step above each point
+    rows[2] *= np.float32(1.0 - 2.0 ** -8)  # one BF16 step below
+    rows[3, ::5] = 0.0
+    xd = torch.from_numpy(rows).to(dev).to(torch.bfloat16)
+    y = nv.linear(xd, c, s, t, quantize_x=True)
+    xc, xs, xt = nv.quantize_act(xd)
+    assert torch.equal(y, nv.linear(xc, c, s, t, x_scales=xs, x_ts=xt))
+
+
+def test_w4a4_in_call_quantization_nonfinite_row(dev, o):
+    """A NaN or Inf activation makes its row's outputs NaN; the other rows are unaffected."""
+    M, N, K = 4, 512, 1024
+    w = weight_f32(45, N, K)
+    (c, s, t), _ = quantize_both(o, w, dev)
+    xd = to_dev_bf16(act_bf16(46, M, K), dev)
+    ref = nv.linear(xd, c, s, t, quantize_x=True).clone()
+    for bad in (float("nan"), float("inf")):
+        xbad = xd.clone()
+        xbad[1, 77] = bad
+        y = nv.linear(xbad, c, s, t, quantize_x=True)
+        assert torch.isnan(y[1]).all()
+        for m in (0, 2, 3):
+            assert torch.equal(y[m], ref[m])
