@@ -206,8 +206,14 @@ def bench_single(nv, dev):
     timer.time(g.replay, 1)
     ms = timer.time(g.replay, 3) / R
     b = linear_bytes(M, N, K)
+    del g
+    # a launch this small is latency: the plain streaming read of the same bytes, timed the
+    # same way, is its measured floor
+    probe = read_probe_roof(nv, dev, b, timer)
+    gbps = b / (ms * 1e-3) / 1e9
     return {"workload": "M=1 K=2048 N=2048", "us": round(ms * 1e3, 3),
-            "GBps": round(b / (ms * 1e-3) / 1e9, 1), "bytes": b}
+            "GBps": round(gbps, 1), "bytes": b, "read_probe_us": probe["us"],
+            "frac_read_probe": round(gbps / probe["GBps"], 4)}
 
 
 def bench_prefill(nv, dev):
