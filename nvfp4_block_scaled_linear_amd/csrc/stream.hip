@@ -151,7 +151,6 @@ __host__ __device__ constexpr int waves_for_k(int64_t K) {
 // waiting for them does not wait for the ring), kQBlocks 16-blocks per thread: K <= 8192
 // keeps a.M * K/16 within kQBlocks * 64 * waves_for_k(K) for every K.
 constexpr int kQBlocks = 8;
-constexpr int64_t kQMaxK = 8192;
 
 struct XqRegs {
   u32x4 v[kQBlocks][2];
@@ -817,6 +816,7 @@ hipError_t launch_stream_cfg(const StreamArgs& a, int act_kind, bool grouped, in
   const int R = (a.M + 3) / 4;
   if (act_kind == 2) {  // in-call quantized activations: one row set, 16-row tiles
     if (R != 1 || tn != 1 || W != waves_for_k(a.K)) return hipErrorInvalidValue;
+    if (a.M * (a.K >> 4) > (int64_t)kQBlocks * 64 * W) return hipErrorInvalidValue;
     return launch_dense<1, 1, 2>(a, W, slds, stream);
   }
   return act_kind == 0 ? dense_tn<0>(a, tn, R, W, slds, stream)
