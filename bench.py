@@ -74,6 +74,70 @@ def warm_until(fn, seconds):
         torch.cuda.synchronize()
 
 
+class PowerSampler:
+    """Samples the GFX clock and the socket power through amdsmi (read-only queries) in a
+    background thread while the GPU runs a workload; also the change of the power-limit
+    residency counter over the window. Every figure is None where amdsmi or a metric is
+    not available."""
+
+    def __init__(self, period_s=0.004):
+        self.period = period_s
+        self.clk, self.pwr = [], []
+        self.ok = False
+        self.res = None
+
+    def _metrics(self):
+        m = self.smi.amdsmi_get_gpu_metrics_info(self.h)
+        return m.get("ppt_residency_acc"), m.get("accumulation_counter")
+
+    def __enter__(self):
+        import threading
+        try:
+            import amdsmi
+            self.smi = amdsmi
+            amdsmi.amdsmi_init()
+            self.h = amdsmi.amdsmi_get_processor_handles()[0]
+            self.m0 = self._metrics()
+            self.ok = True
+        except Exception:
+            return self
+        self.stop = threading.Event()
+
+        def poll():
+            while not self.stop.is_set():
+                try:
+                    self.clk.append(float(self.smi.amdsmi_get_clock_info(
+                        self.h, self.smi.AmdSmiClkType.GFX)["clk"]))
+                    self.pwr.append(float(self.smi.amdsmi_get_power_info(self.h)["current_socket_power"]))
+                except Exception:
+                    pass
+                time.sleep(self.period)
+        self.th = threading.Thread(target=poll, daemon=True)
+        self.th.start()
+        return self
+
+    def __exit__(self, *exc):
+        if not self.ok:
+            return False
+        self.stop.set()
+        self.th.join()
+        frac = None
+        try:
+            m1 = self._metrics()
+            if all(isinstance(v, (int, float)) for v in (*self.m0, *m1)) and m1[1] > self.m0[1]:
+                frac = round((m1[0] - self.m0[0]) / (m1[1] - self.m0[1]), 3)
+        except Exception:
+            pass
+        try:
+            self.smi.amdsmi_shut_down()
+        except Exception:
+            pass
+        med = lambda v: round(float(np.median(v)), 1) if v else None  # noqa: E731
+        self.res = {"gfx_clock_mhz_median": med(self.clk), "socket_power_w_median": med(self.pwr),
+                    "samples": len(self.clk), "power_limit_residency": frac}
+        return False
+
+
 def capture(fn):
     """Records fn's launches into a HIP graph (torch's capture on a side stream)."""
     g = torch.cuda.CUDAGraph()
@@ -233,10 +297,14 @@ def bench_prefill(nv, dev):
     timer = Timer()
     warm_until(g.replay, 0.15)  # the clock settles under sustained MFMA load
     ms = timer.time(g.replay, 10) / R
+    # clock and power under the same load, sampled outside the timed region
+    with PowerSampler() as ps:
+        warm_until(g.replay, 0.3)
     flops = 2.0 * M * N * K
     tf = flops / (ms * 1e-3) / 1e12
     return {"workload": "M=2048 K=4096 N=14336", "us": round(ms * 1e3, 2), "TFLOPs": round(tf, 1),
-            "frac_bf16_mfma": round(tf / BF16_PEAK_TFLOPS, 4), "flop": flops}
+            "frac_bf16_mfma": round(tf / BF16_PEAK_TFLOPS, 4), "flop": flops,
+            "clock_power": ps.res}
 
 
 def bench_w4a4(nv, dev):
