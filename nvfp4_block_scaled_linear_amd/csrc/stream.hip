@@ -737,15 +737,17 @@ hipError_t launch_grouped(const StreamArgs& a, int max_active, int W, bool slds,
   return hipGetLastError();
 }
 
+// Wider tiles are chosen only for three or more row sets (launch_stream), so only those
+// combinations are built.
 template <int TN, int ACT>
 hipError_t dense_r(const StreamArgs& a, int R, int W, bool slds, hipStream_t stream) {
-  switch (R) {
-    case 1: return launch_dense<TN, 1, ACT>(a, W, slds, stream);
-    case 2: return launch_dense<TN, 2, ACT>(a, W, slds, stream);
-    case 3: return launch_dense<TN, 3, ACT>(a, W, slds, stream);
-    case 4: return launch_dense<TN, 4, ACT>(a, W, slds, stream);
-    default: return hipErrorInvalidValue;
+  if constexpr (TN == 1) {
+    if (R == 1) return launch_dense<1, 1, ACT>(a, W, slds, stream);
+    if (R == 2) return launch_dense<1, 2, ACT>(a, W, slds, stream);
   }
+  if (R == 3) return launch_dense<TN, 3, ACT>(a, W, slds, stream);
+  if (R == 4) return launch_dense<TN, 4, ACT>(a, W, slds, stream);
+  return hipErrorInvalidValue;
 }
 
 template <int ACT>
