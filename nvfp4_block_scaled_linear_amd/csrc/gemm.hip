@@ -540,7 +540,7 @@ struct SkRegB {  // one K step of this lane's weight column: 32 codes and their 
 
 template <int ACT>
 __global__ __launch_bounds__(1024) void gemm_splitk(GemmArgs a) {
-  extern __shared__ __attribute__((aligned(16))) uint16_t lds_k[];  // [4][2][BM * LDA]
+  extern __shared__ __attribute__((aligned(16))) uint16_t lds_k[];  // [4][4][BM * LDA]
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -549,12 +549,23 @@ __global__ __launch_bounds__(1024) void gemm_splitk(GemmArgs a) {
   const int64_t M = a.M, N = a.N, K = a.K;
   const uint32_t Ku = (uint32_t)K;
 
-  const int64_t nbm = (M + kSkBM - 1) / kSkBM, nbn = (N + kSkBN - 1) / kSkBN;
-  const int64_t total = nbm * nbn;
-  int64_t lin = blockIdx.x;
-  if (total % 8 == 0) lin = (lin % 8) * (total / 8) + lin / 8;  // XCD runs share rows
-  const int64_t m0 = (int64_t)__builtin_amdgcn_readfirstlane((int)(lin / nbn)) * kSkBM;
-  const int64_t n0 = (int64_t)__builtin_amdgcn_readfirstlane((int)(lin % nbn)) * kSkBN;
+  const int64_t nbn = (N + kSkBN - 1) / kSkBN;
+  // XCD-aware order, weight-stationary: here the weight is the larger operand (W4A4
+  // M = 512, N = K = 4096: 9.4 MB against 1.1 MB), so XCD x (blockIdx % 8) takes the
+  // column tiles [x * nbn / 8, (x + 1) * nbn / 8) for every row tile and fetches only its
+  // eighth of the weight, rather than all of it for one row tile
+  const int64_t lin = blockIdx.x;
+  int64_t mi, ni;
+  if (nbn % 8 == 0) {
+    const int64_t per = nbn / 8, j = lin / 8;
+    mi = j / per;
+    ni = (lin % 8) * per + j % per;
+  } else {
+    mi = lin / nbn;
+    ni = lin % nbn;
+  }
+  const int64_t m0 = (int64_t)__builtin_amdgcn_readfirstlane((int)mi) * kSkBM;
+  const int64_t n0 = (int64_t)__builtin_amdgcn_readfirstlane((int)ni) * kSkBN;
   const int64_t rows_m = (M - m0) < kSkBM ? (M - m0) : kSkBM;
   const int64_t rows_n = (N - n0) < kSkBN ? (N - n0) : kSkBN;
 
@@ -581,7 +592,7 @@ __global__ __launch_bounds__(1024) void gemm_splitk(GemmArgs a) {
   const int nl = 32 * wn + col;
   const uint32_t woff = nl < rows_n ? (uint32_t)(nl * (K >> 1)) : kOOB;
   const uint32_t soff = nl < rows_n ? (uint32_t)(nl * (K >> 4)) : kOOB;
-  uint16_t* as = lds_k + ks * 2 * (kSkBM * LDA);  // this quarter's two buffers
+  uint16_t* as = lds_k + ks * 4 * (kSkBM * LDA);  // this quarter's four buffers
 
   auto issue = [&](int kt, SkRegA<ACT>& ra, SkRegB& rb) {
     const uint32_t k0 = (uint32_t)(kbeg + kt) * BK;
@@ -637,16 +648,19 @@ __global__ __launch_bounds__(1024) void gemm_splitk(GemmArgs a) {
     for (int r = 0; r < 16; r++) acc[mt][r] = 0.f;
 
   // Loads run four steps ahead in a ring of four register sets (the steps are short: a
-  // wave's step is eight MFMAs). Step kt multiplies LDS buffer kt & 1 with its decoded
-  // weights while decoding step kt + 1's weights and staging its activations into the
-  // other buffer, then refills the set it freed with step kt + 4.
+  // wave's step is eight MFMAs). Step kt multiplies LDS buffer kt & 3 with its decoded
+  // weights while decoding step kt + 1's weights and staging step kt + 2's activations
+  // into buffer (kt + 2) & 3, then refills the set it freed with step kt + 4. Staging two
+  // steps ahead into four buffers needs a workgroup barrier only after every second step:
+  // a buffer read in steps kt - 2 or kt - 1 is rewritten in step kt or kt + 1, after the
+  // barrier that ends step kt - 1 (kt even).
   SkRegA<ACT> ra[4];
   SkRegB rb[4];
   u32x4 bd[2][4];
   auto step = [&](auto ic, int kt) {
     constexpr int I = decltype(ic)::value;
     constexpr int J = (I + 1) & 3;
-    const uint16_t* src = as + (kt & 1) * (kSkBM * LDA);
+    const uint16_t* src = as + (kt & 3) * (kSkBM * LDA);
     u32x4 af[8];
 #pragma unroll
     for (int i = 0; i < 8; i++)
@@ -662,17 +676,18 @@ __global__ __launch_bounds__(1024) void gemm_splitk(GemmArgs a) {
       if (i < 6) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);      // one LDS read
       __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);                 // VALU
     }
-    write_a(ra[J], (kt + 1) & 1);
+    write_a(ra[(I + 2) & 3], (kt + 2) & 3);
     __builtin_amdgcn_sched_barrier(0);
     issue(kt + 4, ra[I], rb[I]);
     __builtin_amdgcn_sched_barrier(0);
-    __syncthreads();
+    if (I & 1) __syncthreads();
   };
 
 #pragma unroll
   for (int i = 0; i < 4; i++) issue(i, ra[i], rb[i]);
   decode(rb[0], bd[0]);
   write_a(ra[0], 0);
+  write_a(ra[1], 1);
   __syncthreads();
   for (int kt = 0; kt < KT4; kt += 4) {
     step(std::integral_constant<int, 0>{}, kt);
@@ -714,7 +729,7 @@ __global__ __launch_bounds__(1024) void gemm_splitk(GemmArgs a) {
 template <int ACT>
 hipError_t launch_splitk(const GemmArgs& a, hipStream_t stream) {
   const int64_t blocks = ((a.M + kSkBM - 1) / kSkBM) * ((a.N + kSkBN - 1) / kSkBN);
-  const size_t stage = (size_t)kSkSplit * 2 * kSkBM * LDA * sizeof(uint16_t);
+  const size_t stage = (size_t)kSkSplit * 4 * kSkBM * LDA * sizeof(uint16_t);
   const size_t red = (size_t)(kSkSplit - 1) * 4 * 2 * 16 * 64 * sizeof(float);
   hipLaunchKernelGGL((gemm_splitk<ACT>), dim3((uint32_t)blocks), dim3(1024),
                      stage > red ? stage : red, stream, a);

@@ -264,6 +264,11 @@ def test_linear_splitk_ragged(dev, o):
     y4 = nv.linear(xc, c, s, t, x_scales=xs, x_ts=xt)
     yr4, b4 = o.linear_w4a4(oc, os_, ot, *oq)
     assert_within(y4.cpu().numpy(), yr4, b4, "split-K w4a4")
+    # five 128-column tiles: not a multiple of the eight XCDs, so the plain tile order
+    M, N, K = 200, 600, 1024
+    _say(f"split-K gemm M={M} N={N} K={K}")
+    y, yr, b = _linear_case(dev, o, M, N, K, seed=94)
+    assert_within(y, yr, b, "split-K bf16, five column tiles")
 
 
 def test_linear_leading_dimensions(dev, o):
