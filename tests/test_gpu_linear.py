@@ -342,6 +342,25 @@ def test_negative_control_corrupted_scale_is_detected(dev, o, sweep_weight):
     assert bad_cols.tolist() == [123]
 
 
+@pytest.mark.parametrize("M", [4, 40])  # the streaming kernel, the K-split GEMM
+def test_negative_control_flipped_nibble_is_detected(dev, o, sweep_weight, M):
+    """One weight code with its exponent bit flipped (a magnitude from {0, 1/2, 1, 3/2}
+    swapped with one from {2, 3, 4, 6}) must break parity, in that column only."""
+    cfg = WORKLOADS["decode_sweep"]
+    (c, s, t), _, wdq = sweep_weight
+    xb = act_bf16(cfg["x_seed_base"] + 7, M, cfg["K"])
+    xf = o.bf16_to_f64(xb)
+    k = int(np.argmax(np.max(np.abs(xf), axis=0)))  # a k where some row has a large |x|
+    c_bad = c.clone()
+    c_bad[77, k // 2] ^= 0x04 if k % 2 == 0 else 0x40  # low nibble holds the even k
+    y = nv.linear(to_dev_bf16(xb, dev), c_bad, s, t).cpu().numpy()
+    yr, b = o.linear_f64(xf, wdq)
+    ok, _ = oracle.within_bound(y, yr, b)
+    assert not ok
+    bad_cols = np.nonzero(np.any(np.abs(y - yr) > 1e-4 * b + 1e-6, axis=0))[0]
+    assert bad_cols.tolist() == [77]
+
+
 def test_prefill_full_sampled_rows(dev, o):
     cfg = WORKLOADS["prefill"]
     M, N, K = cfg["M"], cfg["N"], cfg["K"]
