@@ -594,33 +594,46 @@ __global__ __launch_bounds__(1024) void gemm_splitk(GemmArgs a) {
   const uint32_t soff = nl < rows_n ? (uint32_t)(nl * (K >> 4)) : kOOB;
   uint16_t* as = lds_k + ks * 4 * (kSkBM * LDA);  // this quarter's four buffers
 
+  // Offsets: the per-thread part is fixed over the steps and carries the row's
+  // out-of-range bit; a step adds its k0 part and one uniform out-of-range term. K is
+  // whole 64-k steps here, so every k of a step lies below K exactly when k0 does, and
+  // the sums stay below 2^31 before the out-of-range bit (no carry into it).
+  uint32_t xo[2], xso[2];
+#pragma unroll
+  for (int q = 0; q < 2; q++) {
+    const int c = gt + 256 * q;
+    const int row = c >> 3, ch = c & 7;
+    const uint32_t rowok = row < rows_m ? 0u : kOOB;
+    if (ACT == 0) {
+      xo[q] = ((uint32_t)(row * a.ldx * 2) + 16u * ch) | rowok;
+      xso[q] = 0;
+    } else {
+      xo[q] = ((uint32_t)(row * (K >> 1)) + 4u * ch) | rowok;
+      // the step's four scale bytes of the row as one dword (K % 64 == 0 keeps it inside
+      // the row); the piece's byte is picked at staging
+      xso[q] = (uint32_t)(row * (K >> 4)) | rowok;
+    }
+  }
+  const uint32_t wo = woff + 16u * h;  // this lane's K half of each step's 32 code bytes
+
   auto issue = [&](int kt, SkRegA<ACT>& ra, SkRegB& rb) {
     const uint32_t k0 = (uint32_t)(kbeg + kt) * BK;
-    const uint32_t out = kt < KTs ? 0u : kOOB;  // padding steps (uniform)
+    // padding steps and steps past K (uniform)
+    const uint32_t out = (kt < KTs ? 0u : kOOB) | past(Ku, k0);
 #pragma unroll
     for (int q = 0; q < 2; q++) {
-      const int c = gt + 256 * q;
-      const int row = c >> 3, ch = c & 7;
-      const uint32_t k = k0 + 8u * ch;
-      const uint32_t rowok = row < rows_m ? 0u : kOOB;
       if (ACT == 0) {
-        const uint32_t off = (uint32_t)(row * a.ldx * 2) + 2u * k;
-        ra.v[q] = __builtin_amdgcn_raw_buffer_load_b128(xr, off | rowok | out | past(Ku, k), 0, 0);
+        ra.v[q] = __builtin_amdgcn_raw_buffer_load_b128(xr, (xo[q] + 2u * k0) | out, 0, 0);
       } else {
-        // the step's four scale bytes of the row as one dword (K % 64 == 0 keeps it inside
-        // the row); the piece's byte is picked at staging
-        const uint32_t oc = (uint32_t)(row * (K >> 1)) + (k >> 1);
-        const uint32_t os = (uint32_t)(row * (K >> 4)) + (k0 >> 4);
-        ra.c[q] = __builtin_amdgcn_raw_buffer_load_b32(xr, oc | rowok | out | past(Ku, k), 0, 0);
-        ra.s[q] = __builtin_amdgcn_raw_buffer_load_b32(xsr, os | rowok | out | past(Ku, k0), 0, 0);
+        ra.c[q] = __builtin_amdgcn_raw_buffer_load_b32(xr, (xo[q] + (k0 >> 1)) | out, 0, 0);
+        ra.s[q] = __builtin_amdgcn_raw_buffer_load_b32(xsr, (xso[q] + (k0 >> 4)) | out, 0, 0);
       }
     }
-    const uint32_t kh = k0 + 32u * h;
-    rb.c = __builtin_amdgcn_raw_buffer_load_b128(wr, (woff + (kh >> 1)) | out | past(Ku, kh), 0, 0);
+    rb.c = __builtin_amdgcn_raw_buffer_load_b128(wr, (wo + (k0 >> 1)) | out, 0, 0);
     // the step's four scale bytes (both halves) as one dword; this half's two are picked
     // at decode (a 16-bit load here would leave a zero-extension that the compiler hoists
     // to the loop head, waiting there for every load in flight)
-    rb.s = __builtin_amdgcn_raw_buffer_load_b32(sr, (soff + (k0 >> 4)) | out | past(Ku, k0), 0, 0);
+    rb.s = __builtin_amdgcn_raw_buffer_load_b32(sr, (soff + (k0 >> 4)) | out, 0, 0);
   };
   auto write_a = [&](const SkRegA<ACT>& ra, int buf) {
     uint16_t* dst = as + buf * (kSkBM * LDA);
