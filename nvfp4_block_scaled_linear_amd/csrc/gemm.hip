@@ -531,11 +531,9 @@ template <int ACT>
 struct SkRegA {  // one K step of this thread's activation loads (two 16-byte pieces)
   u32x4 v[ACT == 0 ? 2 : 1];
   uint32_t c[ACT == 0 ? 1 : 2];
-  uint32_t s[ACT == 0 ? 1 : 2];
 };
-struct SkRegB {  // one K step of this lane's weight column: 32 codes and their 2 scales
+struct SkRegB {  // one K step of this lane's weight column: 32 codes
   u32x4 c;
-  uint32_t s;
 };
 
 template <int ACT>
@@ -569,12 +567,14 @@ __global__ __launch_bounds__(1024) void gemm_splitk(GemmArgs a) {
   const int64_t rows_m = (M - m0) < kSkBM ? (M - m0) : kSkBM;
   const int64_t rows_n = (N - n0) < kSkBN ? (N - n0) : kSkBN;
 
-  // this quarter's steps: kbeg .. kbeg + KTs - 1, run in whole rounds of four (padding
-  // steps and steps past K read zeros)
+  // this quarter's steps: kbeg .. kbeg + KTs - 1, in whole rounds of four (padding steps
+  // and steps past K read zeros). Quarters start on a round (KTs a multiple of four) and
+  // K is whole rounds (K % 256 == 0), so no round crosses K: a round's 16-byte scale
+  // pieces lie inside their rows or wholly past K.
   const int KT = (int)((K + BK - 1) / BK);
-  const int KTs = (KT + kSkSplit - 1) / kSkSplit;
+  const int KTs = (((KT + kSkSplit - 1) / kSkSplit) + 3) & ~3;
   const int kbeg = ks * KTs;
-  const int KT4 = (KTs + 3) & ~3;
+  const int KT4 = KTs;
 
   __amdgpu_buffer_rsrc_t xr, xsr;
   if (ACT == 0) {
@@ -622,36 +622,56 @@ __global__ __launch_bounds__(1024) void gemm_splitk(GemmArgs a) {
     const uint32_t out = (kt < KTs ? 0u : kOOB) | past(Ku, k0);
 #pragma unroll
     for (int q = 0; q < 2; q++) {
-      if (ACT == 0) {
+      if (ACT == 0)
         ra.v[q] = __builtin_amdgcn_raw_buffer_load_b128(xr, (xo[q] + 2u * k0) | out, 0, 0);
-      } else {
+      else
         ra.c[q] = __builtin_amdgcn_raw_buffer_load_b32(xr, (xo[q] + (k0 >> 1)) | out, 0, 0);
-        ra.s[q] = __builtin_amdgcn_raw_buffer_load_b32(xsr, (xso[q] + (k0 >> 4)) | out, 0, 0);
-      }
     }
     rb.c = __builtin_amdgcn_raw_buffer_load_b128(wr, (wo + (k0 >> 1)) | out, 0, 0);
-    // the step's four scale bytes (both halves) as one dword; this half's two are picked
-    // at decode (a 16-bit load here would leave a zero-extension that the compiler hoists
-    // to the loop head, waiting there for every load in flight)
-    rb.s = __builtin_amdgcn_raw_buffer_load_b32(sr, (soff + (k0 >> 4)) | out, 0, 0);
   };
-  auto write_a = [&](const SkRegA<ACT>& ra, int buf) {
+  // Scales come four steps at a time: one 16-byte piece per weight column (each step's
+  // dword holds its four scale bytes, both K halves) and per activation row, i.e. a
+  // quarter of the cache lines that a load per step would touch. Slot 0 holds the
+  // current round of four steps, slot 1 the next. A step outside the quarter or past K
+  // takes zero scales, as its codes are zero; the piece may reach past the row there.
+  u32x4 wsc[2];
+  u32x4 xsc[2][ACT == 0 ? 1 : 2];
+  auto issue_scales = [&](int kt, u32x4& w, u32x4 (&x)[ACT == 0 ? 1 : 2]) {
+    const uint32_t k0 = (uint32_t)(kbeg + kt) * BK;
+    const uint32_t out = (kt < KTs ? 0u : kOOB) | past(Ku, k0);
+    if (ACT != 0) {
+#pragma unroll
+      for (int q = 0; q < 2; q++)
+        x[q] = __builtin_amdgcn_raw_buffer_load_b128(xsr, (xso[q] + (k0 >> 4)) | out, 0, 0);
+    }
+    w = __builtin_amdgcn_raw_buffer_load_b128(sr, (soff + (k0 >> 4)) | out, 0, 0);
+  };
+  const int KTq = KT - kbeg;  // steps of this quarter below K
+  auto live = [&](int kt) { return kt < KTs && kt < KTq; };  // uniform
+  auto write_a = [&](const SkRegA<ACT>& ra, uint32_t xs0, uint32_t xs1, int buf) {
     uint16_t* dst = as + buf * (kSkBM * LDA);
 #pragma unroll
     for (int q = 0; q < 2; q++) {
       const int c = gt + 256 * q;
-      const int row = c >> 3, ch = c & 7;
+      const int ch = c & 7;
+      const int row = c >> 3;
       u32x4 v;
       if (ACT == 0) v = ra.v[q];
-      else v = decode8(ra.c[q], e4m3_to_f32<0>(ra.s[q] >> (8 * (ch >> 1))));  // exact BF16
+      else v = decode8(ra.c[q], e4m3_to_f32<0>((q ? xs1 : xs0) >> (8 * (ch >> 1))));  // exact BF16
       *reinterpret_cast<u32x4*>(dst + row * LDA + 8 * ch) = v;
     }
   };
-  auto decode = [&](const SkRegB& rb, u32x4 (&bd)[4]) {
-    const uint32_t sw = rb.s >> (16 * h);
+  auto decode = [&](const SkRegB& rb, uint32_t sdw, u32x4 (&bd)[4]) {
+    const uint32_t sw = sdw >> (16 * h);
     const float s0 = e4m3_to_f32<0>(sw), s1 = e4m3_to_f32<1>(sw);
 #pragma unroll
     for (int j = 0; j < 4; j++) bd[j] = decode8(rb.c[j], j < 2 ? s0 : s1);
+  };
+  // the step's scale dwords: step kt of the current round (slot 0) or the next (slot 1)
+  auto wscale = [&](int slot, int j, int kt) { return live(kt) ? wsc[slot][j] : 0u; };
+  auto xscale = [&](int slot, int j, int q, int kt) {
+    if constexpr (ACT == 0) return 0u;
+    else return live(kt) ? xsc[slot][q][j] : 0u;
   };
 
   f32x16 acc[2];
@@ -680,7 +700,8 @@ __global__ __launch_bounds__(1024) void gemm_splitk(GemmArgs a) {
       af[i] = *reinterpret_cast<const u32x4*>(src + (32 * (i & 1) + col) * LDA + 32 * h + 8 * (i >> 1));
 #pragma unroll
     for (int i = 0; i < 8; i++) acc[i & 1] = mfma32(af[i], bd[I & 1][i >> 1], acc[i & 1]);
-    decode(rb[J], bd[J & 1]);
+    constexpr int SD = (I + 1) >> 2, JD = (I + 1) & 3;  // slot and index of step kt + 1
+    decode(rb[J], wscale(SD, JD, kt + 1), bd[J & 1]);
     // interleave: operand reads two ahead of their MFMA, the next step's decode between
     __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
@@ -689,18 +710,28 @@ __global__ __launch_bounds__(1024) void gemm_splitk(GemmArgs a) {
       if (i < 6) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);      // one LDS read
       __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);                 // VALU
     }
-    write_a(ra[(I + 2) & 3], (kt + 2) & 3);
+    constexpr int SA = (I + 2) >> 2, JA = (I + 2) & 3;  // slot and index of step kt + 2
+    write_a(ra[(I + 2) & 3], xscale(SA, JA, 0, kt + 2), xscale(SA, JA, 1, kt + 2), (kt + 2) & 3);
     __builtin_amdgcn_sched_barrier(0);
     issue(kt + 4, ra[I], rb[I]);
+    if (I == 0) issue_scales(kt + 4, wsc[1], xsc[1]);  // the next round's
     __builtin_amdgcn_sched_barrier(0);
     if (I & 1) __syncthreads();
+    if (I == 3) {  // the next round becomes the current one
+      wsc[0] = wsc[1];
+      if constexpr (ACT != 0) {
+        xsc[0][0] = xsc[1][0];
+        xsc[0][1] = xsc[1][1];
+      }
+    }
   };
 
+  issue_scales(0, wsc[0], xsc[0]);
 #pragma unroll
   for (int i = 0; i < 4; i++) issue(i, ra[i], rb[i]);
-  decode(rb[0], bd[0]);
-  write_a(ra[0], 0);
-  write_a(ra[1], 1);
+  decode(rb[0], wscale(0, 0, 0), bd[0]);
+  write_a(ra[0], xscale(0, 0, 0, 0), xscale(0, 0, 1, 0), 0);
+  write_a(ra[1], xscale(0, 1, 0, 1), xscale(0, 1, 1, 1), 1);
   __syncthreads();
   for (int kt = 0; kt < KT4; kt += 4) {
     step(std::integral_constant<int, 0>{}, kt);
@@ -808,9 +839,10 @@ hipError_t launch_gemm_grouped(const GemmArgs& a, int act_kind, int64_t max_tile
 int64_t gemm_max_ldx() { return ((int64_t)1 << 31) / (2 * 256) - 1; }
 
 // K split four ways when the 64 x 256 tiles would not give every CU a workgroup, the K
-// quarters stay at least four steps long and K is whole 64-k steps
+// quarters stay at least four steps long and K is whole rounds of four 64-k steps
 bool use_splitk(int64_t M, int64_t N, int64_t K) {
-  return ((M + 63) / 64) * ((N + BN - 1) / BN) < 256 && K >= 4 * kSkSplit * BK && K % BK == 0;
+  return ((M + 63) / 64) * ((N + BN - 1) / BN) < 256 && K >= 4 * kSkSplit * BK &&
+         K % (4 * BK) == 0;
 }
 
 hipError_t launch_gemm(const GemmArgs& a, int act_kind, hipStream_t stream) {

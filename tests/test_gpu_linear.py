@@ -249,9 +249,10 @@ def test_linear_wide_tiles_padded_rows(dev, o):
 
 def test_linear_splitk_ragged(dev, o):
     """The K-split GEMM (chosen when 64 x 256 tiles would leave CUs idle) on ragged M and
-    N with 33 K steps, so that the last K quarter runs past K and its last steps read
-    zeros; padded activation and output rows; BF16 and NVFP4 activations, every output."""
-    M, N, K = 300, 1000, 2112
+    N with 36 K steps: the quarters take whole rounds of four steps (12, 12, 12), so the
+    last quarter lies wholly past K and reads zeros; padded activation and output rows;
+    BF16 and NVFP4 activations, every output."""
+    M, N, K = 300, 1000, 2304
     _say(f"split-K gemm M={M} N={N} K={K}")
     y, yr, b = _linear_case(dev, o, M, N, K, seed=91, pad_x=40, pad_y=24)
     assert_within(y, yr, b, "split-K bf16")
