@@ -609,8 +609,8 @@ __global__ __launch_bounds__(1024) void gemm_splitk(GemmArgs a) {
       xso[q] = 0;
     } else {
       xo[q] = ((uint32_t)(row * (K >> 1)) + 4u * ch) | rowok;
-      // the step's four scale bytes of the row as one dword (K % 64 == 0 keeps it inside
-      // the row); the piece's byte is picked at staging
+      // the row's scales, loaded a round (16 bytes) at a time; the piece's byte is picked
+      // at staging
       xso[q] = (uint32_t)(row * (K >> 4)) | rowok;
     }
   }
@@ -632,8 +632,9 @@ __global__ __launch_bounds__(1024) void gemm_splitk(GemmArgs a) {
   // Scales come four steps at a time: one 16-byte piece per weight column (each step's
   // dword holds its four scale bytes, both K halves) and per activation row, i.e. a
   // quarter of the cache lines that a load per step would touch. Slot 0 holds the
-  // current round of four steps, slot 1 the next. A step outside the quarter or past K
-  // takes zero scales, as its codes are zero; the piece may reach past the row there.
+  // current round of four steps, slot 1 the next. A round lies wholly inside the quarter
+  // and below K, or it reads zeros; a step outside the quarter or past K also takes zero
+  // scales explicitly (live), as its codes are zero.
   u32x4 wsc[2];
   u32x4 xsc[2][ACT == 0 ? 1 : 2];
   auto issue_scales = [&](int kt, u32x4& w, u32x4 (&x)[ACT == 0 ? 1 : 2]) {
