@@ -86,17 +86,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int64_t nbn = SWIGLU ? (half + BN / 2 - 1) / (BN / 2) : (N + BN - 1) / BN;
 
   int64_t m0 = 0, n0, rows_m;
+  // grouped: tile tile_of and column block cb_of of this workgroup. XCD x (blockIdx % 8)
+  // takes tiles x, x + 8, ... with all their column blocks, so a tile's gathered
+  // activation rows are fetched into one XCD's L2 rather than into every XCD's
+  const int64_t bx = blockIdx.x;
+  const int64_t tile_of = (bx % 8) + 8 * (bx / (8 * nbn));
+  const int64_t cb_of = (bx / 8) % nbn;
   const uint8_t* wcodes = a.w_codes;
   const uint8_t* wscales = a.w_scales;
   float ts = a.w_ts[0];
   if (GROUPED) {
-    const int64_t tile = blockIdx.x / nbn;
+    const int64_t tile = tile_of;
     if (tile >= *a.n_tiles) return;  // uniform over the workgroup
     const int e = a.tiles[2 * tile];
     const int32_t beg = a.tiles[2 * tile + 1];
     const int32_t end = a.offsets[e + 1];
     rows_m = (end - beg) < BM ? (end - beg) : BM;
-    n0 = (blockIdx.x % nbn) * BN;
+    n0 = cb_of * BN;
     wcodes += (int64_t)e * N * (K >> 1);
     wscales += (int64_t)e * N * (K >> 4);
     ts = a.apply_ts ? a.w_ts[e] : 1.0f;
@@ -120,7 +126,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int64_t rows_n = (N - n0) < BN ? (N - n0) : BN;
   // this wave's first weight column: n0 + 64 * wave, or for SwiGLU the gate half (waves
   // 0, 1: n0 = tile * 128) and the matching up half (waves 2, 3)
-  const int64_t wcol0 = SWIGLU ? (wave < 2 ? 0 : half) + (blockIdx.x % nbn) * (BN / 2) + 64 * (wave & 1)
+  const int64_t wcol0 = SWIGLU ? (wave < 2 ? 0 : half) + cb_of * (BN / 2) + 64 * (wave & 1)
                                : n0 + 64 * wave;
   const int64_t col_end = SWIGLU ? (wave < 2 ? half : N) : N;
 
@@ -812,13 +818,15 @@ template <int ACT>
 hipError_t launch_grouped_mt(const GemmArgs& a, int64_t max_tiles, hipStream_t stream) {
   constexpr int BM = 32 * kGroupedMT;
   const size_t lds = 2 * (size_t)BM * LDA * sizeof(uint16_t);
+  // whole groups of eight tiles (the tiles past the list's end return at once)
+  const int64_t tiles8 = (max_tiles + 7) / 8 * 8;
   if (a.a_out) {
-    const int64_t blocks = max_tiles * (((a.N >> 1) + BN / 2 - 1) / (BN / 2));
+    const int64_t blocks = tiles8 * (((a.N >> 1) + BN / 2 - 1) / (BN / 2));
     const size_t xch = (size_t)2 * kGroupedMT * 2 * 16 * 64 * sizeof(float);
     hipLaunchKernelGGL((gemm_kernel<kGroupedMT, ACT, true, true>), dim3((uint32_t)blocks),
                        dim3(256), lds > xch ? lds : xch, stream, a);
   } else {
-    const int64_t blocks = max_tiles * ((a.N + BN - 1) / BN);
+    const int64_t blocks = tiles8 * ((a.N + BN - 1) / BN);
     hipLaunchKernelGGL((gemm_kernel<kGroupedMT, ACT, true>), dim3((uint32_t)blocks), dim3(256),
                        lds, stream, a);
   }
