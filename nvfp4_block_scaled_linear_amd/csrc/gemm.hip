@@ -87,10 +87,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   int64_t m0 = 0, n0, rows_m;
   // grouped: tile tile_of and column block cb_of of this workgroup. XCD x (blockIdx % 8)
-  // takes tiles x, x + 8, ... with all their column blocks, so a tile's gathered
-  // activation rows are fetched into one XCD's L2 rather than into every XCD's
+  // takes the x-th eighth of the tile list, each tile with all its column blocks: a
+  // tile's gathered activation rows are fetched into one XCD's L2, and so, mostly, are
+  // the weights of an expert (its tiles are consecutive)
   const int64_t bx = blockIdx.x;
-  const int64_t tile_of = (bx % 8) + 8 * (bx / (8 * nbn));
+  const int64_t per_xcd = GROUPED ? (*a.n_tiles + 7) / 8 : 0;  // tiles per XCD
+  const int64_t tile_of = (bx / 8) / nbn < per_xcd ? (bx % 8) * per_xcd + (bx / 8) / nbn
+                                                   : INT64_MAX;  // past this XCD's share
   const int64_t cb_of = (bx / 8) % nbn;
   const uint8_t* wcodes = a.w_codes;
   const uint8_t* wscales = a.w_scales;
