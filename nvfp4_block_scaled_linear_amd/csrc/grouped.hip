@@ -211,8 +211,11 @@ __global__ __launch_bounds__(kSortThreads) void route_scan_chunks(int E, int64_t
   int32_t* wsum = sh;      // [16]
   int32_t* cnt = sh + 16;  // [E] routes per expert, then each expert's first slot
   const int tid = threadIdx.x;
+  // (the chunk loops are unrolled so that their loads are in flight together rather than
+  // one round trip per chunk)
   for (int e = tid; e < E; e += kSortThreads) {
     int32_t c = 0;
+#pragma unroll 8
     for (int64_t k = 0; k < nchunks; k++) c += ws.chunk_counts[k * E + e];
     cnt[e] = c;
   }
@@ -221,10 +224,15 @@ __global__ __launch_bounds__(kSortThreads) void route_scan_chunks(int E, int64_t
   // chunk k's first slot for expert e: e's first slot plus the earlier chunks' counts
   for (int e = tid; e < E; e += kSortThreads) {
     int32_t run = cnt[e];
-    for (int64_t k = 0; k < nchunks; k++) {
-      const int32_t c = ws.chunk_counts[k * E + e];
-      ws.chunk_counts[k * E + e] = run;
-      run += c;
+    for (int64_t k0 = 0; k0 < nchunks; k0 += 8) {  // eight counts loaded, then stored
+      int32_t c[8];
+#pragma unroll
+      for (int j = 0; j < 8; j++) c[j] = k0 + j < nchunks ? ws.chunk_counts[(k0 + j) * E + e] : 0;
+#pragma unroll
+      for (int j = 0; j < 8; j++) {
+        if (k0 + j < nchunks) ws.chunk_counts[(k0 + j) * E + e] = run;
+        run += c[j];
+      }
     }
   }
 }
