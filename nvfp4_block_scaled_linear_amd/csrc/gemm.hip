@@ -21,9 +21,9 @@
 //  - Global loads run two K steps ahead in two register sets; they are raw buffer loads
 //    (out-of-range offsets read zeros), so no branch guards a load and the compiler
 //    waits only for the step it needs.
-//  - Workgroups are numbered so that each XCD (blockIdx % 8) owns a contiguous run of
-//    tiles that share activation rows (A-stationary), keeping the reused operand in its
-//    own L2.
+//  - Workgroups are numbered per XCD (blockIdx % 8) so that the operand an XCD reuses
+//    stays in its own L2: the 256-row tiles share activation rows (A-stationary); the
+//    smaller-M kernels take an eighth of the weight's columns per XCD (weight-stationary).
 // The fp32 accumulator is scaled once by the tensor scale(s) in the epilogue.
 #include <type_traits>
 
@@ -116,14 +116,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
     __syncthreads();
   } else {
-    // XCD-aware tile order: consecutive tiles of one XCD share the same M rows.
+    // XCD-aware tile order, weight-stationary: XCD x (blockIdx % 8) takes the column
+    // tiles [x * nbn / 8, (x + 1) * nbn / 8) for every row tile, so it fetches an eighth
+    // of the weight and all of the (here smaller) activation rows; otherwise consecutive
+    // tiles of one XCD share the same rows.
     const int64_t nbm = (M + BM - 1) / BM;
     const int64_t total = nbm * nbn;
     const int64_t bid = blockIdx.x;
-    int64_t lin = bid;
-    if (total % 8 == 0) lin = (bid % 8) * (total / 8) + bid / 8;
-    m0 = (lin / nbn) * BM;
-    n0 = (lin % nbn) * BN;
+    if (nbn % 8 == 0) {
+      const int64_t per = nbn / 8, j = bid / 8;
+      m0 = (j / per) * BM;
+      n0 = ((bid % 8) * per + j % per) * BN;
+    } else {
+      int64_t lin = bid;
+      if (total % 8 == 0) lin = (bid % 8) * (total / 8) + bid / 8;
+      m0 = (lin / nbn) * BM;
+      n0 = (lin % nbn) * BN;
+    }
     rows_m = (M - m0) < BM ? (M - m0) : BM;
   }
   const int64_t rows_n = (N - n0) < BN ? (N - n0) : BN;
