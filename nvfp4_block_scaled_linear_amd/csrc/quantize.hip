@@ -74,10 +74,21 @@ __global__ __launch_bounds__(256) void quantize_rows(const void* x, int64_t ldx,
   const int64_t base = row * ldx;
   bool finite = true;
   float m = 0.0f;
-  for (int64_t b = threadIdx.x; b < nb; b += blockDim.x) {
-    float v[16];
-    load16<IN>(x, base + 16 * b, v);
-    m = fmaxf(m, amax16(v, finite));
+  // rows of at most one block per thread (K <= 4096) keep their block in registers for
+  // the second pass instead of loading it again
+  const bool one = nb <= (int64_t)blockDim.x;  // uniform
+  float keep[16];
+  if (one) {
+    if ((int64_t)threadIdx.x < nb) {
+      load16<IN>(x, base + 16 * (int64_t)threadIdx.x, keep);
+      m = amax16(keep, finite);
+    }
+  } else {
+    for (int64_t b = threadIdx.x; b < nb; b += blockDim.x) {
+      float v[16];
+      load16<IN>(x, base + 16 * b, v);
+      m = fmaxf(m, amax16(v, finite));
+    }
   }
   m = wave_max(m);
   if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
@@ -91,10 +102,15 @@ __global__ __launch_bounds__(256) void quantize_rows(const void* x, int64_t ldx,
   }
   __syncthreads();
   const float t = ts_sh;
-  for (int64_t b = threadIdx.x; b < nb; b += blockDim.x) {
-    float v[16];
-    load16<IN>(x, base + 16 * b, v);
-    quantize_block(v, t, codes + row * (K >> 1) + 8 * b, scales + row * nb + b);
+  if (one) {
+    const int64_t b = threadIdx.x;
+    if (b < nb) quantize_block(keep, t, codes + row * (K >> 1) + 8 * b, scales + row * nb + b);
+  } else {
+    for (int64_t b = threadIdx.x; b < nb; b += blockDim.x) {
+      float v[16];
+      load16<IN>(x, base + 16 * b, v);
+      quantize_block(v, t, codes + row * (K >> 1) + 8 * b, scales + row * nb + b);
+    }
   }
   if (!finite && faults) atomicOr(faults, (uint32_t)NVFP4_FAULT_NONFINITE);
 }
