@@ -31,6 +31,17 @@
  *   - Data faults are reported asynchronously: when `faults` is non-NULL the kernels
  *     OR bits of NVFP4_FAULT_* into that device word. Outputs are undefined when a
  *     call returns a non-OK status or sets a fault bit.
+ *   - Check mode (flags & NVFP4_F_CHECK, nvfp4_linear and nvfp4_grouped_linear): before
+ *     the product, the call scans its operands' data and ORs into *faults
+ *       NVFP4_FAULT_NAN_SCALE  for an E4M3 scale byte that is NaN (0x7F or 0xFF) or a
+ *                              tensor scale that is NaN or infinite (weight or NVFP4
+ *                              activation operand; every expert of a grouped call);
+ *       NVFP4_FAULT_NONFINITE  for a NaN or infinite BF16 activation value;
+ *     (the pages' engine refuses NaN scale bytes and rows whose scaled values overflow,
+ *     issue #565 section 10, PRs #597 and #710). The scan is separate launches on the
+ *     same stream; without the flag nothing is scanned and the product kernels are the
+ *     same as with it. Check mode needs a non-NULL `faults` (NVFP4_ERR_NULL otherwise).
+ *     The product still runs: a NaN scale gives NaN in the outputs it touches.
  *   - The tensor scale is applied once, to the fp32 accumulator (the store scales by
  *     it, as the pages' prompt GEMM scales each slot by its expert's tensor scale:
  *     issue #565 section 4, PR #545).
@@ -70,7 +81,9 @@ enum { NVFP4_OUT_ROUTES = 0, NVFP4_OUT_SWIGLU_BF16 = 1, NVFP4_OUT_COMBINE = 2 };
 /* OR'ed into out_mode of a grouped call: reuse the route grouping already in the workspace */
 enum { NVFP4_OUT_REUSE_GROUPING = 0x100 };
 /* fault bits */
-enum { NVFP4_FAULT_NONFINITE = 1u, NVFP4_FAULT_BAD_ROUTE = 2u };
+enum { NVFP4_FAULT_NONFINITE = 1u, NVFP4_FAULT_BAD_ROUTE = 2u, NVFP4_FAULT_NAN_SCALE = 4u };
+/* call flags (nvfp4_linear, nvfp4_grouped_linear) */
+enum { NVFP4_F_CHECK = 1u };
 
 /* Human-readable name of a status code (static storage). */
 const char* nvfp4_status_string(int32_t status);
@@ -98,12 +111,16 @@ const char* nvfp4_status_string(int32_t status);
  * M <= 16 streams the weight once for all rows (each weight byte is read once for all
  *   M rows, as the pages' multi-row MTP verify does: issue #565 section 4, PRs #808
  *   and #707); larger M runs the tiled matrix-core GEMM.
+ * flags: 0 or NVFP4_F_CHECK (see "Check mode" above); faults: a device word or NULL
+ *   (NULL only without NVFP4_F_CHECK); with NVFP4_ACT_BF16_QUANTIZE a non-finite row
+ *   value is reported as NVFP4_FAULT_NONFINITE in check mode.
  * Errors: NVFP4_ERR_NULL, _SHAPE (also M > 4 or K > 8192 with NVFP4_ACT_BF16_QUANTIZE),
- *   _ALIGN, _ARG (unknown act_kind), _LAUNCH. */
+ *   _ALIGN, _ARG (unknown act_kind or flag bit), _LAUNCH. */
 nvfp4_status nvfp4_linear(int32_t act_kind, const void* x, const uint8_t* x_scales,
                           const float* x_ts, int64_t ldx, int64_t M, int64_t N, int64_t K,
                           const uint8_t* w_codes, const uint8_t* w_scales, const float* w_ts,
-                          float* y, int64_t ldy, void* stream);
+                          float* y, int64_t ldy, uint32_t flags, uint32_t* faults,
+                          void* stream);
 
 /* nvfp4_quantize_act — quantize rows to NVFP4 on the device, bit-exactly by the rule
  *     ts      = amax / 2688            (2688 = 6 * 448; amax over the row or the tensor)
@@ -137,8 +154,9 @@ nvfp4_status nvfp4_quantize_act(int32_t in_type, const void* x, int64_t ldx, int
  *
  * rows_mode NVFP4_ROWS_PER_TOKEN: x has T rows and route r reads row t;
  *           NVFP4_ROWS_PER_ROUTE: x has T*top_k rows and route r reads row r.
- * x: act_kind/x/x_scales/x_ts/ldx exactly as in nvfp4_linear (NVFP4 rows hold one
- *    ts per x row).
+ * x: act_kind/x/x_scales/x_ts/ldx as in nvfp4_linear (NVFP4 rows hold one ts per x
+ *    row), with act_kind NVFP4_ACT_BF16 or NVFP4_ACT_NVFP4 only: the in-call
+ *    quantization NVFP4_ACT_BF16_QUANTIZE is refused here (NVFP4_ERR_ARG).
  * out_mode NVFP4_OUT_ROUTES: y is fp32 [T*top_k][N], row r = x_row(r) w_e^T * ts_e.
  *          NVFP4_OUT_SWIGLU_BF16: N even; y is BF16 bits [T*top_k][N/2], row r =
  *            bf16_rne(silu(g) * u) with g = h[0:N/2], u = h[N/2:N] of the route's fp32
@@ -164,10 +182,11 @@ nvfp4_status nvfp4_quantize_act(int32_t in_type, const void* x, int64_t ldx, int
  *   prompt-sized ones (routes averaging >= 32 per active expert) run MFMA tiles of one
  *   expert's routes (the pages' expert-grouped prompt GEMM, each expert read once per
  *   batch: issue #565 section 4, PR #740).
- * workspace: device scratch (route grouping; the fp32 per-route rows for
- *   NVFP4_OUT_COMBINE, and for NVFP4_OUT_SWIGLU_BF16 on prompt-sized batches); pass
- *   workspace = NULL to receive the needed size in
+ * workspace: device scratch (the route grouping, and the fp32 per-route rows for
+ *   NVFP4_OUT_COMBINE); pass workspace = NULL to receive the needed size in
  *   *workspace_bytes (nothing is enqueued); otherwise *workspace_bytes is its size.
+ *   Its contents need no initialisation: every byte the call reads it writes first.
+ * flags: 0 or NVFP4_F_CHECK (see "Check mode" above; scans every expert's scales).
  * Sizes: one expert's codes (N * K/2 bytes) must fit 32-bit offsets.
  * Expert ids out of range or repeated within a token set NVFP4_FAULT_BAD_ROUTE; such
  *   routes are dropped (their rows are zero; they add nothing to a combine).
@@ -179,7 +198,8 @@ nvfp4_status nvfp4_grouped_linear(int32_t act_kind, const void* x, const uint8_t
                                   const uint8_t* w_scales, const float* w_ts,
                                   const int32_t* topk_ids, const float* topk_w,
                                   int32_t out_mode, void* y, void* workspace,
-                                  size_t* workspace_bytes, uint32_t* faults, void* stream);
+                                  size_t* workspace_bytes, uint32_t flags, uint32_t* faults,
+                                  void* stream);
 
 /* nvfp4_read_probe — measurement support, not part of the layer: one plain streaming read
  * of `bytes` bytes at `buf` in one launch, the measured single-launch read roof that the

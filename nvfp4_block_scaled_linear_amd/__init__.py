@@ -8,7 +8,9 @@ from ._binding import (  # noqa: F401
     ACT_BF16_QUANTIZE,
     ACT_NVFP4,
     EXPORTS,
+    F_CHECK,
     FAULT_BAD_ROUTE,
+    FAULT_NAN_SCALE,
     FAULT_NONFINITE,
     LIB_PATH,
     NVFP4Error,

@@ -18,7 +18,8 @@ TS_PER_ROW, TS_PER_TENSOR = 0, 1
 ROWS_PER_TOKEN, ROWS_PER_ROUTE = 0, 1
 OUT_ROUTES, OUT_SWIGLU_BF16, OUT_COMBINE = 0, 1, 2
 OUT_REUSE_GROUPING = 0x100
-FAULT_NONFINITE, FAULT_BAD_ROUTE = 1, 2
+FAULT_NONFINITE, FAULT_BAD_ROUTE, FAULT_NAN_SCALE = 1, 2, 4
+F_CHECK = 1
 
 EXPORTS = ("nvfp4_status_string", "nvfp4_linear", "nvfp4_quantize_act", "nvfp4_grouped_linear",
            "nvfp4_read_probe")
@@ -45,13 +46,15 @@ def load_library(path: str = LIB_PATH):
     lib.nvfp4_status_string.restype = ctypes.c_char_p
     lib.nvfp4_status_string.argtypes = [i32]
     lib.nvfp4_linear.restype = i32
-    lib.nvfp4_linear.argtypes = [i32, vp, vp, vp, i64, i64, i64, i64, vp, vp, vp, vp, i64, vp]
+    u32 = ctypes.c_uint32
+    lib.nvfp4_linear.argtypes = [i32, vp, vp, vp, i64, i64, i64, i64, vp, vp, vp, vp, i64, u32,
+                                 u32p, vp]
     lib.nvfp4_quantize_act.restype = i32
     lib.nvfp4_quantize_act.argtypes = [i32, vp, i64, i64, i64, i32, vp, vp, vp, u32p, vp]
     lib.nvfp4_grouped_linear.restype = i32
     lib.nvfp4_grouped_linear.argtypes = [i32, vp, vp, vp, i64, i32, i64, i32, i64, i64, i32, vp,
                                          vp, vp, vp, vp, i32, vp, vp,
-                                         ctypes.POINTER(ctypes.c_size_t), u32p, vp]
+                                         ctypes.POINTER(ctypes.c_size_t), u32, u32p, vp]
     lib.nvfp4_read_probe.restype = i32
     lib.nvfp4_read_probe.argtypes = [vp, i64, i32, u32p, vp]
     _lib = lib
@@ -90,10 +93,12 @@ def _check(status: int, what: str):
 
 
 def linear(x, w_codes, w_scales, w_ts, *, x_scales=None, x_ts=None, out=None,
-           quantize_x=False):
+           quantize_x=False, check=False, faults=None):
     """y = x W^T for an NVFP4 weight (codes [N][K/2] u8, scales [N][K/16] u8, ts [1] f32).
     x is BF16 [M][K] (W4A16), or NVFP4 codes [M][K/2] u8 with x_scales/x_ts (W4A4).
-    quantize_x=True (BF16 x, M <= 4): W4A4 with x quantized per row inside the call."""
+    quantize_x=True (BF16 x, M <= 4): W4A4 with x quantized per row inside the call.
+    check=True scans the operands first and ORs FAULT_* bits into `faults` (a device
+    int32 word, required then)."""
     N = w_codes.shape[0]
     K = 2 * w_codes.shape[1]
     if x_scales is None:
@@ -104,7 +109,7 @@ def linear(x, w_codes, w_scales, w_ts, *, x_scales=None, x_ts=None, out=None,
         out = torch.empty((M, N), dtype=torch.float32, device=w_codes.device)
     st = load_library().nvfp4_linear(act, _p(x), _p(x_scales), _p(x_ts), ldx, M, N, K,
                                      _p(w_codes), _p(w_scales), _p(w_ts), _p(out),
-                                     _ld(out), _stream())
+                                     _ld(out), F_CHECK if check else 0, _p(faults), _stream())
     _check(st, "nvfp4_linear")
     return out
 
@@ -129,19 +134,20 @@ def grouped_workspace_size(T: int, top_k: int, N: int, K: int, num_experts: int,
     n = ctypes.c_size_t(0)
     st = load_library().nvfp4_grouped_linear(ACT_BF16, None, None, None, K, ROWS_PER_TOKEN, T,
                                              top_k, N, K, num_experts, None, None, None, None,
-                                             None, out_mode, None, None, ctypes.byref(n), None,
-                                             None)
+                                             None, out_mode, None, None, ctypes.byref(n), 0,
+                                             None, None)
     _check(st, "nvfp4_grouped_linear (workspace query)")
     return n.value
 
 
 def grouped_linear(x, w_codes, w_scales, w_ts, topk_ids, *, topk_w=None, out_mode=OUT_ROUTES,
                    rows_per_route=False, x_scales=None, x_ts=None, out=None, workspace=None,
-                   faults=None, reuse_grouping=False):
+                   faults=None, reuse_grouping=False, check=False):
     """Expert-grouped NVFP4 linear. w_codes [E][N][K/2], w_scales [E][N][K/16], w_ts [E];
     topk_ids [T][top_k] int32. See include/nvfp4.h for the output forms. reuse_grouping
     (OUT_COMBINE with the workspace of the layer's earlier call on the same topk_ids)
-    skips the route grouping."""
+    skips the route grouping. check=True scans every expert's scales and the activations
+    first (see linear)."""
     if reuse_grouping and workspace is None:
         raise ValueError("reuse_grouping needs the workspace that holds the grouping")
     E, N, half = w_codes.shape
@@ -166,7 +172,8 @@ def grouped_linear(x, w_codes, w_scales, w_ts, topk_ids, *, topk_w=None, out_mod
         act, _p(x), _p(x_scales), _p(x_ts), ldx, ROWS_PER_ROUTE if rows_per_route else ROWS_PER_TOKEN,
         T, top_k, N, K, E, _p(w_codes), _p(w_scales), _p(w_ts), _p(topk_ids), _p(topk_w),
         out_mode | (OUT_REUSE_GROUPING if reuse_grouping else 0),
-        _p(out), _p(workspace), ctypes.byref(nbytes), _p(faults), _stream())
+        _p(out), _p(workspace), ctypes.byref(nbytes), F_CHECK if check else 0, _p(faults),
+        _stream())
     _check(st, "nvfp4_grouped_linear")
     return out
 

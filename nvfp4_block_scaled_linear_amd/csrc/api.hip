@@ -40,6 +40,21 @@ nvfp4_status check_act(int32_t act_kind, const void* x, const uint8_t* x_scales,
   return NVFP4_OK;
 }
 
+nvfp4_status check_flags(uint32_t flags, const uint32_t* faults) {
+  if (flags & ~(uint32_t)NVFP4_F_CHECK) return NVFP4_ERR_ARG;
+  if ((flags & NVFP4_F_CHECK) && !faults) return NVFP4_ERR_NULL;
+  if (faults && !aligned(faults, 4)) return NVFP4_ERR_ALIGN;
+  return NVFP4_OK;
+}
+
+// check mode: the activation operand's data (rows x rows of K values)
+hipError_t check_act_data(int32_t act_kind, const void* x, const uint8_t* x_scales,
+                          const float* x_ts, int64_t ldx, int64_t rows, int64_t K,
+                          uint32_t* faults, hipStream_t s) {
+  if (act_kind == NVFP4_ACT_NVFP4) return launch_check_scales(x_scales, rows * (K / 16), x_ts, rows, faults, s);
+  return launch_check_bf16(x, ldx, rows, K, faults, s);
+}
+
 nvfp4_status check_weight(const uint8_t* w_codes, const uint8_t* w_scales, const float* w_ts) {
   if (!w_codes || !w_scales || !w_ts) return NVFP4_ERR_NULL;
   if (!aligned(w_codes, 16) || !aligned(w_scales, 2) || !aligned(w_ts, 4)) return NVFP4_ERR_ALIGN;
@@ -110,8 +125,10 @@ const char* nvfp4_status_string(int32_t status) {
 nvfp4_status nvfp4_linear(int32_t act_kind, const void* x, const uint8_t* x_scales,
                           const float* x_ts, int64_t ldx, int64_t M, int64_t N, int64_t K,
                           const uint8_t* w_codes, const uint8_t* w_scales, const float* w_ts,
-                          float* y, int64_t ldy, void* stream) {
+                          float* y, int64_t ldy, uint32_t flags, uint32_t* faults,
+                          void* stream) {
   nvfp4_status st;
+  if ((st = check_flags(flags, faults)) != NVFP4_OK) return st;
   if ((st = check_k(K)) != NVFP4_OK) return st;
   if (M <= 0 || N <= 0 || M > kMaxDim || N > kMaxDim) return NVFP4_ERR_SHAPE;
   if ((st = check_act(act_kind, x, x_scales, x_ts, ldx, K)) != NVFP4_OK) return st;
@@ -126,6 +143,12 @@ nvfp4_status nvfp4_linear(int32_t act_kind, const void* x, const uint8_t* x_scal
       (M <= kStreamMaxRows ? M * ldx * 2 > kMaxBufferBytes : ldx > gemm_max_ldx()))
     return NVFP4_ERR_SHAPE;
   if (act_kind == NVFP4_ACT_NVFP4 && M * (K / 2) > kMaxBufferBytes) return NVFP4_ERR_SHAPE;
+  if (flags & NVFP4_F_CHECK) {
+    hipError_t e = launch_check_scales(w_scales, N * (K / 16), w_ts, 1, faults, s);
+    if (e == hipSuccess)
+      e = check_act_data(act_kind, x, x_scales, x_ts, ldx, M, K, faults, s);
+    if (e != hipSuccess) return NVFP4_ERR_LAUNCH;
+  }
   if (M <= kStreamMaxRows) {
     StreamArgs a{};
     a.x = x; a.x_scales = x_scales; a.x_ts = x_ts; a.ldx = ldx;
@@ -167,9 +190,13 @@ nvfp4_status nvfp4_grouped_linear(int32_t act_kind, const void* x, const uint8_t
                                   const uint8_t* w_scales, const float* w_ts,
                                   const int32_t* topk_ids, const float* topk_w,
                                   int32_t out_mode, void* y, void* workspace,
-                                  size_t* workspace_bytes, uint32_t* faults, void* stream) {
+                                  size_t* workspace_bytes, uint32_t flags, uint32_t* faults,
+                                  void* stream) {
   nvfp4_status st;
   if (!workspace_bytes) return NVFP4_ERR_NULL;
+  if ((st = check_flags(flags, faults)) != NVFP4_OK) return st;
+  // the in-call quantization is a dense decode-batch form only
+  if (act_kind == NVFP4_ACT_BF16_QUANTIZE) return NVFP4_ERR_ARG;
   // the grouping left in the workspace by the layer's earlier call (combine only)
   const bool reuse = (out_mode & NVFP4_OUT_REUSE_GROUPING) != 0;
   out_mode &= ~(int32_t)NVFP4_OUT_REUSE_GROUPING;
@@ -201,11 +228,17 @@ nvfp4_status nvfp4_grouped_linear(int32_t act_kind, const void* x, const uint8_t
   }
   if (!topk_ids || !y) return NVFP4_ERR_NULL;
   if (out_mode == NVFP4_OUT_COMBINE && !topk_w) return NVFP4_ERR_NULL;
-  if (!aligned(topk_ids, 4) || (topk_w && !aligned(topk_w, 4)) || !aligned(y, 4) ||
-      (faults && !aligned(faults, 4)))
+  if (!aligned(topk_ids, 4) || (topk_w && !aligned(topk_w, 4)) || !aligned(y, 4))
     return NVFP4_ERR_ALIGN;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (flags & NVFP4_F_CHECK) {
+    const int64_t xrows = rows_mode == NVFP4_ROWS_PER_TOKEN ? T : T * top_k;
+    hipError_t e = launch_check_scales(w_scales, (int64_t)num_experts * N * (K / 16), w_ts,
+                                       num_experts, faults, s);
+    if (e == hipSuccess) e = check_act_data(act_kind, x, x_scales, x_ts, ldx, xrows, K, faults, s);
+    if (e != hipSuccess) return NVFP4_ERR_LAUNCH;
+  }
   char* base = static_cast<char*>(workspace);
   RouteWorkspace ws;
   ws.offsets = reinterpret_cast<int32_t*>(base + L.offsets);

@@ -273,12 +273,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
     decode(rb_next, Bd_next);
     // interleave: each MFMA followed by a share of the decode's VALU work, with the LDS
-    // operand reads spread between them
+    // operand reads spread between them (NVFP4 activations: a smaller share per MFMA,
+    // which keeps the 128-row grouped form within its 256 registers, no scratch)
+    constexpr int kValuShare = ACT == 0 ? 160 / (8 * MT) + 1 : 4;
 #pragma unroll
     for (int i = 0; i < 8 * MT; i++) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);           // one MFMA
       if (i % 2 == 0) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-      __builtin_amdgcn_sched_group_barrier(0x002, 160 / (8 * MT) + 1, 0);  // VALU
+      __builtin_amdgcn_sched_group_barrier(0x002, kValuShare, 0);  // VALU
     }
     write_a(ra_next, (kt + 1) & 1);
     __syncthreads();
@@ -851,8 +853,11 @@ int gemm_grouped_tile_rows() { return 32 * kGroupedMT; }
 
 hipError_t launch_gemm_grouped(const GemmArgs& a, int act_kind, int64_t max_tiles,
                                hipStream_t stream) {
-  return act_kind == 0 ? launch_grouped_mt<0>(a, max_tiles, stream)
-                       : launch_grouped_mt<1>(a, max_tiles, stream);
+  switch (act_kind) {
+    case 0: return launch_grouped_mt<0>(a, max_tiles, stream);
+    case 1: return launch_grouped_mt<1>(a, max_tiles, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 // Largest activation row pitch (elements) the GEMM's 32-bit buffer offsets can address
@@ -860,16 +865,21 @@ hipError_t launch_gemm_grouped(const GemmArgs& a, int act_kind, int64_t max_tile
 int64_t gemm_max_ldx() { return ((int64_t)1 << 31) / (2 * 256) - 1; }
 
 // K split four ways when the 64 x 256 tiles would not give every CU a workgroup, the K
-// quarters stay at least four steps long and K is whole rounds of four 64-k steps
-bool use_splitk(int64_t M, int64_t N, int64_t K) {
-  return ((M + 63) / 64) * ((N + BN - 1) / BN) < 256 && K >= 4 * kSkSplit * BK &&
-         K % (4 * BK) == 0;
+// quarters stay at least four steps long and K is whole rounds of four 64-k steps. Its
+// scales come as 16-byte pieces (four steps of one column or row), so the scale bases
+// must be 16-byte aligned (the ABI guarantees 2); otherwise the 64-row kernel runs.
+bool use_splitk(const GemmArgs& a, int act_kind) {
+  const bool aligned16 = (uintptr_t)a.w_scales % 16 == 0 &&
+                         (act_kind == 0 || (uintptr_t)a.x_scales % 16 == 0);
+  return aligned16 && ((a.M + 63) / 64) * ((a.N + BN - 1) / BN) < 256 &&
+         a.K >= 4 * kSkSplit * BK && a.K % (4 * BK) == 0;
 }
 
 hipError_t launch_gemm(const GemmArgs& a, int act_kind, hipStream_t stream) {
+  if (act_kind != 0 && act_kind != 1) return hipErrorInvalidValue;
   if (use_wide(a.M, a.N))
     return act_kind == 0 ? launch_wide<0>(a, stream) : launch_wide<1>(a, stream);
-  if (use_splitk(a.M, a.N, a.K))
+  if (use_splitk(a, act_kind))
     return act_kind == 0 ? launch_splitk<0>(a, stream) : launch_splitk<1>(a, stream);
   return act_kind == 0 ? launch_mt<2, 0>(a, stream) : launch_mt<2, 1>(a, stream);
 }

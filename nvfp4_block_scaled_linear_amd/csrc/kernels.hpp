@@ -110,6 +110,14 @@ hipError_t launch_combine(const float* rows, const int32_t* route_expert,
                           const float* topk_w, const float* w_ts, int64_t T, int top_k,
                           int64_t N, float* y, hipStream_t stream);
 
+// check mode: E4M3 NaN scale bytes [0, bytes) and non-finite tensor scales [0, n_ts) set
+// NVFP4_FAULT_NAN_SCALE; non-finite BF16 values of rows [rows][ld] (K each) set
+// NVFP4_FAULT_NONFINITE
+hipError_t launch_check_scales(const uint8_t* scales, int64_t bytes, const float* ts,
+                               int64_t n_ts, uint32_t* faults, hipStream_t stream);
+hipError_t launch_check_bf16(const void* x, int64_t ld, int64_t rows, int64_t K,
+                             uint32_t* faults, hipStream_t stream);
+
 // measurement support: one streaming read of `bytes` bytes (loads_per_thread 16-byte loads
 // per thread, 1/2/4/8/16)
 hipError_t launch_read_probe(const void* buf, int64_t bytes, int loads_per_thread, uint32_t* sink,

@@ -790,6 +790,9 @@ int pick_tn(int64_t N) {
 hipError_t launch_stream_cfg(const StreamArgs& a, int act_kind, bool grouped, int max_active,
                              int tn, int W, hipStream_t stream) {
   if (W < 1 || W > 4) return hipErrorInvalidValue;
+  // activation kinds: 0 BF16, 1 NVFP4 (both forms), 2 BF16 quantized in the call (dense
+  // only); anything else is refused rather than taken by one of the templates
+  if (act_kind != 0 && act_kind != 1 && !(act_kind == 2 && !grouped)) return hipErrorInvalidValue;
   if (grouped && a.a_out) {
     const bool slds = use_lds_scales(a, 2);
     const int R = a.M > 0 ? (a.M + 3) / 4 : 1;

@@ -42,12 +42,12 @@ def _bind(lib):
         "oracle_bf16_value": (f64, [ctypes.c_uint16]),
         "oracle_bf16_round": (ctypes.c_uint16, [f64]),
         "oracle_quantize": (i32, [vp, i64, i64, i32, vp, vp, vp]),
-        "oracle_quantize_bf16": (i32, [vp, i64, i64, i32, vp, vp, vp, vp]),
         "oracle_dequant": (None, [vp, vp, vp, i32, i64, i64, vp]),
         "oracle_linear": (None, [vp, i64, vp, i64, i64, vp, vp]),
         "oracle_num_threads": (i32, []),
         "oracle_e2m1_encode_batch": (None, [vp, i64, vp]),
         "oracle_e4m3_encode_batch": (None, [vp, i64, vp]),
+        "oracle_bf16_round_batch": (None, [vp, i64, vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -99,6 +99,13 @@ class Oracle:
 
     def bf16_value(self, bits: int) -> float:
         return self.lib.oracle_bf16_value(int(bits))
+
+    def bf16_round_array(self, v) -> np.ndarray:
+        """bf16_round of every element of a float64 array (same shape, uint16 bits)."""
+        v = np.ascontiguousarray(v, dtype=np.float64)
+        out = np.empty(v.shape, dtype=np.uint16)
+        self.lib.oracle_bf16_round_batch(v.ctypes.data, v.size, out.ctypes.data)
+        return out
 
     # -- quantizer -----------------------------------------------------------------
     def quantize(self, w, per_row: bool):
@@ -198,9 +205,14 @@ class Oracle:
         weight (Rocket log entry "The expert split decodes the same tokens; ...",
         section "Why rows and not partial sums"). float64 here; bound per token is
         sum |r| * sum_k |a_k w_k ts_e|."""
+        return self.moe_combine_rows(self.bf16_to_f64(a_bits), ids, rw, d_codes, d_scales, d_ts)
+
+    def moe_combine_rows(self, a, ids, rw, d_codes, d_scales, d_ts):
+        """The same ordered combine on float64 route rows a [T*k][K] (route t*k + j): for
+        route rows that are not BF16, e.g. NVFP4 rows decoded exactly by ``dequant``."""
         T, k = ids.shape
         N = d_codes.shape[1]
-        a = self.bf16_to_f64(a_bits)
+        a = np.asarray(a, dtype=np.float64)
         y = np.zeros((T, N))
         b = np.zeros((T, N))
         cache = {}

@@ -176,13 +176,6 @@ int oracle_quantize(const float* w, int64_t rows, int64_t K, int per_row,
   return 0;
 }
 
-/* Same rule on BF16 input bits (each converted exactly to fp32 first). */
-int oracle_quantize_bf16(const uint16_t* x, int64_t rows, int64_t K, int per_row,
-                         uint8_t* codes, uint8_t* scales, float* ts, float* scratch_f32) {
-  for (int64_t i = 0; i < rows * K; i++) scratch_f32[i] = (float)oracle_bf16_value(x[i]);
-  return oracle_quantize(scratch_f32, rows, K, per_row, codes, scales, ts);
-}
-
 /* ---- Dequantization and the linear layer -------------------------------------------- */
 
 /* out[r][k] = e2m1(code) * e4m3(scale of block k/16) * ts, in float64 (exact: at most
@@ -228,7 +221,13 @@ int oracle_num_threads(void) {
 #endif
 }
 
-/* Batch forms of the two encoders (used by the exhaustive checks of the tests). */
+/* Batch forms of the two encoders (used by the exhaustive checks of the tests) and of
+ * the BF16 rounding (whole SwiGLU outputs of a prompt-sized MoE layer). */
+void oracle_bf16_round_batch(const double* v, int64_t n, uint16_t* out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; i++) out[i] = oracle_bf16_round(v[i]);
+}
+
 void oracle_e2m1_encode_batch(const float* q, int64_t n, int8_t* out) {
 #pragma omp parallel for schedule(static)
   for (int64_t i = 0; i < n; i++) out[i] = (int8_t)oracle_e2m1_encode(q[i]);

@@ -361,9 +361,97 @@ def pin_bf16_round(o):
     assert o.bf16_round(1.0 + 2.0 ** -8 + 2.0 ** -40) == 0x3F81
 
 
+# silu(g) = g / (1 + e^-g) at fixed points, to 19+ significant digits (the logistic
+# function's closed form evaluated in 40-digit decimal arithmetic, not by the oracle)
+SILU_FIXED = {
+    1.0: 0.7310585786300048792511592418218362743650,
+    -1.0: -0.2689414213699951207488407581781637256349,
+    0.5: 0.3112296656009272823194502828727542393766,
+    -4.0: -0.07194483984836623210717255179815369948994,
+    30.0: 29.99999999999719271310934821031384813121,
+    -30.0: -2.807286890651789686151868795985495233474e-12,
+}
+
+
+def pin_swiglu(o):
+    """SwiGLU a = silu(g) * u with g the first half of a gate_up row and u the second:
+    fixed silu values; the identity silu(g) - silu(-g) = g (the logistic function's
+    sigma(g) + sigma(-g) = 1); an all-zero up half or gate half gives zeros; the halves
+    are not swapped."""
+    gs = np.array(list(SILU_FIXED), np.float64)
+    h = np.concatenate([gs, np.ones_like(gs)])[None, :]
+    a = o.swiglu(h)[0]
+    for g, got in zip(gs, a):
+        want = SILU_FIXED[float(g)]
+        assert abs(got - want) <= 4e-16 * abs(want), (g, got, want)
+    # up half scales the result, gate half goes through silu
+    u = np.array([2.0, -3.0, 0.25, 8.0, 1.0, -1.0])
+    a2 = o.swiglu(np.concatenate([gs, u])[None, :])[0]
+    for g, uu, got in zip(gs, u, a2):
+        want = SILU_FIXED[float(g)] * uu
+        assert abs(got - want) <= 4e-16 * abs(want), (g, uu, got, want)
+    # silu(g) - silu(-g) = g
+    g = np.linspace(-12.0, 12.0, 97)
+    ap = o.swiglu(np.concatenate([g, np.ones_like(g)])[None, :])[0]
+    am = o.swiglu(np.concatenate([-g, np.ones_like(g)])[None, :])[0]
+    assert np.all(np.abs((ap - am) - g) <= 1e-14 * np.maximum(1.0, np.abs(g)))
+    # hand-built gate_up rows: zero up half, zero gate half
+    rng = np.random.default_rng(41)
+    gate = rng.normal(0, 3, 64)
+    z = o.swiglu(np.concatenate([gate, np.zeros(64)])[None, :])[0]
+    assert np.all(z == 0.0)
+    z = o.swiglu(np.concatenate([np.zeros(64), rng.normal(0, 3, 64)])[None, :])[0]
+    assert np.all(z == 0.0)
+    # large |g|: silu(g) -> g above, -> 0 below
+    a3 = o.swiglu(np.array([[60.0, -60.0, 1.0, 1.0]]))[0]
+    assert a3[0] == 60.0 and -1e-24 < a3[1] < 0.0
+
+
+def pin_bf16_round_array(o):
+    """The batch BF16 rounding equals the scalar one (itself pinned against PyTorch and on
+    hand-made midpoints by pin_bf16_round) element for element, over normal, tiny, huge,
+    signed-zero and exact-midpoint values."""
+    rng = np.random.default_rng(43)
+    v = np.concatenate([rng.normal(0, 1, 3000), rng.normal(0, 1e-36, 300),
+                        rng.normal(0, 1e30, 300), [0.0, -0.0, 1.0 + 2.0 ** -8,
+                                                   1.0 + 3 * 2.0 ** -8, -(1.0 + 2.0 ** -8)]])
+    got = o.bf16_round_array(v.reshape(-1, 1)).ravel()
+    want = np.array([o.bf16_round(float(x)) for x in v], np.uint16)
+    assert np.array_equal(got, want)
+    assert got[-4] == 0x8000 and got[-3] == 0x3F80 and got[-2] == 0x3F82 and got[-1] == 0xBF80
+
+
+def pin_moe_combine_rows(o, seed=47):
+    """The ordered combine over float64 route rows (the form used for NVFP4 route rows)
+    equals, per token, the router-weighted sum of the W4A4 linear of each route's NVFP4
+    row with its expert, and reduces to moe_down_combine on BF16 rows."""
+    E, T, k, K, N = 3, 4, 2, 32, 24
+    qs = [o.quantize(weight_f32(seed, N, K, stream=300 + e), per_row=False) for e in range(E)]
+    dc = np.stack([q[0] for q in qs]); ds = np.stack([q[1] for q in qs])
+    dt = np.concatenate([q[2] for q in qs])
+    ids = np.array([[2, 0], [1, 2], [0, 1], [2, 1]], np.int32)
+    rw = np.array([[0.5, 0.25], [1.0, -0.5], [0.125, 2.0], [0.75, 0.75]], F32)
+    xb = act_bf16(seed, T * k, K)
+    xc, xs, xt = o.quantize_bf16(xb, per_row=True)
+    a = o.dequant(xc, xs, xt, per_row=True)
+    y, b = o.moe_combine_rows(a, ids, rw, dc, ds, dt)
+    for t in range(T):
+        ref = np.zeros(N)
+        for j in range(k):
+            e = ids[t, j]
+            r = t * k + j
+            yr, _ = o.linear_w4a4(xc[r:r + 1], xs[r:r + 1], xt[r:r + 1], dc[e], ds[e], dt[e:e + 1])
+            ref += float(rw[t, j]) * yr[0]
+        assert np.all(np.abs(y[t] - ref) <= 1e-13 * b[t]), t
+    yb, _ = o.moe_down_combine(xb, ids, rw, dc, ds, dt)
+    yc, _ = o.moe_combine_rows(o.bf16_to_f64(xb), ids, rw, dc, ds, dt)
+    assert np.array_equal(yb, yc)
+
+
 ALL_PINS = [pin_worked_example, pin_quantizer_bruteforce, pin_quantizer_properties,
             pin_quantizer_refuses_nonfinite, pin_dequant_exact, pin_linear_bruteforce,
-            pin_linear_invariants, pin_w4a4, pin_moe, pin_bf16_round]
+            pin_linear_invariants, pin_w4a4, pin_moe, pin_bf16_round, pin_swiglu,
+            pin_bf16_round_array, pin_moe_combine_rows]
 
 
 def pin_codec_quick(o):

@@ -54,8 +54,9 @@ def test_status_strings(lib):
 
 
 def lin(lib, act=0, x=P, xs=None, xt=None, ldx=4096, M=4, N=128, K=4096, wc=P, ws=P, wt=P,
-        y=P, ldy=128):
-    return lib.nvfp4_linear(act, x, xs, xt, ldx, M, N, K, wc, ws, wt, y, ldy, None)
+        y=P, ldy=128, flags=0, faults=None):
+    return lib.nvfp4_linear(act, x, xs, xt, ldx, M, N, K, wc, ws, wt, y, ldy, flags, faults,
+                            None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -71,6 +72,9 @@ def lin(lib, act=0, x=P, xs=None, xt=None, ldx=4096, M=4, N=128, K=4096, wc=P, w
     (dict(act=2, M=5), ERR_SHAPE), (dict(act=2, K=8224, ldx=8224), ERR_SHAPE),
     (dict(act=2, xs=P), ERR_ARG), (dict(act=2, xt=P), ERR_ARG), (dict(act=2, ldx=4100), ERR_ALIGN),
     (dict(act=3), ERR_ARG),
+    # check mode: a known flag bit only, and a fault word to report into
+    (dict(flags=2), ERR_ARG), (dict(flags=1), ERR_NULL), (dict(flags=1, faults=P + 2), ERR_ALIGN),
+    (dict(faults=P + 1), ERR_ALIGN), (dict(flags=0x80000001, faults=P), ERR_ARG),
 ])
 def test_linear_refusals(lib, kw, status):
     assert lin(lib, **kw) == status
@@ -91,12 +95,14 @@ def test_quantize_refusals(lib, kw, status):
     assert quant(lib, **kw) == status
 
 
-def grouped(lib, x=P, ldx=2048, rows_mode=0, T=16, k=8, N=1536, K=2048, E=128, wc=P, ws=P, wt=P,
-            ids=P, tw=P, out_mode=0, y=P, work=P, nbytes=1 << 30, faults=None, pass_nbytes=True):
+def grouped(lib, act=0, x=P, xs=None, xt=None, ldx=2048, rows_mode=0, T=16, k=8, N=1536,
+            K=2048, E=128, wc=P, ws=P, wt=P, ids=P, tw=P, out_mode=0, y=P, work=P,
+            nbytes=1 << 30, flags=0, faults=None, pass_nbytes=True):
     n = ctypes.c_size_t(nbytes)
-    return lib.nvfp4_grouped_linear(0, x, None, None, ldx, rows_mode, T, k, N, K, E, wc, ws, wt,
+    return lib.nvfp4_grouped_linear(act, x, xs, xt, ldx, rows_mode, T, k, N, K, E, wc, ws, wt,
                                     ids, tw, out_mode, y, work,
-                                    ctypes.byref(n) if pass_nbytes else None, faults, None), n.value
+                                    ctypes.byref(n) if pass_nbytes else None, flags, faults,
+                                    None), n.value
 
 
 def test_grouped_workspace_query(lib):
@@ -125,6 +131,13 @@ def test_grouped_workspace_query(lib):
     (dict(work=P + 16), ERR_ALIGN), (dict(x=None), ERR_NULL), (dict(ids=None), ERR_NULL),
     (dict(y=None), ERR_NULL), (dict(out_mode=2, tw=None), ERR_NULL), (dict(ids=P + 2), ERR_ALIGN),
     (dict(wc=P + 8), ERR_ALIGN),
+    # the in-call quantization is a dense-call form: refused here, also with every output
+    # form and for the workspace query
+    (dict(act=2), ERR_ARG), (dict(act=2, out_mode=1), ERR_ARG), (dict(act=2, out_mode=2), ERR_ARG),
+    (dict(act=2, work=None, nbytes=0), ERR_ARG), (dict(act=3), ERR_ARG),
+    (dict(act=1, xs=None, xt=P), ERR_NULL), (dict(act=1, xs=P, xt=None), ERR_NULL),
+    (dict(act=0, xs=P), ERR_ARG),
+    (dict(flags=2), ERR_ARG), (dict(flags=1), ERR_NULL), (dict(faults=P + 2), ERR_ALIGN),
 ])
 def test_grouped_refusals(lib, kw, status):
     assert grouped(lib, **kw)[0] == status
@@ -148,3 +161,4 @@ def test_binding_fails_loudly_without_library(tmp_path):
             _binding.load_library(str(tmp_path / "absent.so"))
     finally:
         _binding._lib = saved
+

@@ -398,3 +398,133 @@ def test_grouped_reuse_grouping_prefill(dev, o):
     dc, dsc, dts, _, _, _ = _small_experts(o, dev, E, 96, N // 2, 122)
     _reuse_check(dev, to_dev_bf16(xb, dev), (wc, wsc, wts), (dc, dsc, dts),
                  torch.from_numpy(ids).to(dev), torch.from_numpy(rw).to(dev), "prefill")
+
+
+# ---- the grouped GEMM beyond one column block, at the layer's real shape, and with NVFP4
+# activations -----------------------------------------------------------------------------
+
+def _swiglu_bits_check(o, a, h, label):
+    """GPU SwiGLU BF16 rows against the BF16 rounding of the float64 SwiGLU of the GPU's
+    own fp32 rows (same call shape): within one BF16 ulp everywhere, bit-exact nearly
+    everywhere (an fp32 product can straddle a BF16 rounding point)."""
+    a_bits = a.view(torch.int16).cpu().numpy().view(np.uint16)
+    ref_bits = o.bf16_round_array(o.swiglu(np.asarray(h, np.float64)))
+    diff = np.abs(a_bits.astype(np.int32) - ref_bits.astype(np.int32))
+    assert np.all(diff <= 1), (label, np.argwhere(diff > 1)[:5].tolist())
+    exact = float(np.mean(diff == 0))
+    assert exact >= 0.999, (label, exact)
+    _say(f"{label}: SwiGLU BF16 bit-exact fraction {exact:.6f}")
+
+
+def test_grouped_prefill_gemm_several_column_blocks(dev, o):
+    """Prompt-sized routes (128 per expert) with N = 800: four 256-column blocks per tile
+    for the per-route rows (the last ragged) and four 128-column gate/up blocks for SwiGLU
+    (half = 400, the last ragged); every output of every route against the oracle, the
+    SwiGLU rows from them, the ordered combine."""
+    E, N, K, T, k = 8, 800, 256, 512, 2
+    _say(f"grouped GEMM, several column blocks: E={E} N={N} K={K} T={T} k={k}")
+    wc, wsc, wts, oc, os_, ot, ids, rw, xb = _prefill_case(dev, o, E, N, K, T, k, 131)
+    x = to_dev_bf16(xb, dev)
+    ids_d = torch.from_numpy(ids).to(dev)
+    h = nv.grouped_linear(x, wc, wsc, wts, ids_d).cpu().numpy()
+    x64 = o.bf16_to_f64(xb)
+    for e in range(E):
+        routes = np.nonzero(ids.ravel() == e)[0]
+        wdq = o.dequant(oc[e], os_[e], ot[e:e + 1], per_row=False)
+        yr, b = o.linear_f64(x64[routes // k], wdq)
+        assert_within(h[routes], yr, b, f"column blocks: expert {e} rows")
+    a = nv.grouped_linear(x, wc, wsc, wts, ids_d, out_mode=nv.OUT_SWIGLU_BF16)
+    _swiglu_bits_check(o, a, h, "column blocks")
+    y = nv.grouped_linear(x, wc, wsc, wts, ids_d, topk_w=torch.from_numpy(rw).to(dev),
+                          out_mode=nv.OUT_COMBINE).cpu().numpy()
+    yr, b = o.moe_down_combine(np.repeat(xb, k, axis=0), ids, rw, oc, os_, ot)
+    assert_within(y, yr, b, "column blocks: combine")
+
+
+def test_moe_prefill_layer_full_shape(dev, o, moe):
+    """The MoE layer at prompt size as the benchmark runs it: 4096 tokens over the 128
+    experts, top-8 (32768 routes, the chunked grouping, six SwiGLU column blocks of the
+    1536-wide gate_up and eight of the 2048-wide down), checked stage by stage on the GPU's
+    own intermediates: 128 sampled routes' gate_up rows element-wise, every SwiGLU BF16
+    value from the GPU's fp32 rows, and 64 sampled tokens' down + ordered combine."""
+    cfg = WORKLOADS["moe_decode"]
+    E, k, T = cfg["E"], cfg["top_k"], 4096
+    _say(f"MoE prefill layer: T={T} E={E} top-{k}")
+    ids, rw = moe_routes(cfg["route_seed"] + 1, T, E, k)
+    ids = ids.astype(np.int32)
+    rw = rw.astype(np.float32)
+    xb = act_bf16(cfg["x_seed"] + 1, T, cfg["K_gu"])
+    x = to_dev_bf16(xb, dev)
+    ids_d = torch.from_numpy(ids).to(dev)
+    rw_d = torch.from_numpy(rw).to(dev)
+    # (i) gate_up per-route rows
+    h_d = nv.grouped_linear(x, moe["gc"], moe["gs"], moe["gt"], ids_d)
+    rng = np.random.default_rng(17)
+    routes = np.r_[0, T * k - 1, rng.choice(T * k, 126, replace=False)]
+    h_s = h_d[torch.from_numpy(routes).to(dev)].cpu().numpy()
+    toks, js = routes // k, routes % k
+    hr, hb = o.moe_gate_up(xb[toks], ids[toks, js][:, None].astype(np.int32), moe["ogc"],
+                           moe["ogs"], moe["ogt"])
+    assert_within(h_s, hr, hb, "prefill layer: gate_up rows")
+    # (ii) SwiGLU -> BF16, every value, from the GPU's own rows
+    a = nv.grouped_linear(x, moe["gc"], moe["gs"], moe["gt"], ids_d, out_mode=nv.OUT_SWIGLU_BF16)
+    _swiglu_bits_check(o, a, h_d.cpu().numpy(), "prefill layer")
+    del h_d
+    # (iii) down + ordered combine on the GPU's BF16 rows, reusing the grouping as the
+    # layer does, and without the reuse: the same bits
+    need = max(nv.grouped_workspace_size(T, k, cfg["N_gu"], cfg["K_gu"], E, nv.OUT_SWIGLU_BF16),
+               nv.grouped_workspace_size(T, k, cfg["N_d"], cfg["K_d"], E, nv.OUT_COMBINE))
+    ws = torch.empty((need,), dtype=torch.uint8, device=dev)
+    nv.grouped_linear(x, moe["gc"], moe["gs"], moe["gt"], ids_d, out_mode=nv.OUT_SWIGLU_BF16,
+                      out=a, workspace=ws)
+    y = nv.grouped_linear(a, moe["dc"], moe["ds"], moe["dt"], ids_d, topk_w=rw_d,
+                          out_mode=nv.OUT_COMBINE, rows_per_route=True, workspace=ws,
+                          reuse_grouping=True)
+    y2 = nv.grouped_linear(a, moe["dc"], moe["ds"], moe["dt"], ids_d, topk_w=rw_d,
+                           out_mode=nv.OUT_COMBINE, rows_per_route=True)
+    assert torch.equal(y, y2)
+    a_bits = a.view(torch.int16).cpu().numpy().view(np.uint16)
+    tsel = np.r_[0, T - 1, rng.choice(T, 62, replace=False)]
+    a_sel = np.concatenate([a_bits[t * k:(t + 1) * k] for t in tsel])
+    yr, yb = o.moe_down_combine(a_sel, ids[tsel], rw[tsel], moe["odc"], moe["ods"], moe["odt"])
+    assert_within(y.cpu().numpy()[tsel], yr, yb, "prefill layer: down + combine")
+
+
+def _w4a4_experts_case(dev, o, E, N, K, T, k, seed):
+    wc, wsc, wts, oc, os_, ot = _small_experts(o, dev, E, N, K, seed)
+    ids, rw = moe_routes(seed + 1, T, E, k)
+    ids = ids.astype(np.int32)
+    xb = act_bf16(seed + 2, T, K)
+    xc, xs, xt = nv.quantize_act(to_dev_bf16(xb, dev))
+    qc, qs, qt = o.quantize_bf16(xb, per_row=True)
+    assert np.array_equal(xc.cpu().numpy(), qc) and np.array_equal(xs.cpu().numpy(), qs)
+    assert np.array_equal(xt.cpu().numpy().view(np.uint32), qt.view(np.uint32))
+    return (wc, wsc, wts, oc, os_, ot, ids, rw.astype(np.float32), (xc, xs, xt),
+            (qc, qs, qt))
+
+
+@pytest.mark.parametrize("E,N,K,T,k", [(8, 320, 256, 512, 2),   # GEMM path (128 per expert)
+                                       (16, 192, 256, 4, 4)])    # streaming path (decode size)
+def test_grouped_w4a4_every_output_form(dev, o, E, N, K, T, k):
+    """NVFP4 activations (quantized on the device, bit-exact with the oracle) through the
+    grouped call in all three output forms: per-route rows against the oracle's W4A4
+    linear, SwiGLU BF16 from those rows, and the ordered combine against the oracle's
+    combine of the exactly decoded rows."""
+    _say(f"grouped W4A4: E={E} N={N} K={K} T={T} k={k}")
+    (wc, wsc, wts, oc, os_, ot, ids, rw, (xc, xs, xt),
+     (qc, qs, qt)) = _w4a4_experts_case(dev, o, E, N, K, T, k, 141 + T)
+    ids_d = torch.from_numpy(ids).to(dev)
+    h = nv.grouped_linear(xc, wc, wsc, wts, ids_d, x_scales=xs, x_ts=xt).cpu().numpy()
+    xhat = o.dequant(qc, qs, qt, per_row=True)
+    for e in np.unique(ids):
+        routes = np.nonzero(ids.ravel() == e)[0]
+        wdq = o.dequant(oc[e], os_[e], ot[e:e + 1], per_row=False)
+        yr, b = o.linear_f64(xhat[routes // k], wdq)
+        assert_within(h[routes], yr, b, f"grouped w4a4 rows, expert {e}")
+    a = nv.grouped_linear(xc, wc, wsc, wts, ids_d, x_scales=xs, x_ts=xt,
+                          out_mode=nv.OUT_SWIGLU_BF16)
+    _swiglu_bits_check(o, a, h, f"grouped w4a4 T={T}")
+    y = nv.grouped_linear(xc, wc, wsc, wts, ids_d, x_scales=xs, x_ts=xt,
+                          topk_w=torch.from_numpy(rw).to(dev), out_mode=nv.OUT_COMBINE).cpu().numpy()
+    yr, b = o.moe_combine_rows(np.repeat(xhat, k, axis=0), ids, rw, oc, os_, ot)
+    assert_within(y, yr, b, f"grouped w4a4 T={T}: combine")

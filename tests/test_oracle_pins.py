@@ -3,6 +3,7 @@ planted mistake — a plausible slip in the oracle's C source, applied to a copy
 CPU — must make at least one pin fail."""
 import os
 
+import numpy as np
 import pytest
 
 import oracle
@@ -58,3 +59,21 @@ def test_planted_mistake_is_caught(tmp_path, name):
         except Exception:  # any failure of a pin counts as caught
             caught.append(pin.__name__)
     assert caught, f"planted mistake {name} passed every pin"
+
+
+# planted mistakes in the SwiGLU reading (Python), each of which must fail pin_swiglu
+SWIGLU_MUTANTS = {
+    "sigmoid_without_g": lambda h: (lambda g, u: 1.0 / (1.0 + np.exp(-g)) * u)(*np.split(h, 2, axis=1)),
+    "exp_sign_flipped": lambda h: (lambda g, u: g / (1.0 + np.exp(g)) * u)(*np.split(h, 2, axis=1)),
+    "halves_swapped": lambda h: (lambda u, g: g / (1.0 + np.exp(-g)) * u)(*np.split(h, 2, axis=1)),
+    "gelu_tanh_instead": lambda h: (lambda g, u: 0.5 * g * (1 + np.tanh(0.7978845608 * (g + 0.044715 * g ** 3))) * u)(*np.split(h, 2, axis=1)),
+    "fp32_arithmetic": lambda h: (lambda g, u: (g.astype(np.float32) / (1 + np.exp(-g.astype(np.float32))) * u.astype(np.float32)).astype(np.float64))(*np.split(np.asarray(h, np.float64), 2, axis=1)),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SWIGLU_MUTANTS))
+def test_planted_swiglu_mistake_is_caught(orc, name):
+    o = oracle.Oracle(orc.lib)
+    o.swiglu = SWIGLU_MUTANTS[name]
+    with pytest.raises(AssertionError):
+        P.pin_swiglu(o)
