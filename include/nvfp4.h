@@ -201,6 +201,36 @@ nvfp4_status nvfp4_grouped_linear(int32_t act_kind, const void* x, const uint8_t
                                   size_t* workspace_bytes, uint32_t flags, uint32_t* faults,
                                   void* stream);
 
+/* nvfp4_grouped_linear_noalloc — nvfp4_grouped_linear for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, and harnesses that
+ * forbid allocation. Same arguments and results as nvfp4_grouped_linear without
+ * `workspace` / `workspace_bytes`: the call uses the library's fixed scratch array of
+ * NVFP4_NOALLOC_SCRATCH_BYTES on the current device (hipGetDevice, which must be the device
+ * `stream` runs on), and calls no allocating routine. Each GPU holds its array from its
+ * first such call until the process ends.
+ * Limit: a call whose workspace would exceed NVFP4_NOALLOC_SCRATCH_BYTES (see
+ *   nvfp4_grouped_linear's workspace query) returns NVFP4_ERR_WORKSPACE, enqueuing nothing.
+ *   16 MiB covers the route grouping of up to ~10^6 routes and the fp32 per-route rows of
+ *   a decode-sized NVFP4_OUT_COMBINE (e.g. 128 routes x 2048 columns = 1 MiB).
+ * Sharing: every call on one GPU uses the same array and leaves its contents there (the
+ *   route grouping first, so NVFP4_OUT_REUSE_GROUPING works between two of these calls
+ *   on one stream, the later reusing the earlier's grouping). Calls that can overlap on
+ *   one GPU (two streams, two threads) race on the array and give undefined results:
+ *   order them on one stream. The kernels write every scratch byte they read, so no
+ *   clearing is needed between calls.
+ * Errors: as nvfp4_grouped_linear; _LAUNCH also when the device's scratch address cannot
+ *   be obtained. */
+#define NVFP4_NOALLOC_SCRATCH_BYTES (16u << 20)
+nvfp4_status nvfp4_grouped_linear_noalloc(int32_t act_kind, const void* x,
+                                          const uint8_t* x_scales, const float* x_ts,
+                                          int64_t ldx, int32_t rows_mode, int64_t T,
+                                          int32_t top_k, int64_t N, int64_t K,
+                                          int32_t num_experts, const uint8_t* w_codes,
+                                          const uint8_t* w_scales, const float* w_ts,
+                                          const int32_t* topk_ids, const float* topk_w,
+                                          int32_t out_mode, void* y, uint32_t flags,
+                                          uint32_t* faults, void* stream);
+
 /* nvfp4_read_probe — measurement support, not part of the layer: one plain streaming read
  * of `bytes` bytes at `buf` in one launch, the measured single-launch read roof that the
  * weight-streaming calls are compared against (the pages set their decode paths beside a

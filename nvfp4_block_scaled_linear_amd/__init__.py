@@ -18,7 +18,9 @@ from ._binding import (  # noqa: F401
     OUT_REUSE_GROUPING,
     OUT_ROUTES,
     OUT_SWIGLU_BF16,
+    NOALLOC_SCRATCH_BYTES,
     grouped_linear,
+    grouped_linear_noalloc,
     grouped_workspace_size,
     linear,
     load_library,

@@ -22,7 +22,8 @@ FAULT_NONFINITE, FAULT_BAD_ROUTE, FAULT_NAN_SCALE = 1, 2, 4
 F_CHECK = 1
 
 EXPORTS = ("nvfp4_status_string", "nvfp4_linear", "nvfp4_quantize_act", "nvfp4_grouped_linear",
-           "nvfp4_read_probe")
+           "nvfp4_grouped_linear_noalloc", "nvfp4_read_probe")
+NOALLOC_SCRATCH_BYTES = 16 << 20
 
 _lib = None
 
@@ -55,6 +56,9 @@ def load_library(path: str = LIB_PATH):
     lib.nvfp4_grouped_linear.argtypes = [i32, vp, vp, vp, i64, i32, i64, i32, i64, i64, i32, vp,
                                          vp, vp, vp, vp, i32, vp, vp,
                                          ctypes.POINTER(ctypes.c_size_t), u32, u32p, vp]
+    lib.nvfp4_grouped_linear_noalloc.restype = i32
+    lib.nvfp4_grouped_linear_noalloc.argtypes = [i32, vp, vp, vp, i64, i32, i64, i32, i64, i64,
+                                                 i32, vp, vp, vp, vp, vp, i32, vp, u32, u32p, vp]
     lib.nvfp4_read_probe.restype = i32
     lib.nvfp4_read_probe.argtypes = [vp, i64, i32, u32p, vp]
     _lib = lib
@@ -175,6 +179,26 @@ def grouped_linear(x, w_codes, w_scales, w_ts, topk_ids, *, topk_w=None, out_mod
         _p(out), _p(workspace), ctypes.byref(nbytes), F_CHECK if check else 0, _p(faults),
         _stream())
     _check(st, "nvfp4_grouped_linear")
+    return out
+
+
+def grouped_linear_noalloc(x, w_codes, w_scales, w_ts, topk_ids, *, out, topk_w=None,
+                           out_mode=OUT_ROUTES, rows_per_route=False, x_scales=None, x_ts=None,
+                           faults=None, reuse_grouping=False, check=False):
+    """grouped_linear on the library's fixed per-device scratch (no workspace argument and
+    no allocation: `out` must be given). Calls on one device share that scratch, so they
+    must not overlap; reuse_grouping reuses the grouping of the previous such call."""
+    E, N, half = w_codes.shape
+    K = 2 * half
+    T, top_k = topk_ids.shape
+    act = ACT_BF16 if x_scales is None else ACT_NVFP4
+    ldx = _ld(x) if act == ACT_BF16 else K
+    st = load_library().nvfp4_grouped_linear_noalloc(
+        act, _p(x), _p(x_scales), _p(x_ts), ldx, ROWS_PER_ROUTE if rows_per_route else ROWS_PER_TOKEN,
+        T, top_k, N, K, E, _p(w_codes), _p(w_scales), _p(w_ts), _p(topk_ids), _p(topk_w),
+        out_mode | (OUT_REUSE_GROUPING if reuse_grouping else 0), _p(out),
+        F_CHECK if check else 0, _p(faults), _stream())
+    _check(st, "nvfp4_grouped_linear_noalloc")
     return out
 
 

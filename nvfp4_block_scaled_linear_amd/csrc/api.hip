@@ -1,8 +1,11 @@
 // C ABI of libnvfp4 (declared and documented in include/nvfp4.h): argument checks on the
-// host, then kernel dispatch on the caller's stream. Nothing here allocates memory,
-// synchronizes, or keeps state between calls.
+// host, then kernel dispatch on the caller's stream. Nothing here allocates memory or
+// synchronizes; the only state kept between calls is each device's address of the
+// no-allocation call's fixed scratch array.
 #include <limits.h>
 #include <stdint.h>
+
+#include <mutex>
 
 #include "kernels.hpp"
 #include "nvfp4.h"
@@ -103,6 +106,31 @@ Layout grouped_layout(int64_t T, int top_k, int E, int64_t N, int32_t out_mode) 
   if (out_mode == NVFP4_OUT_COMBINE) o = up256(o + sizeof(float) * R * (size_t)N);
   L.total = o;
   return L;
+}
+
+// The no-allocation grouped call's scratch: a fixed device array (one per GPU, held
+// until the process ends) in place of the caller's workspace. Host code never passes the
+// array's name (a host-side stand-in, not a device address): each device's address comes
+// from hipGetSymbolAddress, taken once per device with that device current.
+constexpr size_t kScratchBytes = (size_t)NVFP4_NOALLOC_SCRATCH_BYTES;
+__device__ __attribute__((aligned(256))) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+
+// this thread's current device's scratch address
+nvfp4_status device_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return NVFP4_ERR_LAUNCH;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return NVFP4_ERR_LAUNCH;
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return NVFP4_OK;
 }
 
 }  // namespace
@@ -318,6 +346,31 @@ nvfp4_status nvfp4_grouped_linear(int32_t act_kind, const void* x, const uint8_t
                        static_cast<float*>(y), s);
   }
   return launch_status(e);
+}
+
+nvfp4_status nvfp4_grouped_linear_noalloc(int32_t act_kind, const void* x,
+                                          const uint8_t* x_scales, const float* x_ts,
+                                          int64_t ldx, int32_t rows_mode, int64_t T,
+                                          int32_t top_k, int64_t N, int64_t K,
+                                          int32_t num_experts, const uint8_t* w_codes,
+                                          const uint8_t* w_scales, const float* w_ts,
+                                          const int32_t* topk_ids, const float* topk_w,
+                                          int32_t out_mode, void* y, uint32_t flags,
+                                          uint32_t* faults, void* stream) {
+  // the size this call needs, from the host-side checks alone (nothing is enqueued)
+  size_t need = 0;
+  nvfp4_status st = nvfp4_grouped_linear(act_kind, x, x_scales, x_ts, ldx, rows_mode, T, top_k,
+                                         N, K, num_experts, w_codes, w_scales, w_ts, topk_ids,
+                                         topk_w, out_mode, y, nullptr, &need, flags, faults,
+                                         stream);
+  if (st != NVFP4_OK) return st;
+  if (need > kScratchBytes) return NVFP4_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if ((st = device_scratch(&ws)) != NVFP4_OK) return st;
+  size_t have = kScratchBytes;
+  return nvfp4_grouped_linear(act_kind, x, x_scales, x_ts, ldx, rows_mode, T, top_k, N, K,
+                              num_experts, w_codes, w_scales, w_ts, topk_ids, topk_w, out_mode,
+                              y, ws, &have, flags, faults, stream);
 }
 
 nvfp4_status nvfp4_read_probe(const void* buf, int64_t bytes, int32_t loads_per_thread,

@@ -162,3 +162,30 @@ def test_binding_fails_loudly_without_library(tmp_path):
     finally:
         _binding._lib = saved
 
+
+def noalloc(lib, act=0, x=P, ldx=2048, rows_mode=0, T=16, k=8, N=1536, K=2048, E=128, wc=P,
+            ws=P, wt=P, ids=P, tw=P, out_mode=0, y=P, flags=0, faults=None):
+    return lib.nvfp4_grouped_linear_noalloc(act, x, None, None, ldx, rows_mode, T, k, N, K, E, wc,
+                                            ws, wt, ids, tw, out_mode, y, flags, faults, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(E=0), ERR_ARG), (dict(k=0), ERR_ARG), (dict(out_mode=3), ERR_ARG),
+    (dict(out_mode=0x100), ERR_ARG), (dict(T=0), ERR_SHAPE), (dict(K=2047), ERR_SHAPE),
+    (dict(act=2), ERR_ARG), (dict(flags=1), ERR_NULL), (dict(flags=4), ERR_ARG),
+    # beyond the fixed scratch: the combine of 4096 tokens x 8 routes x 2048 fp32 columns
+    (dict(T=4096, N=2048, K=768, out_mode=2), ERR_WORKSPACE),
+    (dict(T=2048, k=8, N=512, K=768, out_mode=2), ERR_WORKSPACE),
+])
+def test_noalloc_refusals(lib, kw, status):
+    """The no-allocation grouped call refuses bad arguments, and calls whose workspace
+    would exceed its fixed scratch, on the host: before it touches a device."""
+    assert noalloc(lib, **kw) == status
+
+
+def test_noalloc_scratch_limit_matches_the_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define NVFP4_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == nv.NOALLOC_SCRATCH_BYTES
+    # the largest combine that fits: a decode-sized MoE layer (16 tokens x top-8 x 2048)
+    assert nv.grouped_workspace_size(16, 8, 2048, 768, 128, nv.OUT_COMBINE) < nv.NOALLOC_SCRATCH_BYTES
