@@ -392,24 +392,38 @@ __device__ __forceinline__ void pass4(const StreamArgs& a, const uint8_t* wc, co
         wb[4 * d + 2] = cvt2<2>(b.w[t][d]);
         wb[4 * d + 3] = cvt2<3>(b.w[t][d]);
       }
+      // Scale block 0 (k 0..15 of the lane's 32, activation pieces 0, 1) and block 1 (k
+      // 16..31, pieces 2, 3) of every row set: 2R independent chains of four MFMAs, issued
+      // round-robin so that no MFMA waits on the one before it, then each chain's
+      // partial times its block's scale into the accumulator (block 0, then block 1).
+      f32x4 c0[R], c1[R];
 #pragma unroll
       for (int r = 0; r < R; r++) {
-        // scale block 0: k 0..15 of the lane's 32, pieces 0, 1 (suppliers bp = 0, 1)
-        f32x4 c = f32x4{0.f, 0.f, 0.f, 0.f};
-        c = mfma4<0>(A[r][0], A[r][1], wb[0], wb[1], c);
-        c = mfma4<0>(A[r][2], A[r][3], wb[2], wb[3], c);
-        c = mfma4<1>(A[r][0], A[r][1], wb[4], wb[5], c);
-        c = mfma4<1>(A[r][2], A[r][3], wb[6], wb[7], c);
+        c0[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+        c1[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
 #pragma unroll
-        for (int qq = 0; qq < 4; qq++) acc[t][r][qq] = __builtin_fmaf(s0, c[qq], acc[t][r][qq]);
-        // scale block 1: k 16..31, pieces 2, 3
-        c = f32x4{0.f, 0.f, 0.f, 0.f};
-        c = mfma4<2>(A[r][0], A[r][1], wb[8], wb[9], c);
-        c = mfma4<2>(A[r][2], A[r][3], wb[10], wb[11], c);
-        c = mfma4<3>(A[r][0], A[r][1], wb[12], wb[13], c);
-        c = mfma4<3>(A[r][2], A[r][3], wb[14], wb[15], c);
+      for (int r = 0; r < R; r++) c0[r] = mfma4<0>(A[r][0], A[r][1], wb[0], wb[1], c0[r]);
 #pragma unroll
-        for (int qq = 0; qq < 4; qq++) acc[t][r][qq] = __builtin_fmaf(s1, c[qq], acc[t][r][qq]);
+      for (int r = 0; r < R; r++) c1[r] = mfma4<2>(A[r][0], A[r][1], wb[8], wb[9], c1[r]);
+#pragma unroll
+      for (int r = 0; r < R; r++) c0[r] = mfma4<0>(A[r][2], A[r][3], wb[2], wb[3], c0[r]);
+#pragma unroll
+      for (int r = 0; r < R; r++) c1[r] = mfma4<2>(A[r][2], A[r][3], wb[10], wb[11], c1[r]);
+#pragma unroll
+      for (int r = 0; r < R; r++) c0[r] = mfma4<1>(A[r][0], A[r][1], wb[4], wb[5], c0[r]);
+#pragma unroll
+      for (int r = 0; r < R; r++) c1[r] = mfma4<3>(A[r][0], A[r][1], wb[12], wb[13], c1[r]);
+#pragma unroll
+      for (int r = 0; r < R; r++) c0[r] = mfma4<1>(A[r][2], A[r][3], wb[6], wb[7], c0[r]);
+#pragma unroll
+      for (int r = 0; r < R; r++) c1[r] = mfma4<3>(A[r][2], A[r][3], wb[14], wb[15], c1[r]);
+#pragma unroll
+      for (int r = 0; r < R; r++) {
+#pragma unroll
+        for (int qq = 0; qq < 4; qq++) acc[t][r][qq] = __builtin_fmaf(s0, c0[r][qq], acc[t][r][qq]);
+#pragma unroll
+        for (int qq = 0; qq < 4; qq++) acc[t][r][qq] = __builtin_fmaf(s1, c1[r][qq], acc[t][r][qq]);
       }
     }
   };
