@@ -122,13 +122,18 @@ __host__ __device__ __forceinline__ uint32_t xq_bytes(int64_t K) {
 }
 
 // LDS layout of a workgroup: [scales | transpose buffers of the W waves, or the quantized
-// rows] during the stream, then the reduction buffer over the same bytes.
+// rows | the waves' partial sums]. The partial sums have their own bytes, so a wave can
+// write them while another still streams.
+__host__ __device__ __forceinline__ uint32_t lds_red_offset(int TN, int R, int W, int64_t K,
+                                                            bool slds, int act = 0) {
+  const uint32_t stream =
+      lds_scale_bytes(TN, K, slds) + (act == 2 ? xq_bytes(K) : (uint32_t)(W * R) * kXSet);
+  return (stream + 15u) & ~15u;
+}
+// one wave's partials: 16 weight rows x 4 activation rows per (tile, row set)
 __host__ __device__ __forceinline__ size_t lds_bytes(int TN, int R, int W, int64_t K, bool slds,
                                                      int act = 0) {
-  const size_t stream =
-      lds_scale_bytes(TN, K, slds) + (act == 2 ? (size_t)xq_bytes(K) : (size_t)W * R * kXSet);
-  const size_t red = (size_t)W * TN * R * 64 * 4 * sizeof(float);
-  return stream > red ? stream : red;
+  return lds_red_offset(TN, R, W, K, slds, act) + (size_t)W * TN * R * 16 * 4 * sizeof(float);
 }
 
 // Waves splitting K: about eight 128-k steps per wave, one to four waves. The in-call
@@ -276,7 +281,9 @@ __device__ __forceinline__ void pass4(const StreamArgs& a, const uint8_t* wc, co
   const uint32_t K = (uint32_t)a.K;
   const uint32_t kb = K >> 1, sb = K >> 4;
   const int NS = (int)((K + 127u) >> 7);
-  const int per_wave = (NS + W - 1) / W;
+  // an even number of steps per wave, so that each wave's scale bytes (8 per step and row)
+  // start on a 16-byte boundary
+  const int per_wave = 2 * ((NS + 2 * W - 1) / (2 * W));
   const int first = wave * per_wave;
   const int NSW = first < NS ? min(per_wave, NS - first) : 0;  // uniform over the wave
 
@@ -428,31 +435,33 @@ __device__ __forceinline__ void pass4(const StreamArgs& a, const uint8_t* wc, co
     }
   };
 
-  // With SLDS the workgroup first copies its tile's scale rows (one contiguous block of
-  // rows_here * K/16 bytes) into LDS with 16-byte loads; the weight ring is issued before
-  // the copy is waited on, so the two latencies overlap.
-  constexpr int kScaleRegs = 4;  // 16-byte scale chunks per thread held in flight
-  u32x4 sreg[kScaleRegs];
-  const uint32_t chunks_per_row = sb >> 4;  // SLDS requires K % 256 == 0
-  const uint32_t s_chunks = 16u * TN * chunks_per_row;  // 16 LDS rows per tile
-  // chunk c: tile c / (16 * chunks_per_row), row (c / chunks_per_row) % 16
-  auto chunk_src = [&](uint32_t cidx) -> uint32_t {
-    const uint32_t lrow = cidx / chunks_per_row, col = (cidx % chunks_per_row) * 16;
-    const int t = (int)(lrow >> 4), row = (int)(lrow & 15);
-    bool ok = cidx < s_chunks;
-    uint32_t off = 0;
-#pragma unroll
-    for (int tt = 0; tt < TN; tt++)
-      if (tt == t) {
-        ok = ok && row < lim[tt];
-        off = (uint32_t)((tt * tstride + row) * sb) + col;
-      }
-    return ok ? off : kOOB;
+  // With SLDS each wave copies the scale bytes of its own steps (8 per 128-k step and
+  // weight row: bytes [8 first, 8 (first + NSW)) of each tile row) into the workgroup's
+  // scale rows in LDS and reads back only those, so no wave waits for another. Lane L
+  // copies 16-byte piece L % 4 (+ 4j) of row L / 4 of each tile, so one load per lane and
+  // tile covers eight steps; that first round is issued before the weight ring, so its
+  // latency overlaps the ring's. Pieces past the wave's steps, and rows past N, read as
+  // zero; the former go to a spare slot after the scale rows.
+  const uint32_t s_pieces = (uint32_t)(NSW + 1) >> 1;  // 16-byte pieces per row (uniform)
+  const int srow_l = lane >> 2;                        // tile row of the lane's pieces
+  auto piece_src = [&](int t, uint32_t p) -> uint32_t {
+    const bool ok = p < s_pieces && srow_l < lim[t];
+    return ok ? (uint32_t)((t * tstride + srow_l) * sb) + 8u * (uint32_t)first + 16u * p : kOOB;
   };
+  auto piece_put = [&](int t, uint32_t p, u32x4 v) {
+    const uint32_t at = p < s_pieces ? (16u * t + srow_l) * sls + 8u * (uint32_t)first + 16u * p
+                                     : 16u * TN * sls;
+    uint32_t* d = reinterpret_cast<uint32_t*>(lds_s + at);  // rows are 4-byte aligned
+    d[0] = v[0];
+    d[1] = v[1];
+    d[2] = v[2];
+    d[3] = v[3];
+  };
+  u32x4 sreg[TN];
   if (SLDS) {
 #pragma unroll
-    for (int qq = 0; qq < kScaleRegs; qq++)
-      sreg[qq] = __builtin_amdgcn_raw_buffer_load_b128(sr, chunk_src(threadIdx.x + qq * blockDim.x), 0, 0);
+    for (int t = 0; t < TN; t++)
+      sreg[t] = __builtin_amdgcn_raw_buffer_load_b128(sr, piece_src(t, lane & 3), 0, 0);
   }
   XqRegs xq_regs;
   if constexpr (ACT == 2) {
@@ -466,30 +475,21 @@ __device__ __forceinline__ void pass4(const StreamArgs& a, const uint8_t* wc, co
     load_scales(j, j);
   }
   // In-call quantization of the (up to four) BF16 rows while the weight ring is in flight;
-  // the barrier after the scale copy below (or its own) publishes the rows.
+  // every wave reads all of them, hence the barrier.
   if constexpr (ACT == 2) {
     xq_finish(a, xq_regs, xbuf);
-    if (!SLDS) __syncthreads();
+    __syncthreads();
   }
   if (SLDS) {
-    // Chunks past the tiles go to the spare 16 bytes after the scale rows, so the stores
-    // need no branch (a branch would make the wave wait for every load in flight).
-    const uint32_t spare = 16u * TN * sls;
-    auto put = [&](uint32_t cidx, u32x4 v) {
-      const uint32_t row = cidx / chunks_per_row, col = (cidx % chunks_per_row) * 16;
-      const uint32_t at = cidx < s_chunks ? row * sls + col : spare;
-      uint32_t* d = reinterpret_cast<uint32_t*>(lds_s + at);
-      d[0] = v[0];
-      d[1] = v[1];
-      d[2] = v[2];
-      d[3] = v[3];
-    };
 #pragma unroll
-    for (int qq = 0; qq < kScaleRegs; qq++) put(threadIdx.x + qq * blockDim.x, sreg[qq]);
-    // tiles with more chunks than the prefetch holds copy the rest directly
-    for (uint32_t cidx = threadIdx.x + kScaleRegs * blockDim.x; cidx < s_chunks; cidx += blockDim.x)
-      put(cidx, __builtin_amdgcn_raw_buffer_load_b128(sr, chunk_src(cidx), 0, 0));
-    __syncthreads();
+    for (int t = 0; t < TN; t++) piece_put(t, lane & 3, sreg[t]);
+    // runs longer than eight steps: the further pieces, loaded and stored directly
+    const uint32_t s_rounds = (s_pieces + 3u) & ~3u;  // uniform trip count
+    for (uint32_t p = (uint32_t)(lane & 3) + 4u; p < s_rounds; p += 4u) {
+#pragma unroll
+      for (int t = 0; t < TN; t++)
+        piece_put(t, p, __builtin_amdgcn_raw_buffer_load_b128(sr, piece_src(t, p), 0, 0));
+    }
   }
   // Rounds of kDepth steps; every round but the last refills the ring, the last one only
   // drains it (a peeled round rather than guarded loads, which would make the compiler
@@ -510,41 +510,66 @@ __device__ __forceinline__ void pass4(const StreamArgs& a, const uint8_t* wc, co
     if (last + j < NSW) compute(buf[j], kstep[j], j);
 }
 
-// Adds the partials of the four k-groups and of the waves in a fixed order and hands each
-// (x row m, weight row n, sum) to `store`. acc[t][r][q] is x row 4r + q, weight row
-// 16t + nl. LDS: red[wave][t][r][lane][q], over the bytes the stream used (hence the
-// barrier first).
-template <int TN, int R, typename Store>
-__device__ __forceinline__ void reduce_store(const f32x4 (&acc)[TN][R], float* red, int64_t n0,
-                                             Store store) {
+// The fixed order in which partial sums meet: a wave's four k-groups in registers,
+// (g0 + g2) + (g1 + g3), then the waves in order in LDS, starting from zero.
+//
+// group_sum: the sum over the k-groups of lane i's partial (lane 16g + i holds group g's),
+// left in every lane. v_permlane32_swap with v as both operands returns the rows (0, 1,
+// 0, 1) and (2, 3, 2, 3) of v; v_permlane16_swap with s as both returns (0, 0, 2, 2) and
+// (1, 1, 3, 3) of s.
+__device__ __forceinline__ float group_sum(float v) {
+  const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  const float s = __uint_as_float(h[0]) + __uint_as_float(h[1]);
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(s), __float_as_uint(s), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// acc[t][r][q] of lane (g, i) is the partial of weight row 16t + i and activation row
+// 4r + q over k-group g of this wave's steps. The k-groups' sums go to
+// red[wave][t][r][i][q] (lanes 0..15 write them).
+template <int TN, int R>
+__device__ __forceinline__ void write_partials(const f32x4 (&acc)[TN][R], float* red) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int W = blockDim.x >> 6;
-  __syncthreads();
 #pragma unroll
   for (int t = 0; t < TN; t++)
 #pragma unroll
-    for (int r = 0; r < R; r++)
-      *reinterpret_cast<f32x4*>(red + (((wave * TN + t) * R + r) * 64 + lane) * 4) = acc[t][r];
-  __syncthreads();
-  // one output per (t, r, q, nl)
-  for (int o = threadIdx.x; o < TN * R * 64; o += blockDim.x) {
-    const int nl = o & 15, q = (o >> 4) & 3, r = (o >> 6) % R, t = (o >> 6) / R;
-    const int lane0 = 4 * (nl >> 2) + (nl & 3);  // the group-0 lane holding row nl
-    float s = 0.f;
-    for (int w = 0; w < W; w++)
+    for (int r = 0; r < R; r++) {
+      f32x4 v;
 #pragma unroll
-      for (int gg = 0; gg < 4; gg++)
-        s += red[(((w * TN + t) * R + r) * 64 + lane0 + 16 * gg) * 4 + q];
-    store(4 * r + q, n0 + 16 * t + nl, s);
-  }
+      for (int q = 0; q < 4; q++) v[q] = group_sum(acc[t][r][q]);
+      if (lane < 16) *reinterpret_cast<f32x4*>(red + (((wave * TN + t) * R + r) * 16 + lane) * 4) = v;
+    }
+}
+
+// the sum over the W waves, in order, of output (tile t, row set r, weight row i, act row q)
+template <int TN, int R>
+__device__ __forceinline__ float wave_sum(const float* red, int W, int t, int r, int i, int q) {
+  float s = 0.f;
+  for (int w = 0; w < W; w++) s += red[(((w * TN + t) * R + r) * 16 + i) * 4 + q];
+  return s;
+}
+
+// Adds the partials in the fixed order and hands each (x row m, weight row n, sum) to
+// `store`. red: the workgroup's partial-sum bytes (lds_red_offset), which no stream step
+// uses, so only the one barrier between the writes and the reads is needed.
+template <int TN, int R, typename Store>
+__device__ __forceinline__ void reduce_store(const f32x4 (&acc)[TN][R], float* red, int64_t n0,
+                                             Store store) {
+  const int W = blockDim.x >> 6;
+  write_partials<TN, R>(acc, red);
   __syncthreads();
+  // one output per (t, r, q, i)
+  for (int o = threadIdx.x; o < TN * R * 64; o += blockDim.x) {
+    const int i = o & 15, q = (o >> 4) & 3, r = (o >> 6) % R, t = (o >> 6) / R;
+    store(4 * r + q, n0 + 16 * t + i, wave_sum<TN, R>(red, W, t, r, i, q));
+  }
 }
 
 template <int TN, int R, int ACT, bool SLDS>
 __global__ __launch_bounds__(256) void stream_dense(StreamArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  float* red = reinterpret_cast<float*>(lds);
+  float* red = reinterpret_cast<float*>(lds + lds_red_offset(TN, R, blockDim.x >> 6, a.K, SLDS, ACT));
   const int64_t n0 = (int64_t)blockIdx.x * 16 * TN;
   const int i = (threadIdx.x >> 4) & 3;  // the x row this lane loads within a set of four
   RowMap rm;
@@ -574,7 +599,7 @@ __global__ __launch_bounds__(256) void stream_dense(StreamArgs a) {
     const float* tq = reinterpret_cast<const float*>(lds + lds_scale_bytes(TN, a.K, SLDS) +
                                                      4 * xq_row_bytes(a.K) + 32);
 #pragma unroll
-    for (int m = 0; m < 4; m++) ts_q[m] = tq[m];  // before the reduction reuses the bytes
+    for (int m = 0; m < 4; m++) ts_q[m] = tq[m];
   }
   reduce_store<TN, R>(acc, red, n0, [&](int m, int64_t n, float s) {
     if (m < a.M && n < a.N) {
@@ -587,7 +612,7 @@ __global__ __launch_bounds__(256) void stream_dense(StreamArgs a) {
 template <int R, int ACT, bool SLDS>
 __global__ __launch_bounds__(256) void stream_grouped(StreamArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  float* red = reinterpret_cast<float*>(lds);
+  float* red = reinterpret_cast<float*>(lds + lds_red_offset(1, R, blockDim.x >> 6, a.K, SLDS));
   const int slot = blockIdx.y;
   if (slot >= *a.n_active) return;  // uniform over the workgroup
   const int e = a.active[slot];
@@ -628,6 +653,7 @@ __global__ __launch_bounds__(256) void stream_grouped(StreamArgs a) {
         a.y[(int64_t)rr * a.ldy + n] = s * f;
       }
     });
+    __syncthreads();  // the next pass writes its partials over these
   }
 }
 
@@ -639,7 +665,7 @@ __global__ __launch_bounds__(256) void stream_grouped(StreamArgs a) {
 template <int R, int ACT, bool SLDS>
 __global__ __launch_bounds__(256) void stream_grouped_swiglu(StreamArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  float* red = reinterpret_cast<float*>(lds);
+  float* red = reinterpret_cast<float*>(lds + lds_red_offset(2, R, blockDim.x >> 6, a.K, SLDS));
   const int slot = blockIdx.y;
   if (slot >= *a.n_active) return;  // uniform over the workgroup
   const int e = a.active[slot];
@@ -652,8 +678,6 @@ __global__ __launch_bounds__(256) void stream_grouped_swiglu(StreamArgs a) {
   const int vr = (int)((half - n0) < 16 ? (half - n0) : 16);
   const int lim[2] = {vr, vr};
   const int i = (threadIdx.x >> 4) & 3;
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
   const int W = blockDim.x >> 6;
   for (int c0 = beg; c0 < end; c0 += 4 * R) {
     const int rows = min(4 * R, end - c0);
@@ -674,23 +698,12 @@ __global__ __launch_bounds__(256) void stream_grouped_swiglu(StreamArgs a) {
     }
     f32x4 acc[2][R];
     pass4<2, R, ACT, SLDS, grouped_ring_depth(R)>(a, wc, ws, n0, half, lim, rm, lds, acc);
-    __syncthreads();
-#pragma unroll
-    for (int t = 0; t < 2; t++)
-#pragma unroll
-      for (int r = 0; r < R; r++)
-        *reinterpret_cast<f32x4*>(red + (((wave * 2 + t) * R + r) * 64 + lane) * 4) = acc[t][r];
+    write_partials<2, R>(acc, red);
     __syncthreads();
     for (int o = threadIdx.x; o < R * 64; o += blockDim.x) {
       const int nl = o & 15, q = (o >> 4) & 3, r = o >> 6;
-      const int lane0 = 4 * (nl >> 2) + (nl & 3);
-      float sg = 0.f, su = 0.f;
-      for (int w = 0; w < W; w++)
-#pragma unroll
-        for (int gg = 0; gg < 4; gg++) {
-          sg += red[(((w * 2 + 0) * R + r) * 64 + lane0 + 16 * gg) * 4 + q];
-          su += red[(((w * 2 + 1) * R + r) * 64 + lane0 + 16 * gg) * 4 + q];
-        }
+      const float sg = wave_sum<2, R>(red, W, 0, r, nl, q);
+      const float su = wave_sum<2, R>(red, W, 1, r, nl, q);
       const int m = 4 * r + q;
       const int64_t n = n0 + nl;
       if (m < rows && n < half) {
