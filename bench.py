@@ -64,6 +64,33 @@ class Timer:
         torch.cuda.synchronize()
         return self.a.elapsed_time(self.b) / reps  # ms per fn()
 
+    @staticmethod
+    def samples(fn, reps):
+        """ms of each of `reps` back-to-back calls of fn, from one event recorded between
+        consecutive calls on the current stream."""
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        torch.cuda.synchronize()
+        ev[0].record()
+        for i in range(reps):
+            fn()
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        return [ev[i].elapsed_time(ev[i + 1]) for i in range(reps)]
+
+
+def timed(g, reps, per):
+    """Mean ms per unit over `reps` timed replays of graph g holding `per` units, and the
+    spread of the per-replay means (us)."""
+    samp = [t / per * 1e3 for t in Timer.samples(g.replay, reps)]
+    return float(np.mean(samp)) * 1e-3, spread(samp)
+
+
+def spread(per_launch_us):
+    """Median, p10 and p90 of per-launch times (each sample: one replay's mean launch)."""
+    a = np.asarray(per_launch_us, dtype=np.float64)
+    return {"us_med": round(float(np.median(a)), 3), "us_p10": round(float(np.percentile(a, 10)), 3),
+            "us_p90": round(float(np.percentile(a, 90)), 3), "replays": int(a.size)}
+
 
 def warm_until(fn, seconds):
     """Untimed repetitions of fn for about `seconds` of wall time."""
@@ -218,9 +245,12 @@ def bench_decode_sweep(nv, dev, steps, warmup):
                 nv.linear(xs[M], W[j][0], W[j][1], t, out=ys[M])
         gm = capture(one_m)
         timer.time(gm.replay, 1)
-        ms = timer.time(gm.replay, max(2, reps)) / R
+        # each replay launches the kernel R times, each on its own weight copy
+        samp = [t / R * 1e3 for t in Timer.samples(gm.replay, max(25, reps))]
+        ms = float(np.mean(samp)) * 1e-3
         b = linear_bytes(M, N, K)
-        per_m[str(M)] = {"us": round(ms * 1e3, 3), "GBps": round(b / (ms * 1e-3) / 1e9, 1),
+        per_m[str(M)] = {"us": round(ms * 1e3, 3), **spread(samp), "launches_per_replay": R,
+                         "GBps": round(b / (ms * 1e-3) / 1e9, 1),
                          "frac_hbm": round(b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
                          "bytes": b}
         del gm
@@ -274,14 +304,15 @@ def bench_single(nv, dev):
     g = capture(run)
     timer = Timer()
     timer.time(g.replay, 1)
-    ms = timer.time(g.replay, 3) / R
+    ms, sp = timed(g, 25, R)
     b = linear_bytes(M, N, K)
     del g
     # a launch this small is latency: the plain streaming read of the same bytes, timed the
     # same way, is its measured floor
     probe = read_probe_roof(nv, dev, b, timer)
     gbps = b / (ms * 1e-3) / 1e9
-    return {"workload": "M=1 K=2048 N=2048", "us": round(ms * 1e3, 3),
+    return {"workload": "M=1 K=2048 N=2048", "us": round(ms * 1e3, 3), **sp,
+            "launches_per_replay": R,
             "GBps": round(gbps, 1), "bytes": b, "read_probe_us": probe["us"],
             "frac_read_probe": round(gbps / probe["GBps"], 4)}
 
@@ -302,7 +333,7 @@ def bench_prefill(nv, dev):
     g = capture(run)
     timer = Timer()
     warm_until(g.replay, 0.15)  # the clock settles under sustained MFMA load
-    ms = timer.time(g.replay, 10) / R
+    ms, sp = timed(g, 25, R)
     # clock and power under the same load, back-to-back replays outside the timed region
     with PowerSampler() as ps:
         for _ in range(max(1, int(0.3 / (ms * R * 1e-3)))):
@@ -310,7 +341,8 @@ def bench_prefill(nv, dev):
         torch.cuda.synchronize()
     flops = 2.0 * M * N * K
     tf = flops / (ms * 1e-3) / 1e12
-    return {"workload": "M=2048 K=4096 N=14336", "us": round(ms * 1e3, 2), "TFLOPs": round(tf, 1),
+    return {"workload": "M=2048 K=4096 N=14336", "us": round(ms * 1e3, 2), **sp,
+            "launches_per_replay": R, "TFLOPs": round(tf, 1),
             "frac_bf16_mfma": round(tf / BF16_PEAK_TFLOPS, 4), "flop": flops,
             "clock_power": ps.res}
 
@@ -336,10 +368,11 @@ def bench_w4a4(nv, dev):
                 nv.linear(xc, W[j][0], W[j][1], t, x_scales=xs_, x_ts=xt, out=y)
         g = capture(run)
         warm_until(g.replay, 0.1)
-        ms = timer.time(g.replay, 5) / reps_in
+        ms, sp = timed(g, 25, reps_in)
         b = weight_bytes(N, K) + 4 + M * (2 * K + K // 2 + K // 16 + 4) + M * (K // 2 + K // 16 + 4) + 4 * M * N
         fl = 2.0 * M * N * K
-        out[str(M)] = {"us_quantize_plus_linear": round(ms * 1e3, 3),
+        out[str(M)] = {"us_quantize_plus_linear": round(ms * 1e3, 3), **sp,
+                       "pairs_per_replay": reps_in,
                        "GBps": round(b / (ms * 1e-3) / 1e9, 1),
                        "TFLOPs": round(fl / (ms * 1e-3) / 1e12, 2)}
         del g
@@ -375,7 +408,9 @@ def bench_w4a4_in_call(nv, dev):
         for name, fn in (("us_two_calls", two_calls), ("us_in_call", in_call)):
             g = capture(fn)
             warm_until(g.replay, 0.05)
-            rec[name] = round(timer.time(g.replay, 5) / R * 1e3, 3)
+            ms, sp = timed(g, 25, R)
+            rec[name] = round(ms * 1e3, 3)
+            rec[name + "_p10_p90"] = [sp["us_p10"], sp["us_p90"]]
             del g
         out[str(M)] = rec
     return out
@@ -414,12 +449,12 @@ def bench_moe(nv, dev):
     g = capture(run)
     timer = Timer()
     timer.time(g.replay, 1)
-    ms = timer.time(g.replay, 3) / R
+    ms, sp = timed(g, 25, R)
     D = len(np.unique(ids))
     per_expert = weight_bytes(cfg["N_gu"], cfg["K_gu"]) + weight_bytes(cfg["N_d"], cfg["K_d"]) + 8
     b = D * per_expert + T * cfg["K_gu"] * 2 + T * cfg["N_d"] * 4
     return {"workload": "128 experts, gate_up 2048->1536 + down 768->2048, 16 tokens, top-8",
-            "distinct_experts": D, "us_layer": round(ms * 1e3, 2),
+            "distinct_experts": D, "us_layer": round(ms * 1e3, 2), **sp, "layers_per_replay": R,
             "GBps": round(b / (ms * 1e-3) / 1e9, 1), "frac_hbm": round(b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
             "bytes": b}
 
@@ -455,12 +490,12 @@ def bench_moe_prefill(nv, dev):
     g = capture(run)
     timer = Timer()
     warm_until(g.replay, 0.15)
-    ms = timer.time(g.replay, 10)
+    ms, sp = timed(g, 25, 1)
     R = T * k
     flops = 2.0 * R * (cfg["N_gu"] * cfg["K_gu"] + cfg["N_d"] * cfg["K_d"])
     tf = flops / (ms * 1e-3) / 1e12
     return {"workload": f"{T} tokens, 128 experts, top-8, gate_up 2048->1536 + down 768->2048",
-            "us_layer": round(ms * 1e3, 2), "TFLOPs": round(tf, 1),
+            "us_layer": round(ms * 1e3, 2), **sp, "TFLOPs": round(tf, 1),
             "frac_bf16_mfma": round(tf / BF16_PEAK_TFLOPS, 4), "flop": flops}
 
 
@@ -513,11 +548,24 @@ def measured_traffic():
 
 def summarize_rocprof(out_dir, calib_bytes):
     """Prints a short text summary of rocprofv3 output under out_dir: per-kernel dispatch
-    counts and mean durations from --kernel-trace --stats, and per-kernel mean FETCH_SIZE /
-    WRITE_SIZE from --pmc runs, the latter scaled by what the same counters read for the
-    1 GiB device copy (calib_bytes read and written)."""
+    counts and mean durations from --kernel-trace --stats; per-kernel median, p10 and p90
+    of the dispatch durations from the kernel trace itself; and per-kernel mean
+    FETCH_SIZE / WRITE_SIZE from --pmc runs, scaled by what the same counters read for
+    the 1 GiB device copy (calib_bytes read and written)."""
     import csv
     import glob
+    traces = sorted(glob.glob(os.path.join(out_dir, "**", "*kernel_trace.csv"), recursive=True))
+    for f in traces:
+        durs = {}
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+                durs.setdefault(r["Kernel_Name"], []).append(d)
+        print(f"dispatch durations (us) from {os.path.relpath(f, out_dir)}: median p10 p90")
+        for name, d in sorted(durs.items(), key=lambda kv: -len(kv[1])):
+            a = np.asarray(d)
+            print(f"  {name[:110]:110s} n {a.size:6d} med {np.median(a):9.3f} "
+                  f"p10 {np.percentile(a, 10):9.3f} p90 {np.percentile(a, 90):9.3f}")
     stats = sorted(glob.glob(os.path.join(out_dir, "**", "*kernel_stats.csv"), recursive=True))
     for f in stats:
         print(f"kernel stats: {os.path.relpath(f, out_dir)}")
@@ -553,6 +601,12 @@ def summarize_rocprof(out_dir, calib_bytes):
         f = factors.get(ctr)
         scaled = f"{kib * 1024 * f:14.0f} B" if f else "   (uncalibrated)"
         print(f"  {ctr:10s} {kname[:100]:100s} dispatches {n:6d} mean {kib:12.1f} KiB {scaled}")
+    # per kernel: scaled FETCH + WRITE per dispatch (the HBM bytes one launch moves)
+    if "FETCH_SIZE" in factors and "WRITE_SIZE" in factors:
+        names = sorted({k for k, c in means if c == "FETCH_SIZE"} & {k for k, c in means if c == "WRITE_SIZE"})
+        for kname in names:
+            b = sum(means[(kname, c)][0] * 1024 * factors[c] for c in ("FETCH_SIZE", "WRITE_SIZE"))
+            print(f"  traffic {kname[:100]:100s} {b:14.0f} B per dispatch")
     # the streaming kernel over every launch of the run (each decode M launches equally often)
     if "FETCH_SIZE" in factors and "WRITE_SIZE" in factors:
         tot = 0.0
@@ -564,31 +618,134 @@ def summarize_rocprof(out_dir, calib_bytes):
         print(f"traffic_bytes_per_launch: {tot:.0f}")
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def _clock(fn, min_s=0.3, max_reps=1000):
+    """Seconds per call of fn, repeated for at least min_s of wall time."""
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        fn()
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= min_s or n >= max_reps:
+            return el / n
+
+
 def cpu_baseline(decode):
-    """The CPU oracle (as written for the tests) on the same decode sweep: dequantize the
-    weight, then the float64 linear for each M. Repeated until ~10 s of work."""
+    """The CPU oracle (the code the tests check against, not tuned for speed) on the same
+    workloads, on the host's threads: the headline figure on the full decode sweep
+    (dequantize the weight once, then the float64 linear for M = 1, 2, 4, 8, 16), and per
+    workload the quantizer and the linear timed separately, on the sample stated."""
     import oracle
-    from synth import WORKLOADS, act_bf16, weight_f32
+    from synth import WORKLOADS, act_bf16, moe_expert_weights, moe_routes, weight_f32
+    o = oracle.Oracle()
+    cores = o.num_threads()
+    per = {}
+    # decode sweep (the headline): weight quantize, then dequantize + linear per step
     cfg = WORKLOADS["decode_sweep"]
     N, K = cfg["N"], cfg["K"]
-    o = oracle.Oracle()
-    oc, os_, ot = o.quantize(weight_f32(cfg["w_seed"], N, K), per_row=False)
-    xs = {M: act_bf16(cfg["x_seed_base"] + M, M, K) for M in cfg["Ms"]}
+    w = weight_f32(cfg["w_seed"], N, K)
+    t_q = _clock(lambda: o.quantize(w, per_row=False), min_s=0.5, max_reps=3)
+    oc, os_, ot = o.quantize(w, per_row=False)
+    xs = {M: o.bf16_to_f64(act_bf16(cfg["x_seed_base"] + M, M, K)) for M in cfg["Ms"]}
+    t_dq = _clock(lambda: o.dequant(oc, os_, ot, per_row=False), min_s=0.5, max_reps=5)
+    wdq = o.dequant(oc, os_, ot, per_row=False)
+    t_lin = {str(M): _clock(lambda M=M: o.linear_f64(xs[M], wdq), min_s=1.0) for M in cfg["Ms"]}
+    per_step = t_dq + sum(t_lin.values())
+    per["decode_sweep"] = {"quantize_weight_s": round(t_q, 4), "dequantize_s": round(t_dq, 4),
+                           "linear_s": {m: round(v, 5) for m, v in t_lin.items()},
+                           "sample": "full (12288x4096 weight, all five M)"}
+    # single linear
+    cfg = WORKLOADS["single_linear"]
+    w = weight_f32(cfg["w_seed"], cfg["N"], cfg["K"])
+    t_q = _clock(lambda: o.quantize(w, per_row=False))
+    q = o.quantize(w, per_row=False)
+    xb = act_bf16(cfg["x_seed"], cfg["M"], cfg["K"])
+    t_lin = _clock(lambda: o.linear(xb, *q))
+    per["single_linear"] = {"quantize_weight_s": round(t_q, 5), "linear_s": round(t_lin, 5),
+                            "sample": "full"}
+    # prefill: the weight quantize in full, the linear on 16 of the 2048 rows
+    cfg = WORKLOADS["prefill"]
+    w = weight_f32(cfg["w_seed"], cfg["N"], cfg["K"])
+    t_q = _clock(lambda: o.quantize(w, per_row=False), min_s=0.5, max_reps=2)
+    q = o.quantize(w, per_row=False)
+    del w
+    wdq = o.dequant(*q, per_row=False)
+    rows = 16
+    xb = o.bf16_to_f64(act_bf16(cfg["x_seed"], rows, cfg["K"]))
+    t_lin = _clock(lambda: o.linear_f64(xb, wdq), min_s=1.0, max_reps=3)
+    per["prefill"] = {"quantize_weight_s": round(t_q, 4),
+                      "linear_s_per_row": round(t_lin / rows, 5),
+                      "linear_s_full_estimate": round(t_lin / rows * cfg["M"], 2),
+                      "sample": f"linear on {rows} of {cfg['M']} rows (time per row scaled to all)"}
+    del wdq
+    # W4A4: activation quantize per row and the W4A4 linear
+    cfg = WORKLOADS["w4a4"]
+    w = weight_f32(cfg["w_seed"], cfg["N"], cfg["K"])
+    qw = o.quantize(w, per_row=False)
+    wdq = o.dequant(*qw, per_row=False)
+    rec = {}
+    for M in cfg["Ms"]:
+        xb = act_bf16(cfg["x_seed_base"] + M, M, cfg["K"])
+        t_qa = _clock(lambda: o.quantize_bf16(xb, per_row=True), min_s=0.2)
+        xq = o.quantize_bf16(xb, per_row=True)
+        m_s = min(M, 16)
+        t_l = _clock(lambda: o.linear_w4a4(xq[0][:m_s], xq[1][:m_s], xq[2][:m_s], *qw, wdq=wdq),
+                     min_s=0.3)
+        rec[str(M)] = {"quantize_act_s": round(t_qa, 6), "linear_s_per_row": round(t_l / m_s, 6),
+                       "sample": "full" if m_s == M else f"linear on {m_s} of {M} rows"}
+    per["w4a4"] = rec
+    # MoE decode layer: the oracle's stages on the 16 tokens (each routed expert
+    # dequantized once); expert weights quantized for the routed experts only
+    cfg = WORKLOADS["moe_decode"]
+    E, T, k = cfg["E"], cfg["T"], cfg["top_k"]
+    ids, rw = moe_routes(cfg["route_seed"], T, E, k)
+    used = sorted(set(int(e) for e in np.unique(ids)))
+    shape = (cfg["N_gu"], cfg["K_gu"], cfg["N_d"], cfg["K_d"])
+    gq, dq = {}, {}
     t0 = time.perf_counter()
-    reps = 0
-    while True:
-        wdq = o.dequant(oc, os_, ot, per_row=False)
-        for M in cfg["Ms"]:
-            o.linear_f64(o.bf16_to_f64(xs[M]), wdq)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= 12.0 or reps >= 2000:
-            break
-    per_step = el / reps
+    for e in used:
+        gu, dn = moe_expert_weights(cfg["w_seed"], e, *shape)
+        gq[e] = o.quantize(gu, per_row=False)
+        dq[e] = o.quantize(dn, per_row=False)
+    t_q = time.perf_counter() - t0
+
+    def stack(qs, i, shp, dt):
+        out = np.zeros((E,) + shp, dt)
+        for e, qq in qs.items():
+            out[e] = qq[i] if i < 2 else qq[2][0]
+        return out
+    gc = stack(gq, 0, (cfg["N_gu"], cfg["K_gu"] // 2), np.uint8)
+    gs = stack(gq, 1, (cfg["N_gu"], cfg["K_gu"] // 16), np.uint8)
+    gt = np.array([gq[e][2][0] if e in gq else 0.0 for e in range(E)], np.float32)
+    dc = stack(dq, 0, (cfg["N_d"], cfg["K_d"] // 2), np.uint8)
+    ds = stack(dq, 1, (cfg["N_d"], cfg["K_d"] // 16), np.uint8)
+    dt = np.array([dq[e][2][0] if e in dq else 0.0 for e in range(E)], np.float32)
+    xb = act_bf16(cfg["x_seed"], T, cfg["K_gu"])
+
+    def layer():
+        h, _ = o.moe_gate_up(xb, ids, gc, gs, gt)
+        a = o.bf16_round_array(o.swiglu(h))
+        o.moe_down_combine(a, ids, rw, dc, ds, dt)
+    t_layer = _clock(layer, min_s=1.0, max_reps=3)
+    per["moe_decode"] = {"quantize_weights_s": round(t_q, 3), "layer_s": round(t_layer, 4),
+                         "sample": f"full layer; weights quantized for the {len(used)} routed experts"}
     return {"value": round(decode["step_bytes"] / per_step / 1e9, 3), "unit": "GB/s",
-            "cores": o.num_threads(), "kind": "oracle",
-            "sample": f"full decode sweep (dequantize W 12288x4096, float64 linear for M=1,2,4,8,16) x{reps}, "
-                      f"{per_step:.2f} s per sweep on {o.num_threads()} OpenMP threads ({os.cpu_count()} host CPUs visible)"}
+            "cores": cores, "kind": "oracle", "cpu_model": cpu_model(),
+            "sample": f"full decode sweep: dequantize the 12288x4096 weight once, then the "
+                      f"float64 linear for M=1,2,4,8,16 ({per_step:.3f} s per sweep) on {cores} "
+                      f"OpenMP threads ({os.cpu_count()} host CPUs visible)",
+            "per_config": per}
 
 
 def main():
@@ -599,6 +756,12 @@ def main():
     ap.add_argument("--only", choices=["all", "decode", "single", "prefill", "w4a4", "moe",
                                        "moe_prefill"],
                     default="all", help="run the decode sweep plus one other workload (all: every one)")
+    ap.add_argument("--legs", default=None,
+                    help="comma-separated workloads to run besides the decode sweep "
+                         "(single, prefill, w4a4, moe, moe_prefill); overrides --only")
+    ap.add_argument("--no-decode", action="store_true",
+                    help="skip the decode sweep (profiling runs of other workloads; the line "
+                         "then has no headline value)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--copy-probe", action="store_true", help="also time a 1 GiB device copy")
     ap.add_argument("--summarize-rocprof", metavar="DIR",
@@ -620,6 +783,12 @@ def main():
     torch.cuda.set_device(dev)
     nv.load_library()
 
+    legs = set(args.legs.split(",")) if args.legs else None
+    if args.no_decode:
+        rec = {"metric": METRIC, "value": None, "note": "decode sweep skipped (--no-decode)"}
+        run_legs(nv, dev, args, legs, rec)
+        print(json.dumps(rec), flush=True)
+        return
     log("decode sweep ...")
     d = bench_decode_sweep(nv, dev, args.steps, args.warmup)
     value = d["step_bytes"] / (d["ms_step"] * 1e-3) / 1e9
@@ -630,6 +799,7 @@ def main():
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": d["timed_steps"],
+        "steps_requested": args.steps,  # timed in whole replays of the sweep graph
         "warmup": args.warmup,
         "ms_per_step": round(d["ms_step"], 5),
         "higher_is_better": True,
@@ -653,8 +823,19 @@ def main():
         "per_m": d["per_m"],
         "read_probe": d["probe"],
     }
+    run_legs(nv, dev, args, legs, rec)
+    if args.copy_probe or (args.only == "all" and legs is None):
+        rec["hbm_copy_GBps"] = hbm_copy_probe(dev)
+    if not args.no_cpu:
+        log("cpu oracle baseline ...")
+        rec["cpu_baseline"] = cpu_baseline(d)
+    print(json.dumps(rec), flush=True)
+
+
+def run_legs(nv, dev, args, legs, rec):
+    """The workloads besides the decode sweep, each under its own key of rec."""
     def want(name):
-        return args.only in ("all", name)
+        return name in legs if legs is not None else args.only in ("all", name)
     if want("single"):
         log("single linear ...")
         rec["single_linear"] = bench_single(nv, dev)
@@ -671,12 +852,8 @@ def main():
     if want("moe_prefill"):
         log("moe prefill ...")
         rec["moe_prefill"] = bench_moe_prefill(nv, dev)
-    if args.copy_probe or args.only == "all":
+    if args.no_decode and args.copy_probe:
         rec["hbm_copy_GBps"] = hbm_copy_probe(dev)
-    if not args.no_cpu:
-        log("cpu oracle baseline ...")
-        rec["cpu_baseline"] = cpu_baseline(d)
-    print(json.dumps(rec), flush=True)
 
 
 if __name__ == "__main__":

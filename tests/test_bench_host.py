@@ -54,6 +54,26 @@ def test_summarize_rocprof_calibrates_and_sums_traffic(tmp_path, capsys):
     assert line and int(line[0].split(":")[1]) == int(want)
 
 
+def test_summarize_rocprof_dispatch_percentiles(tmp_path, capsys):
+    """Median, p10 and p90 of the dispatch durations in a kernel trace, per kernel."""
+    rows = [["k_a", 1000 * i, 1000 * i + 1000 * (i + 1)] for i in range(10)]  # 1..10 us
+    rows += [["k_b", 0, 5000]] * 3
+    _write_csv(tmp_path / "run_kernel_trace.csv", ["Kernel_Name", "Start_Timestamp", "End_Timestamp"],
+               rows)
+    bench.summarize_rocprof(str(tmp_path), calib_bytes=1 << 30)
+    out = capsys.readouterr().out
+    line_a = [ln for ln in out.splitlines() if ln.strip().startswith("k_a")][0].split()
+    assert line_a[2] == "10" and float(line_a[4]) == 5.5
+    assert abs(float(line_a[6]) - 1.9) < 1e-9 and abs(float(line_a[8]) - 9.1) < 1e-9
+    line_b = [ln for ln in out.splitlines() if ln.strip().startswith("k_b")][0].split()
+    assert line_b[2] == "3" and float(line_b[4]) == 5.0
+
+
+def test_spread_percentiles():
+    sp = bench.spread([1.0, 2.0, 3.0, 4.0, 5.0])
+    assert sp == {"us_med": 3.0, "us_p10": 1.4, "us_p90": 4.6, "replays": 5}
+
+
 def test_committed_counter_summary_matches_the_kernel_sources():
     """The FETCH/WRITE summary under profiles/ names the hash of the streaming kernel's
     sources it was taken on; it must be the current one, so that the bench's roofline
