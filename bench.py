@@ -380,9 +380,9 @@ def bench_w4a4(nv, dev):
 
 
 def bench_w4a4_in_call(nv, dev):
-    """W4A4 for decode-sized batches two ways on the W4A4 weight (K = N = 4096): the
-    quantizer launch followed by the NVFP4-activation linear, and the one-launch form that
-    quantizes each row inside the weight-streaming kernel (bit for bit the same result)."""
+    """W4A4 for one row two ways on the W4A4 weight (K = N = 4096): the quantizer launch
+    followed by the NVFP4-activation linear, and the one-launch form that quantizes the
+    row inside the weight-streaming kernel (bit for bit the same result)."""
     from synth import WORKLOADS, act_bf16, weight_f32
     cfg = WORKLOADS["w4a4"]
     N, K = cfg["N"], cfg["K"]
@@ -391,7 +391,7 @@ def bench_w4a4_in_call(nv, dev):
     W = copies(c, s, R)
     out = {}
     timer = Timer()
-    for M in (1, 2, 4):
+    for M in (1,):
         x = to_bf16(act_bf16(cfg["x_seed_base"] + M, M, K), dev)
         xc, xs_, xt = nv.quantize_act(x)
         y = torch.empty((M, N), dtype=torch.float32, device=dev)

@@ -98,14 +98,15 @@ const char* nvfp4_status_string(int32_t status);
  *   them with NVFP4_TS_PER_ROW); ldx is ignored. Both operands are decoded exactly;
  *   y[m][n] = acc * (x_ts[m] * ts). (W4A16 and W4A4 variants: issue #565 section 4,
  *   PRs #682 and #687.)
- * W4A4 with in-call quantization (act_kind = NVFP4_ACT_BF16_QUANTIZE), for decode-sized
- *   batches, M <= 4 and K <= 8192: x is BF16 as for W4A16; each row is quantized inside
- *   the call by the per-row rule of nvfp4_quantize_act (NVFP4_TS_PER_ROW) and multiplied
- *   as W4A4, bit for bit the result of nvfp4_quantize_act followed by the NVFP4_ACT_NVFP4
- *   call, in one launch and with no stored codes (the activation quantization folded
- *   into the kernel that uses it, as the pages plan for their prompt kernels: issue #565
- *   section 4, "Remaining Round 1 items"). x_scales and x_ts must be NULL. A row holding
- *   a NaN or Inf gives NaN outputs in that row.
+ * W4A4 with in-call quantization (act_kind = NVFP4_ACT_BF16_QUANTIZE), for one row, M = 1
+ *   and K <= 8192: x is BF16 as for W4A16; the row is quantized inside the call by the
+ *   per-row rule of nvfp4_quantize_act (NVFP4_TS_PER_ROW) and multiplied as W4A4, bit for
+ *   bit the result of nvfp4_quantize_act followed by the NVFP4_ACT_NVFP4 call, in one
+ *   launch and with no stored codes (the activation quantization folded into the kernel
+ *   that uses it, as the pages plan for their prompt kernels: issue #565 section 4,
+ *   "Remaining Round 1 items"). Every workgroup quantizes the whole row, so for more rows
+ *   the two calls are faster; they are refused here. x_scales and x_ts must be NULL. A row
+ *   holding a NaN or Inf gives NaN outputs.
  * Weight: w_codes [N][K/2] (16-byte aligned), w_scales [N][K/16] (2-byte aligned),
  *   w_ts [1]. y [M][ldy] fp32, ldy >= N. K % 32 == 0.
  * M <= 16 streams the weight once for all rows (each weight byte is read once for all
@@ -114,7 +115,7 @@ const char* nvfp4_status_string(int32_t status);
  * flags: 0 or NVFP4_F_CHECK (see "Check mode" above); faults: a device word or NULL
  *   (NULL only without NVFP4_F_CHECK); with NVFP4_ACT_BF16_QUANTIZE a non-finite row
  *   value is reported as NVFP4_FAULT_NONFINITE in check mode.
- * Errors: NVFP4_ERR_NULL, _SHAPE (also M > 4 or K > 8192 with NVFP4_ACT_BF16_QUANTIZE),
+ * Errors: NVFP4_ERR_NULL, _SHAPE (also M != 1 or K > 8192 with NVFP4_ACT_BF16_QUANTIZE),
  *   _ALIGN, _ARG (unknown act_kind or flag bit), _LAUNCH. */
 nvfp4_status nvfp4_linear(int32_t act_kind, const void* x, const uint8_t* x_scales,
                           const float* x_ts, int64_t ldx, int64_t M, int64_t N, int64_t K,

@@ -100,7 +100,7 @@ def linear(x, w_codes, w_scales, w_ts, *, x_scales=None, x_ts=None, out=None,
            quantize_x=False, check=False, faults=None):
     """y = x W^T for an NVFP4 weight (codes [N][K/2] u8, scales [N][K/16] u8, ts [1] f32).
     x is BF16 [M][K] (W4A16), or NVFP4 codes [M][K/2] u8 with x_scales/x_ts (W4A4).
-    quantize_x=True (BF16 x, M <= 4): W4A4 with x quantized per row inside the call.
+    quantize_x=True (BF16 x, one row): W4A4 with x quantized inside the call.
     check=True scans the operands first and ORs FAULT_* bits into `faults` (a device
     int32 word, required then)."""
     N = w_codes.shape[0]

@@ -160,7 +160,7 @@ nvfp4_status nvfp4_linear(int32_t act_kind, const void* x, const uint8_t* x_scal
   if ((st = check_k(K)) != NVFP4_OK) return st;
   if (M <= 0 || N <= 0 || M > kMaxDim || N > kMaxDim) return NVFP4_ERR_SHAPE;
   if ((st = check_act(act_kind, x, x_scales, x_ts, ldx, K)) != NVFP4_OK) return st;
-  if (act_kind == NVFP4_ACT_BF16_QUANTIZE && (M > 4 || K > 8192)) return NVFP4_ERR_SHAPE;
+  if (act_kind == NVFP4_ACT_BF16_QUANTIZE && (M != 1 || K > 8192)) return NVFP4_ERR_SHAPE;
   if ((st = check_weight(w_codes, w_scales, w_ts)) != NVFP4_OK) return st;
   if (!y) return NVFP4_ERR_NULL;
   if (ldy < N || ldy > kMaxDim) return NVFP4_ERR_SHAPE;

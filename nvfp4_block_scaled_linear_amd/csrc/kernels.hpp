@@ -26,6 +26,8 @@ struct StreamArgs {
   int64_t x_rows;   // rows in x (bounds the activation reads)
   int32_t M;        // dense: number of rows (<= 16); grouped: rows per expert pass hint
   int32_t apply_ts; // multiply the accumulator by the weight's tensor scale
+  int32_t rsplit;   // dense: workgroups sharing one weight tile, each taking its own sets
+                    // of four rows (0 or 1: one workgroup takes every row)
   // grouped form (NULL for dense)
   const int32_t* offsets;    // [E+1] route ranges per expert in `sorted`
   const int32_t* sorted;     // route ids grouped by expert
@@ -40,9 +42,10 @@ struct StreamArgs {
 
 hipError_t launch_stream(const StreamArgs& a, int act_kind, bool grouped, int max_active,
                          hipStream_t stream);
-// the same with an explicit tile choice: tn 16-row tiles per workgroup, W waves splitting K
+// the same with an explicit launch shape: tn 16-row tiles per workgroup, W waves splitting
+// K, rsets sets of four activation rows per workgroup (dense; 0: all rows in one)
 hipError_t launch_stream_cfg(const StreamArgs& a, int act_kind, bool grouped, int max_active,
-                             int tn, int W, hipStream_t stream);
+                             int tn, int W, int rsets, hipStream_t stream);
 
 struct GemmArgs {
   const void* x;

@@ -570,13 +570,23 @@ template <int TN, int R, int ACT, bool SLDS>
 __global__ __launch_bounds__(256) void stream_dense(StreamArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   float* red = reinterpret_cast<float*>(lds + lds_red_offset(TN, R, blockDim.x >> 6, a.K, SLDS, ACT));
-  const int64_t n0 = (int64_t)blockIdx.x * 16 * TN;
+  // Row split: S workgroups share a weight tile, split s taking activation rows
+  // [4R s, 4R (s + 1)). A row's arithmetic does not depend on the other rows of its
+  // workgroup, so the split changes no result. The S splits of a tile are S apart in
+  // steps of eight workgroups, which puts them on the same XCD (workgroup b runs on XCD
+  // b % 8) and lets all but one read the tile from that XCD's L2.
+  const int S = a.rsplit > 1 ? a.rsplit : 1;
+  const int64_t bid = blockIdx.x;
+  const int64_t tile = S == 1 ? bid : (bid % 8) + 8 * (bid / (8 * S));
+  const int m0 = S == 1 ? 0 : (int)((bid / 8) % S) * 4 * R;
+  const int64_t n0 = tile * 16 * TN;
+  if (n0 >= a.N) return;  // padding of the split grid to whole groups of eight (uniform)
   const int i = (threadIdx.x >> 4) & 3;  // the x row this lane loads within a set of four
   RowMap rm;
 #pragma unroll
   for (int r = 0; r < 4; r++) {
-    const int m = 4 * r + i;
-    const bool ok = m < a.M;
+    const int m = m0 + 4 * r + i;
+    const bool ok = r < R && m < a.M;
     if (ACT == 0) {
       rm.off[r] = ok ? (uint32_t)(m * a.ldx * 2) : kOOB;
       rm.soff[r] = kOOB;
@@ -601,7 +611,8 @@ __global__ __launch_bounds__(256) void stream_dense(StreamArgs a) {
 #pragma unroll
     for (int m = 0; m < 4; m++) ts_q[m] = tq[m];
   }
-  reduce_store<TN, R>(acc, red, n0, [&](int m, int64_t n, float s) {
+  reduce_store<TN, R>(acc, red, n0, [&](int mr, int64_t n, float s) {
+    const int m = m0 + mr;
     if (m < a.M && n < a.N) {
       const float f = (ACT == 0) ? ts : (ACT == 2 ? ts_q[m & 3] * ts : a.x_ts[m] * ts);
       a.y[(int64_t)m * a.ldy + n] = s * f;
@@ -740,7 +751,8 @@ hipError_t launch_grouped_swiglu(const StreamArgs& a, int max_active, int W, boo
 template <int TN, int R, int ACT>
 hipError_t launch_dense(const StreamArgs& a, int W, bool slds, hipStream_t stream) {
   const size_t lds = lds_bytes(TN, R, W, a.K, slds, ACT);
-  const int64_t groups = (a.N + 16 * TN - 1) / (16 * TN);
+  const int64_t tiles = (a.N + 16 * TN - 1) / (16 * TN);
+  const int64_t groups = a.rsplit > 1 ? (tiles + 7) / 8 * 8 * a.rsplit : tiles;
   if (slds)
     hipLaunchKernelGGL((stream_dense<TN, R, ACT, true>), dim3((uint32_t)groups), dim3(64 * W), lds,
                        stream, a);
@@ -814,8 +826,9 @@ int pick_tn(int64_t N) {
 
 }  // namespace
 
-hipError_t launch_stream_cfg(const StreamArgs& a, int act_kind, bool grouped, int max_active,
-                             int tn, int W, hipStream_t stream) {
+hipError_t launch_stream_cfg(const StreamArgs& a_in, int act_kind, bool grouped, int max_active,
+                             int tn, int W, int rsets, hipStream_t stream) {
+  StreamArgs a = a_in;
   if (W < 1 || W > 4) return hipErrorInvalidValue;
   // activation kinds: 0 BF16, 1 NVFP4 (both forms), 2 BF16 quantized in the call (dense
   // only); anything else is refused rather than taken by one of the templates
@@ -845,7 +858,13 @@ hipError_t launch_stream_cfg(const StreamArgs& a, int act_kind, bool grouped, in
                                     : launch_grouped<4, 1>(a, max_active, W, slds, stream);
     }
   }
-  const int R = (a.M + 3) / 4;
+  const int sets = (a.M + 3) / 4;
+  // default: one workgroup per tile takes every row, except on launches of at most 256
+  // tiles (one workgroup per CU) with three or more row sets, where two workgroups share a
+  // tile (W4A4 M=16, N=4096: 8.0 against 8.8 us); the split changes no result
+  if (rsets <= 0 && tn == 1 && (a.N + 15) / 16 <= 256 && sets >= 3) rsets = (sets + 1) / 2;
+  const int R = rsets > 0 && rsets < sets ? rsets : sets;
+  a.rsplit = (sets + R - 1) / R;
   if (act_kind == 2) {  // in-call quantized activations: one row set, 16-row tiles
     if (R != 1 || tn != 1 || W != waves_for_k(a.K)) return hipErrorInvalidValue;
     if (a.M * (a.K >> 4) > (int64_t)kQBlocks * 64 * W) return hipErrorInvalidValue;
@@ -862,7 +881,7 @@ hipError_t launch_stream(const StreamArgs& a, int act_kind, bool grouped, int ma
   // N=12288: 10.2 us against 10.6 us with 48-row tiles); more row sets: wider tiles share
   // each activation load among more weight rows
   const int tn = (grouped || a.M <= 8) ? 1 : pick_tn(a.N);
-  return launch_stream_cfg(a, act_kind, grouped, max_active, tn, W, stream);
+  return launch_stream_cfg(a, act_kind, grouped, max_active, tn, W, 0, stream);
 }
 
 }  // namespace nvfp4

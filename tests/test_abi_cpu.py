@@ -69,7 +69,7 @@ def lin(lib, act=0, x=P, xs=None, xt=None, ldx=4096, M=4, N=128, K=4096, wc=P, w
     (dict(wc=P + 4), ERR_ALIGN), (dict(ws=P + 1), ERR_ALIGN), (dict(wt=P + 2), ERR_ALIGN),
     (dict(y=None), ERR_NULL), (dict(ldy=100), ERR_SHAPE), (dict(y=P + 2), ERR_ALIGN),
     # W4A4 with in-call quantization: BF16 x, at most four rows, K <= 8192, no x scales
-    (dict(act=2, M=5), ERR_SHAPE), (dict(act=2, K=8224, ldx=8224), ERR_SHAPE),
+    (dict(act=2, M=5), ERR_SHAPE), (dict(act=2, M=2), ERR_SHAPE), (dict(act=2, M=1, K=8224, ldx=8224), ERR_SHAPE),
     (dict(act=2, xs=P), ERR_ARG), (dict(act=2, xt=P), ERR_ARG), (dict(act=2, ldx=4100), ERR_ALIGN),
     (dict(act=3), ERR_ARG),
     # check mode: a known flag bit only, and a fault word to report into

@@ -115,6 +115,42 @@ def test_quantizer_weights_bit_exact(dev, o, name):
     quantize_both(o, w, dev, per_tensor=True)
 
 
+def _decision_point_rows():
+    """fp32 rows whose blocks have divisor e4m3(s) * ts == 1 exactly: the row amax 2688
+    (block 0) gives ts = 1, and every other block holds a 6, so ratio = 1 and s = 1.0
+    (0x38). The other 15 values of such a block are then the quotients q themselves:
+    every fp32 within 64 ulps of each E2M1 decision point (0.25, 0.75, 1.25, 1.75, 2.5,
+    3.5, 5) and of 6, of both signs, then +-0 and values just above 0."""
+    vals = []
+    for t in (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0):
+        u = np.array([t], np.float32).view(np.uint32)[0]
+        vals.append((np.arange(-64, 65, dtype=np.int64) + int(u)).astype(np.uint32).view(np.float32))
+    v = np.concatenate(vals)
+    v = v[np.abs(v) <= 6.0]
+    v = np.concatenate([v, -v, np.array([0.0, -0.0, 1e-30, -1e-30, 2 ** -149, -(2 ** -149)], np.float32)])
+    nblk = (len(v) + 14) // 15
+    v = np.concatenate([v, np.zeros(nblk * 15 - len(v), np.float32)]).reshape(nblk, 15)
+    blocks = np.concatenate([np.full((nblk, 1), 6.0, np.float32), v], axis=1)
+    head = np.zeros((1, 16), np.float32)
+    head[0, 0] = 2688.0
+    flat = np.concatenate([head, blocks]).reshape(-1)
+    K = 256
+    flat = np.concatenate([flat, np.zeros((-len(flat)) % K, np.float32)])
+    rows = flat.reshape(-1, K)
+    rows[:, 0] = 2688.0  # each row's amax (per-row ts = 1)
+    return np.ascontiguousarray(rows)
+
+
+@pytest.mark.parametrize("per_tensor", [False, True])
+def test_quantizer_every_e2m1_decision_point(dev, o, per_tensor):
+    """The device's E2M1 encoding (the hardware FP4 conversion at scale 1.0) against the
+    oracle's nearest-value encoder on quotients packed densely around every decision point,
+    through nvfp4_quantize_act: codes, scales and ts bit for bit."""
+    w = _decision_point_rows()
+    _say(f"quantize decision points {w.shape} per_tensor={per_tensor}")
+    quantize_both(o, w, dev, per_tensor=per_tensor)
+
+
 def test_quantizer_flags_nonfinite(dev):
     faults = torch.zeros(1, dtype=torch.int32, device=dev)
     for bad in (np.nan, np.inf):
@@ -440,18 +476,24 @@ def test_read_probe_reads_every_byte(dev):
             assert sink.cpu().view(torch.int32).numpy().view(np.uint32)[0] == mark, (u, where)
 
 
-# W4A4 with the activation quantization inside the call (decode-sized: M <= 4)
+def _in_call(xd, c, s, t):
+    """W4A4 with in-call quantization, one row per call (the form takes one row)."""
+    return torch.cat([nv.linear(xd[m:m + 1], c, s, t, quantize_x=True) for m in range(xd.shape[0])])
+
+
+# W4A4 with the activation quantization inside the call (one row per call)
 @pytest.mark.parametrize("M,N,K,pad", [(1, 4096, 4096, 0), (4, 4096, 4096, 0), (3, 1000, 4128, 24),
                                        (4, 777, 544, 8), (2, 12288, 8192, 0), (4, 64, 32, 0)])
 def test_w4a4_in_call_quantization(dev, o, M, N, K, pad):
-    """Bit for bit the two-call W4A4 (quantize_act, then the NVFP4-activation linear), and
-    within the bound of the oracle's W4A4 on the oracle's own quantization."""
+    """Each row bit for bit the two-call W4A4 (quantize_act, then the NVFP4-activation
+    linear, on all M rows at once), and within the bound of the oracle's W4A4 on the
+    oracle's own quantization."""
     _say(f"w4a4 in-call quantization M={M} N={N} K={K}")
     w = weight_f32(40 + M, N, K)
     (c, s, t), oq = quantize_both(o, w, dev)
     xb = act_bf16(41 + M, M, K + pad)
     xd = to_dev_bf16(xb, dev)[:, :K]
-    y = nv.linear(xd, c, s, t, quantize_x=True)
+    y = _in_call(xd, c, s, t)
     xc, xs, xt = nv.quantize_act(xd)
     y2 = nv.linear(xc, c, s, t, x_scales=xs, x_ts=xt)
     assert torch.equal(y, y2)
@@ -474,22 +516,22 @@ def test_w4a4_in_call_quantization_ties(dev, o):
     rows[2] *= np.float32(1.0 - 2.0 ** -8)  # one BF16 step below
     rows[3, ::5] = 0.0
     xd = torch.from_numpy(rows).to(dev).to(torch.bfloat16)
-    y = nv.linear(xd, c, s, t, quantize_x=True)
+    y = _in_call(xd, c, s, t)
     xc, xs, xt = nv.quantize_act(xd)
     assert torch.equal(y, nv.linear(xc, c, s, t, x_scales=xs, x_ts=xt))
 
 
 def test_w4a4_in_call_quantization_nonfinite_row(dev, o):
-    """A NaN or Inf activation makes its row's outputs NaN; the other rows are unaffected."""
+    """A NaN or Inf activation makes its row's outputs NaN; the other rows' calls are unaffected."""
     M, N, K = 4, 512, 1024
     w = weight_f32(45, N, K)
     (c, s, t), _ = quantize_both(o, w, dev)
     xd = to_dev_bf16(act_bf16(46, M, K), dev)
-    ref = nv.linear(xd, c, s, t, quantize_x=True).clone()
+    ref = _in_call(xd, c, s, t).clone()
     for bad in (float("nan"), float("inf")):
         xbad = xd.clone()
         xbad[1, 77] = bad
-        y = nv.linear(xbad, c, s, t, quantize_x=True)
+        y = _in_call(xbad, c, s, t)
         assert torch.isnan(y[1]).all()
         for m in (0, 2, 3):
             assert torch.equal(y[m], ref[m])
