@@ -262,6 +262,63 @@ def bench_decode_sweep(nv, dev, steps, warmup):
                 timed_steps=timed_steps, per_m=per_m, launches_per_step=len(Ms), probe=probe)
 
 
+def bench_decode_prefetch(nv, dev):
+    """A chain of decode launches over distinct weights (the sweep's K=4096, N=12288 weight
+    in 40 copies, M cycling through 1, 2, 4, 8, 16), as consecutive layers of a decode step
+    run: without prefetch, and with each next layer's weight (codes and scales) read into
+    the caches by nvfp4_prefetch on a second stream while the current layer runs (forked
+    before it, joined before the next layer). Per-layer time over the chain."""
+    from synth import WORKLOADS, act_bf16, weight_f32
+    cfg = WORKLOADS["decode_sweep"]
+    N, K, Ms = cfg["N"], cfg["K"], cfg["Ms"]
+    c, s, t = quantize_weight(nv, weight_f32(cfg["w_seed"], N, K), dev)
+    R = len(Ms) * math.ceil(max(len(Ms), math.ceil(ROTATE_BYTES / weight_bytes(N, K))) / len(Ms))
+    W = copies(c, s, R)
+    xs = {M: to_bf16(act_bf16(cfg["x_seed_base"] + M, M, K), dev) for M in Ms}
+    ys = {M: torch.empty((M, N), dtype=torch.float32, device=dev) for M in Ms}
+    side = torch.cuda.Stream()
+    ref = {M: nv.linear(xs[M], c, s, t).clone() for M in Ms}
+
+    def chain(workgroups):
+        for j in range(R):
+            M = Ms[j % len(Ms)]
+            if workgroups:
+                nxt = W[(j + 1) % R]
+                side.wait_stream(torch.cuda.current_stream())
+                with torch.cuda.stream(side):
+                    nv.prefetch(nxt[0], workgroups)
+                    nv.prefetch(nxt[1], workgroups)
+            nv.linear(xs[M], W[j][0], W[j][1], t, out=ys[M])
+            if workgroups:
+                torch.cuda.current_stream().wait_stream(side)
+    out = {"layers_per_replay": R, "bytes_per_layer_avg": sum(linear_bytes(M, N, K) for M in Ms) // len(Ms)}
+    for wg in (0, 128, 256, 512):
+        g = capture(lambda: chain(wg))
+        g.replay()
+        torch.cuda.synchronize()
+        for M in Ms:
+            assert torch.equal(ys[M], ref[M]), f"prefetch changed a result at M={M}"
+        warm_until(g.replay, 0.05)
+        ms, sp = timed(g, 25, R)
+        key = "no_prefetch" if wg == 0 else f"prefetch_wg{wg}"
+        out[key] = {"us_per_layer": round(ms * 1e3, 3), **sp,
+                    "GBps": round(out["bytes_per_layer_avg"] / (ms * 1e-3) / 1e9, 1)}
+        del g
+    # eager launches (host-enqueued, no graph), where the host leaves gaps between layers
+    for wg in (0, 256):
+        chain(wg)
+        torch.cuda.synchronize()
+        samp = []
+        for _ in range(5):
+            t0 = time.perf_counter()
+            chain(wg)
+            torch.cuda.synchronize()
+            samp.append((time.perf_counter() - t0) / R * 1e6)
+        key = "eager_no_prefetch" if wg == 0 else f"eager_prefetch_wg{wg}"
+        out[key] = {"us_per_layer": round(float(np.median(samp)), 3)}
+    return out
+
+
 def read_probe_roof(nv, dev, nbytes, timer):
     """The measured single-launch read roof: the library's plain streaming-read kernel over
     buffers of the M=1 launch's algorithmic size, rotated over >= 1 GiB like the weights,
@@ -754,11 +811,11 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--only", choices=["all", "decode", "single", "prefill", "w4a4", "moe",
-                                       "moe_prefill"],
+                                       "moe_prefill", "prefetch"],
                     default="all", help="run the decode sweep plus one other workload (all: every one)")
     ap.add_argument("--legs", default=None,
                     help="comma-separated workloads to run besides the decode sweep "
-                         "(single, prefill, w4a4, moe, moe_prefill); overrides --only")
+                         "(single, prefill, w4a4, moe, moe_prefill, prefetch); overrides --only")
     ap.add_argument("--no-decode", action="store_true",
                     help="skip the decode sweep (profiling runs of other workloads; the line "
                          "then has no headline value)")
@@ -852,6 +909,9 @@ def run_legs(nv, dev, args, legs, rec):
     if want("moe_prefill"):
         log("moe prefill ...")
         rec["moe_prefill"] = bench_moe_prefill(nv, dev)
+    if want("prefetch"):
+        log("decode chain with next-weight prefetch ...")
+        rec["decode_prefetch"] = bench_decode_prefetch(nv, dev)
     if args.no_decode and args.copy_probe:
         rec["hbm_copy_GBps"] = hbm_copy_probe(dev)
 

@@ -232,6 +232,26 @@ nvfp4_status nvfp4_grouped_linear_noalloc(int32_t act_kind, const void* x,
                                           int32_t out_mode, void* y, uint32_t flags,
                                           uint32_t* faults, void* stream);
 
+/* nvfp4_prefetch — next-weight prefetch: reads [buf, buf + bytes) on `stream` and discards
+ * the values, so that the bytes are in the caches (L2 and the 256 MB Infinity Cache) when a
+ * later call reads them. For a sequence of layers, issue it for layer i + 1's weight codes
+ * and scales on a second stream (of the same priority) while layer i runs, and have layer
+ * i + 1 wait for it: each weight byte then leaves HBM once, ahead of the call that needs
+ * it, so that call does not wait for the ramp and tail of its own HBM stream (the pages
+ * prefetch weight rows into L2 ahead of the gemv calls that read them: issue #565
+ * section 4, "Remaining Round 1 items"). Nothing is written; results of other calls do
+ * not change.
+ * Measured on MI355X for the 28 MB decode weights: it does not pay while the previous
+ * layer runs, since the HBM read of the next weight and the running call share the L2 and
+ * the fabric (a chain of graph-replayed decode launches takes 18.4 us per layer with it
+ * against 9.8 us without). Its use is a weight read while the GPU is otherwise idle, for
+ * instance the first layer's during host-side work between decode steps.
+ * buf: device memory, 16-byte aligned; bytes: 16 .. 2^31 - 16, a multiple of 16.
+ * workgroups: the most workgroups the read may use (1 .. 8192; 0: 512), which bounds its
+ *   share of the chip while it overlaps another call.
+ * Errors: NVFP4_ERR_NULL, _SHAPE, _ALIGN, _ARG, _LAUNCH. */
+nvfp4_status nvfp4_prefetch(const void* buf, int64_t bytes, int32_t workgroups, void* stream);
+
 /* nvfp4_read_probe — measurement support, not part of the layer: one plain streaming read
  * of `bytes` bytes at `buf` in one launch, the measured single-launch read roof that the
  * weight-streaming calls are compared against (the pages set their decode paths beside a

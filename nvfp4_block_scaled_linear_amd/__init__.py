@@ -23,6 +23,7 @@ from ._binding import (  # noqa: F401
     grouped_linear_noalloc,
     grouped_workspace_size,
     linear,
+    prefetch,
     load_library,
     quantize_act,
     read_probe,

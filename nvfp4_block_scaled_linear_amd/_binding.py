@@ -22,7 +22,7 @@ FAULT_NONFINITE, FAULT_BAD_ROUTE, FAULT_NAN_SCALE = 1, 2, 4
 F_CHECK = 1
 
 EXPORTS = ("nvfp4_status_string", "nvfp4_linear", "nvfp4_quantize_act", "nvfp4_grouped_linear",
-           "nvfp4_grouped_linear_noalloc", "nvfp4_read_probe")
+           "nvfp4_grouped_linear_noalloc", "nvfp4_prefetch", "nvfp4_read_probe")
 NOALLOC_SCRATCH_BYTES = 16 << 20
 
 _lib = None
@@ -59,6 +59,8 @@ def load_library(path: str = LIB_PATH):
     lib.nvfp4_grouped_linear_noalloc.restype = i32
     lib.nvfp4_grouped_linear_noalloc.argtypes = [i32, vp, vp, vp, i64, i32, i64, i32, i64, i64,
                                                  i32, vp, vp, vp, vp, vp, i32, vp, u32, u32p, vp]
+    lib.nvfp4_prefetch.restype = i32
+    lib.nvfp4_prefetch.argtypes = [vp, i64, i32, vp]
     lib.nvfp4_read_probe.restype = i32
     lib.nvfp4_read_probe.argtypes = [vp, i64, i32, u32p, vp]
     _lib = lib
@@ -200,6 +202,15 @@ def grouped_linear_noalloc(x, w_codes, w_scales, w_ts, topk_ids, *, out, topk_w=
         F_CHECK if check else 0, _p(faults), _stream())
     _check(st, "nvfp4_grouped_linear_noalloc")
     return out
+
+
+def prefetch(buf, workgroups: int = 0, stream=None):
+    """Next-weight prefetch: read the bytes of `buf` (a contiguous device tensor) into the
+    caches on `stream` (default: the current stream), values discarded."""
+    nbytes = buf.numel() * buf.element_size()
+    s = ctypes.c_void_p(stream.cuda_stream) if stream is not None else _stream()
+    st = load_library().nvfp4_prefetch(_p(buf), nbytes, int(workgroups), s)
+    _check(st, "nvfp4_prefetch")
 
 
 def read_probe(buf, loads_per_thread: int, sink):

@@ -373,6 +373,15 @@ nvfp4_status nvfp4_grouped_linear_noalloc(int32_t act_kind, const void* x,
                               y, ws, &have, flags, faults, stream);
 }
 
+nvfp4_status nvfp4_prefetch(const void* buf, int64_t bytes, int32_t workgroups, void* stream) {
+  if (!buf) return NVFP4_ERR_NULL;
+  if (bytes < 16 || bytes > ((int64_t)1 << 31) - 16 || bytes % 16 != 0) return NVFP4_ERR_SHAPE;
+  if (!aligned(buf, 16)) return NVFP4_ERR_ALIGN;
+  if (workgroups < 0 || workgroups > 8192) return NVFP4_ERR_ARG;
+  return launch_status(launch_prefetch(buf, bytes, workgroups ? workgroups : 512,
+                                       static_cast<hipStream_t>(stream)));
+}
+
 nvfp4_status nvfp4_read_probe(const void* buf, int64_t bytes, int32_t loads_per_thread,
                               uint32_t* sink, void* stream) {
   if (!buf || !sink) return NVFP4_ERR_NULL;

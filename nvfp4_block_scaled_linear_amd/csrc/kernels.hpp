@@ -121,6 +121,10 @@ hipError_t launch_check_scales(const uint8_t* scales, int64_t bytes, const float
 hipError_t launch_check_bf16(const void* x, int64_t ld, int64_t rows, int64_t K,
                              uint32_t* faults, hipStream_t stream);
 
+// next-weight prefetch: a streaming read of [buf, buf + bytes), values discarded, on at most
+// `workgroups` workgroups
+hipError_t launch_prefetch(const void* buf, int64_t bytes, int workgroups, hipStream_t stream);
+
 // measurement support: one streaming read of `bytes` bytes (loads_per_thread 16-byte loads
 // per thread, 1/2/4/8/16)
 hipError_t launch_read_probe(const void* buf, int64_t bytes, int loads_per_thread, uint32_t* sink,

@@ -152,6 +152,15 @@ def test_read_probe_refusals(lib, args, status):
     assert lib.nvfp4_read_probe(*args, None) == status
 
 
+@pytest.mark.parametrize("args,status", [
+    ((None, 4096, 0), ERR_NULL), ((P, 0, 0), ERR_SHAPE), ((P, 4100, 0), ERR_SHAPE),
+    ((P, 1 << 31, 0), ERR_SHAPE), ((P + 8, 4096, 0), ERR_ALIGN), ((P, 4096, -1), ERR_ARG),
+    ((P, 4096, 9000), ERR_ARG),
+])
+def test_prefetch_refusals(lib, args, status):
+    assert lib.nvfp4_prefetch(*args, None) == status
+
+
 def test_binding_fails_loudly_without_library(tmp_path):
     from nvfp4_block_scaled_linear_amd import _binding
     saved = _binding._lib

@@ -190,3 +190,23 @@ def test_splitk_shape_with_offset_scale_views(dev, o):
     for ws_, xs_ in ((s, xsv), (sv, xs), (sv, xsv)):
         y4 = nv.linear(xc, c, ws_, t, x_scales=xs_, x_ts=xt).cpu().numpy()
         assert_within(y4, yr4, b4, "offset scales w4a4")
+
+
+def test_prefetch_reads_without_writing(dev, o):
+    """nvfp4_prefetch reads a buffer on a stream and changes nothing: the buffer's bytes
+    and a following linear on the prefetched weight are unchanged, for the smallest size,
+    a size that is not a whole number of its load rounds, and with each workgroup cap."""
+    N, K = 640, 1024
+    (c, s, t), oq = quantize_both(o, weight_f32(351, N, K), dev)
+    x = to_dev_bf16(act_bf16(352, 4, K), dev)
+    y0 = nv.linear(x, c, s, t)
+    c0, s0 = c.clone(), s.clone()
+    for wg in (0, 1, 7, 512):
+        nv.prefetch(c, wg)
+        nv.prefetch(s, wg)
+        nv.prefetch(c[:1, :16].contiguous(), wg)  # 16 bytes
+    torch.cuda.synchronize()
+    assert torch.equal(c, c0) and torch.equal(s, s0)
+    assert torch.equal(nv.linear(x, c, s, t), y0)
+    with pytest.raises(nv.NVFP4Error, match="ALIGN"):
+        nv.prefetch(c.view(-1)[8:8 + 4096])
