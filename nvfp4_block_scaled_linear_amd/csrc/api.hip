@@ -81,7 +81,7 @@ bool grouped_uses_gemm(int64_t T, int top_k, int E) {
 
 // grouped-call workspace layout: 256-byte aligned regions
 struct Layout {
-  size_t offsets, active, n_active, route_expert, sorted, rows, tiles, n_tiles, chunks, total;
+  size_t offsets, active, n_active, route_expert, sorted, slots, rows, tiles, n_tiles, chunks, total;
   int64_t max_tiles;
 };
 
@@ -99,6 +99,7 @@ Layout grouped_layout(int64_t T, int top_k, int E, int64_t N, int32_t out_mode) 
   L.n_active = o; o = up256(o + sizeof(int32_t));
   L.route_expert = o; o = up256(o + sizeof(int32_t) * R);
   L.sorted = o; o = up256(o + sizeof(int32_t) * R);
+  L.slots = o; o = up256(o + kSlotInts * sizeof(int32_t) * (R < (size_t)E ? R : (size_t)E));
   L.tiles = o; o = up256(o + sizeof(int32_t) * 2 * (size_t)L.max_tiles);
   L.n_tiles = o; o = up256(o + sizeof(int32_t));
   L.chunks = o; o = up256(o + sizeof(int32_t) * (size_t)route_chunk_ints(T, top_k, E));
@@ -274,6 +275,8 @@ nvfp4_status nvfp4_grouped_linear(int32_t act_kind, const void* x, const uint8_t
   ws.n_active = reinterpret_cast<int32_t*>(base + L.n_active);
   ws.route_expert = reinterpret_cast<int32_t*>(base + L.route_expert);
   ws.sorted = reinterpret_cast<int32_t*>(base + L.sorted);
+  ws.slots = reinterpret_cast<int32_t*>(base + L.slots);
+  ws.max_slots = (int32_t)(T * top_k < num_experts ? T * top_k : num_experts);
   ws.rows = reinterpret_cast<float*>(base + L.rows);
   ws.tiles = reinterpret_cast<int32_t*>(base + L.tiles);
   ws.n_tiles = reinterpret_cast<int32_t*>(base + L.n_tiles);
@@ -321,7 +324,7 @@ nvfp4_status nvfp4_grouped_linear(int32_t act_kind, const void* x, const uint8_t
   a.x = x; a.x_scales = x_scales; a.x_ts = x_ts; a.ldx = ldx;
   a.w_codes = w_codes; a.w_scales = w_scales; a.w_ts = w_ts;
   a.N = N; a.K = K;
-  a.offsets = ws.offsets; a.sorted = ws.sorted; a.active = ws.active; a.n_active = ws.n_active;
+  a.slots = ws.slots; a.sorted = ws.sorted;
   a.rows_per_token = rows_mode == NVFP4_ROWS_PER_TOKEN ? 1 : 0;
   a.x_rows = rows_mode == NVFP4_ROWS_PER_TOKEN ? T : T * top_k;
   a.top_k = top_k;

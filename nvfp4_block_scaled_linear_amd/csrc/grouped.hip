@@ -64,10 +64,13 @@ __device__ __forceinline__ int32_t block_exclusive_scan(int32_t v, int32_t* wsum
   return base + x - v;
 }
 
-// Offsets, the active list and the tile list from the per-expert counts in cnt[E] (LDS);
-// afterwards cnt[e] holds expert e's first slot in `sorted`.
+// Offsets, the active list, the slot record headers and the tile list from the per-expert
+// counts in cnt[E] (LDS); afterwards cnt[e] holds expert e's first slot in `sorted`. A
+// slot record gives a streaming workgroup its expert, its route range and (when the
+// caller fills them: slot_of != NULL, then slot_of[e] is e's slot) its first routes in
+// one 64-byte read, without the dependent reads of the active list, offsets and routes.
 __device__ __forceinline__ void expert_scans(const RouteWorkspace& ws, int E, int32_t* cnt,
-                                             int32_t* wsum) {
+                                             int32_t* wsum, int32_t* slot_of = nullptr) {
   const int tid = threadIdx.x, nt = blockDim.x;
   int32_t run = 0, act_run = 0, tile_run = 0;
   for (int e0 = 0; e0 < E; e0 += nt) {
@@ -80,7 +83,12 @@ __device__ __forceinline__ void expert_scans(const RouteWorkspace& ws, int E, in
     const int32_t to = block_exclusive_scan(ntile, wsum, &tot_t) + tile_run;
     if (e < E) {
       ws.offsets[e] = o;
-      if (c > 0) ws.active[a] = e;
+      if (c > 0) {
+        ws.active[a] = e;
+        const int32_t n = slot_of ? (c < kSlotRoutes ? c : kSlotRoutes) : 0;
+        *reinterpret_cast<int4*>(ws.slots + kSlotInts * a) = make_int4(e, o, o + c, n);
+        if (slot_of) slot_of[e] = a;
+      }
       if (ntile > 0) write_tiles(ws, e, o, c, to);
       cnt[e] = o;
     }
@@ -88,6 +96,7 @@ __device__ __forceinline__ void expert_scans(const RouteWorkspace& ws, int E, in
     act_run += tot_a;
     tile_run += tot_t;
   }
+  for (int s = act_run + tid; s < ws.max_slots; s += nt) ws.slots[kSlotInts * s] = -1;
   if (tid == 0) {
     ws.offsets[E] = run;
     *ws.n_active = act_run;
@@ -277,6 +286,7 @@ __global__ __launch_bounds__(kSortThreads) void route_sort_fast(const int32_t* i
   int32_t* rexp = sh + nt;                  // [nt] expert of each route, -1 dropped/padding
   int32_t* wsum = sh + 2 * nt;              // [16] wave totals of a scan
   int32_t* cnt = sh + 2 * nt + 16;          // [E] routes per expert
+  int32_t* slot_of = cnt + E;               // [E] slot of each active expert
   const int R = (int)(T * top_k);
   const int tid = threadIdx.x;
 
@@ -300,8 +310,8 @@ __global__ __launch_bounds__(kSortThreads) void route_sort_fast(const int32_t* i
   rexp[tid] = my_e;
   __syncthreads();
 
-  // offsets, active list, tile list; cnt becomes each expert's first slot
-  expert_scans(ws, E, cnt, wsum);
+  // offsets, active list, slot records, tile list; cnt becomes each expert's first slot
+  expert_scans(ws, E, cnt, wsum, slot_of);
 
   if (my_e >= 0) {
     // stable place among the expert's routes
@@ -313,6 +323,7 @@ __global__ __launch_bounds__(kSortThreads) void route_sort_fast(const int32_t* i
     }
     for (int r = full; r < tid; r++) rank += (rexp[r] == my_e);
     ws.sorted[cnt[my_e] + rank] = tid;
+    if (rank < kSlotRoutes) ws.slots[kSlotInts * slot_of[my_e] + 4 + rank] = tid;
   }
 }
 
@@ -403,7 +414,7 @@ hipError_t launch_route_sort(const int32_t* topk_ids, int64_t T, int top_k, int 
                              int64_t zero_row_bytes, hipStream_t stream) {
   if (T * top_k <= kFastRoutes) {
     const int nt = (int)((T * top_k + 63) / 64 * 64);
-    const size_t lds = sizeof(int32_t) * ((size_t)2 * nt + 16 + (size_t)E);
+    const size_t lds = sizeof(int32_t) * ((size_t)2 * nt + 16 + 2 * (size_t)E);
     hipLaunchKernelGGL(route_sort_fast, dim3(1), dim3(nt), lds, stream, topk_ids, T, top_k, E,
                        ws, faults, zero_out, zero_row_bytes);
     return hipGetLastError();

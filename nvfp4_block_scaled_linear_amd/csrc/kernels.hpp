@@ -29,10 +29,8 @@ struct StreamArgs {
   int32_t rsplit;   // dense: workgroups sharing one weight tile, each taking its own sets
                     // of four rows (0 or 1: one workgroup takes every row)
   // grouped form (NULL for dense)
-  const int32_t* offsets;    // [E+1] route ranges per expert in `sorted`
+  const int32_t* slots;      // [grid y] slot records (RouteWorkspace::slots)
   const int32_t* sorted;     // route ids grouped by expert
-  const int32_t* active;     // [E] active experts, ascending
-  const int32_t* n_active;   // [1]
   int32_t rows_per_token;    // x row of route r: r / top_k (1) or r (0)
   int32_t top_k;
   // grouped gate_up with the SwiGLU epilogue (NULL otherwise): a[route][n] =
@@ -98,7 +96,14 @@ struct RouteWorkspace {
   int32_t* n_tiles;       // [1]
   int32_t tile_rows;      // GEMM path: routes per tile (0: no tile list)
   int32_t* chunk_counts;  // chunked grouping: [chunks][E] counts, then first slots
+  int32_t* slots;         // [max_slots][kSlotInts] slot records, one per active expert in
+                          // ascending id: (expert, begin, end, n, the expert's first n
+                          // routes of `sorted`, n <= kSlotRoutes); expert -1 in the slots
+                          // past the last one
+  int32_t max_slots;      // min(routes, experts)
 };
+constexpr int kSlotInts = 16;
+constexpr int kSlotRoutes = kSlotInts - 4;
 
 // int32 entries of the chunked grouping's count table for this route set (0 when the
 // route set is grouped by a single workgroup)

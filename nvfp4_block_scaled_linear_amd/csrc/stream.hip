@@ -504,10 +504,12 @@ __device__ __forceinline__ void pass4(const StreamArgs& a, const uint8_t* wc, co
       __builtin_amdgcn_sched_barrier(0);  // refill the slot now, not at the end of the round
     }
   }
+  // (a wave with no steps computes nothing: its ring read zeros, but its scale rows in
+  // LDS were never written)
   const int last = (rounds - 1) * kDepth;
 #pragma unroll
   for (int j = 0; j < kDepth; j++)
-    if (last + j < NSW) compute(buf[j], kstep[j], j);
+    if (rounds > 0 && last + j < NSW) compute(buf[j], kstep[j], j);
 }
 
 // The fixed order in which partial sums meet: a wave's four k-groups in registers,
@@ -620,27 +622,53 @@ __global__ __launch_bounds__(256) void stream_dense(StreamArgs a) {
   });
 }
 
+// The routes of a grouped workgroup's expert, from its slot record: the first ones come
+// with the record (read together with its header), later ones from `sorted`.
+struct SlotRoutes {
+  int e, beg, count, n;
+  int4 q[kSlotRoutes / 4];
+  __device__ __forceinline__ explicit SlotRoutes(const StreamArgs& a) {
+    const int4* rec = reinterpret_cast<const int4*>(a.slots + kSlotInts * blockIdx.y);
+    const int4 h = rec[0];
+#pragma unroll
+    for (int j = 0; j < kSlotRoutes / 4; j++) q[j] = rec[1 + j];
+    e = h.x, beg = h.y, count = h.z - h.y, n = h.w;
+  }
+  // route c (0 <= c < count) of the expert
+  __device__ __forceinline__ int route(const StreamArgs& a, int c) const {
+    int v = q[0].x;
+#pragma unroll
+    for (int j = 0; j < kSlotRoutes / 4; j++) {
+      v = c == 4 * j + 0 ? q[j].x : v;
+      v = c == 4 * j + 1 ? q[j].y : v;
+      v = c == 4 * j + 2 ? q[j].z : v;
+      v = c == 4 * j + 3 ? q[j].w : v;
+    }
+    if (c >= n) v = a.sorted[beg + c];
+    return v;
+  }
+};
+
 template <int R, int ACT, bool SLDS>
 __global__ __launch_bounds__(256) void stream_grouped(StreamArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   float* red = reinterpret_cast<float*>(lds + lds_red_offset(1, R, blockDim.x >> 6, a.K, SLDS));
-  const int slot = blockIdx.y;
-  if (slot >= *a.n_active) return;  // uniform over the workgroup
-  const int e = a.active[slot];
-  const int beg = a.offsets[e], end = a.offsets[e + 1];
+  const SlotRoutes sr(a);
+  const int e = sr.e;
+  if (e < 0) return;  // a slot past the active experts (uniform over the workgroup)
   const uint8_t* wc = a.w_codes + (int64_t)e * a.N * (a.K >> 1);
   const uint8_t* ws = a.w_scales + (int64_t)e * a.N * (a.K >> 4);
   const float ts = a.apply_ts ? a.w_ts[e] : 1.0f;
   const int64_t n0 = (int64_t)blockIdx.x * 16;
   const int i = (threadIdx.x >> 4) & 3;
-  for (int c0 = beg; c0 < end; c0 += 4 * R) {
-    const int rows = min(4 * R, end - c0);
+  for (int c0 = 0; c0 < sr.count; c0 += 4 * R) {
+    const int rows = min(4 * R, sr.count - c0);
     RowMap rm;
 #pragma unroll
     for (int r = 0; r < 4; r++) {
       const int m = 4 * r + i;
       const bool ok = r < R && m < rows;
-      const int route = a.sorted[c0 + (ok ? m : 0)];
+      const int route = sr.route(a, c0 + (ok ? m : 0));
       const int64_t xrow = a.rows_per_token ? route / a.top_k : route;
       if (ACT == 0) {
         rm.off[r] = ok ? (uint32_t)(xrow * a.ldx * 2) : kOOB;
@@ -655,7 +683,7 @@ __global__ __launch_bounds__(256) void stream_grouped(StreamArgs a) {
     pass4<1, R, ACT, SLDS, grouped_ring_depth(R)>(a, wc, ws, n0, 16, lim, rm, lds, acc);
     reduce_store<1, R>(acc, red, n0, [&](int m, int64_t n, float s) {
       if (m < rows && n < a.N) {
-        const int rr = a.sorted[c0 + m];
+        const int rr = sr.route(a, c0 + m);
         float f = ts;
         if (ACT != 0) {
           const int64_t xrr = a.rows_per_token ? rr / a.top_k : rr;
@@ -677,10 +705,9 @@ template <int R, int ACT, bool SLDS>
 __global__ __launch_bounds__(256) void stream_grouped_swiglu(StreamArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   float* red = reinterpret_cast<float*>(lds + lds_red_offset(2, R, blockDim.x >> 6, a.K, SLDS));
-  const int slot = blockIdx.y;
-  if (slot >= *a.n_active) return;  // uniform over the workgroup
-  const int e = a.active[slot];
-  const int beg = a.offsets[e], end = a.offsets[e + 1];
+  const SlotRoutes sr(a);
+  const int e = sr.e;
+  if (e < 0) return;  // a slot past the active experts (uniform over the workgroup)
   const uint8_t* wc = a.w_codes + (int64_t)e * a.N * (a.K >> 1);
   const uint8_t* ws = a.w_scales + (int64_t)e * a.N * (a.K >> 4);
   const float ts = a.w_ts[e];
@@ -690,14 +717,14 @@ __global__ __launch_bounds__(256) void stream_grouped_swiglu(StreamArgs a) {
   const int lim[2] = {vr, vr};
   const int i = (threadIdx.x >> 4) & 3;
   const int W = blockDim.x >> 6;
-  for (int c0 = beg; c0 < end; c0 += 4 * R) {
-    const int rows = min(4 * R, end - c0);
+  for (int c0 = 0; c0 < sr.count; c0 += 4 * R) {
+    const int rows = min(4 * R, sr.count - c0);
     RowMap rm;
 #pragma unroll
     for (int r = 0; r < 4; r++) {
       const int m = 4 * r + i;
       const bool ok = r < R && m < rows;
-      const int route = a.sorted[c0 + (ok ? m : 0)];
+      const int route = sr.route(a, c0 + (ok ? m : 0));
       const int64_t xrow = a.rows_per_token ? route / a.top_k : route;
       if (ACT == 0) {
         rm.off[r] = ok ? (uint32_t)(xrow * a.ldx * 2) : kOOB;
@@ -718,7 +745,7 @@ __global__ __launch_bounds__(256) void stream_grouped_swiglu(StreamArgs a) {
       const int m = 4 * r + q;
       const int64_t n = n0 + nl;
       if (m < rows && n < half) {
-        const int rr = a.sorted[c0 + m];
+        const int rr = sr.route(a, c0 + m);
         float f = ts;
         if (ACT != 0) {
           const int64_t xrr = a.rows_per_token ? rr / a.top_k : rr;

@@ -238,6 +238,74 @@ def test_grouped_combine_with_dropped_routes(dev, o):
     assert f & nv.FAULT_BAD_ROUTE
 
 
+def test_grouped_stream_with_grouping_kernel(dev, o):
+    """320 routes on the streaming kernels (more routes than experts, several per expert):
+    per-route rows against the oracle (dropped routes zero), the combine, and bit
+    equality with the same routes split into two calls of 160 routes each."""
+    E, N, K, T, k = 64, 48, 128, 40, 8
+    ids, _ = moe_routes(141, T, E, k)
+    ids = ids.astype(np.int32)
+    dropped = [(2, 3), (17, 0), (39, 7)]
+    ids[2, 3] = ids[2, 1]
+    ids[17, 0] = -5
+    ids[39, 7] = E
+    _say(f"grouped stream, 320 routes: T={T} k={k} E={E}")
+    f = _combine_check(dev, o, ids, E, N, K, 142, "grouping kernel + stream: combine")
+    assert f & nv.FAULT_BAD_ROUTE
+    wc, wsc, wts, oc, os_, ot = _small_experts(o, dev, E, N, K, 142)
+    xb = act_bf16(143, T, K)
+    x = to_dev_bf16(xb, dev)
+    faults = torch.zeros(1, dtype=torch.int32, device=dev)
+    h = nv.grouped_linear(x, wc, wsc, wts, torch.from_numpy(ids).to(dev), faults=faults)
+    assert int(faults.item()) & nv.FAULT_BAD_ROUTE
+    hn = h.cpu().numpy()
+    for t, j in dropped:
+        assert np.all(hn[t * k + j] == 0), (t, j)
+    for r in np.r_[0, T * k - 1, np.random.default_rng(7).choice(T * k, 24, replace=False)]:
+        t, j = divmod(int(r), k)
+        if (t, j) in dropped:
+            continue
+        e = int(ids[t, j])
+        yr, b = o.linear(xb[t:t + 1], oc[e], os_[e], ot[e:e + 1])
+        assert_within(hn[r:r + 1], yr, b, f"grouping kernel + stream: route {t},{j}")
+    half = T // 2
+    parts = [nv.grouped_linear(x[p * half:(p + 1) * half].contiguous(), wc, wsc, wts,
+                               torch.from_numpy(ids[p * half:(p + 1) * half].copy()).to(dev))
+             for p in range(2)]
+    assert torch.equal(torch.cat(parts), h)
+
+
+def test_grouped_many_experts_few_routes(dev, o):
+    """2600 experts, 14 of them routed (ids up to 2599, far apart): each active expert's
+    slot record and weight offset; dropped routes (repeat, out of range) zeroed and
+    flagged; the experts no route picks hold zero weights, which no output may touch."""
+    E, N, K, T, k = 2600, 32, 64, 6, 4
+    ids = np.array([[5, 2100, 2599, 64], [2100, 7, 2047, 2048], [0, 5, 5, 2600],
+                    [2599, 2598, 1, 2], [3000, 2049, 2100, 6], [64, 65, 2047, 0]], np.int32)
+    dropped = [(2, 2), (2, 3), (4, 0)]
+    used = sorted({int(e) for e in ids.ravel() if 0 <= e < E})
+    _say(f"many experts: E={E}, {len(used)} experts routed")
+    q = {e: quantize_both(o, weight_f32(151, N, K, stream=200 + e), dev) for e in used}
+    wc = torch.zeros((E, N, K // 2), dtype=torch.uint8, device=dev)
+    wsc = torch.zeros((E, N, K // 16), dtype=torch.uint8, device=dev)
+    wts = torch.zeros(E, dtype=torch.float32, device=dev)
+    for e in used:
+        wc[e], wsc[e], wts[e] = q[e][0][0], q[e][0][1], q[e][0][2][0]
+    xb = act_bf16(152, T, K)
+    faults = torch.zeros(1, dtype=torch.int32, device=dev)
+    h = nv.grouped_linear(to_dev_bf16(xb, dev), wc, wsc, wts, torch.from_numpy(ids).to(dev),
+                          faults=faults).cpu().numpy()
+    assert int(faults.item()) & nv.FAULT_BAD_ROUTE
+    for t in range(T):
+        for j in range(k):
+            if (t, j) in dropped:
+                assert np.all(h[t * k + j] == 0), (t, j)
+                continue
+            e = int(ids[t, j])
+            yr, b = o.linear(xb[t:t + 1], *q[e][1])
+            assert_within(h[t * k + j:t * k + j + 1], yr, b, f"many experts: route {t},{j}")
+
+
 def test_grouped_many_routes_general_sort(dev, o):
     """More routes than one sorting workgroup holds at once (T * top_k > 1024): the
     chunked route grouping (one chunk here), several 16-row passes per expert, in both
