@@ -32,6 +32,7 @@ METRIC = "NVFP4 linear µs & achieved HBM GB/s (M=1..16); prefill TFLOP/s; % roo
 HBM_PEAK_GBPS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 ROTATE_BYTES = 1 << 30
+LEG_REPLAYS = 25  # timed graph replays per leg (--leg-replays)
 
 
 def log(*a):
@@ -299,7 +300,7 @@ def bench_decode_prefetch(nv, dev):
         for M in Ms:
             assert torch.equal(ys[M], ref[M]), f"prefetch changed a result at M={M}"
         warm_until(g.replay, 0.05)
-        ms, sp = timed(g, 25, R)
+        ms, sp = timed(g, LEG_REPLAYS, R)
         key = "no_prefetch" if wg == 0 else f"prefetch_wg{wg}"
         out[key] = {"us_per_layer": round(ms * 1e3, 3), **sp,
                     "GBps": round(out["bytes_per_layer_avg"] / (ms * 1e-3) / 1e9, 1)}
@@ -361,7 +362,7 @@ def bench_single(nv, dev):
     g = capture(run)
     timer = Timer()
     timer.time(g.replay, 1)
-    ms, sp = timed(g, 25, R)
+    ms, sp = timed(g, LEG_REPLAYS, R)
     b = linear_bytes(M, N, K)
     del g
     # a launch this small is latency: the plain streaming read of the same bytes, timed the
@@ -390,7 +391,7 @@ def bench_prefill(nv, dev):
     g = capture(run)
     timer = Timer()
     warm_until(g.replay, 0.15)  # the clock settles under sustained MFMA load
-    ms, sp = timed(g, 25, R)
+    ms, sp = timed(g, LEG_REPLAYS, R)
     # clock and power under the same load, back-to-back replays outside the timed region
     with PowerSampler() as ps:
         for _ in range(max(1, int(0.3 / (ms * R * 1e-3)))):
@@ -425,7 +426,7 @@ def bench_w4a4(nv, dev):
                 nv.linear(xc, W[j][0], W[j][1], t, x_scales=xs_, x_ts=xt, out=y)
         g = capture(run)
         warm_until(g.replay, 0.1)
-        ms, sp = timed(g, 25, reps_in)
+        ms, sp = timed(g, LEG_REPLAYS, reps_in)
         b = weight_bytes(N, K) + 4 + M * (2 * K + K // 2 + K // 16 + 4) + M * (K // 2 + K // 16 + 4) + 4 * M * N
         fl = 2.0 * M * N * K
         out[str(M)] = {"us_quantize_plus_linear": round(ms * 1e3, 3), **sp,
@@ -465,7 +466,7 @@ def bench_w4a4_in_call(nv, dev):
         for name, fn in (("us_two_calls", two_calls), ("us_in_call", in_call)):
             g = capture(fn)
             warm_until(g.replay, 0.05)
-            ms, sp = timed(g, 25, R)
+            ms, sp = timed(g, LEG_REPLAYS, R)
             rec[name] = round(ms * 1e3, 3)
             rec[name + "_p10_p90"] = [sp["us_p10"], sp["us_p90"]]
             del g
@@ -506,7 +507,7 @@ def bench_moe(nv, dev):
     g = capture(run)
     timer = Timer()
     timer.time(g.replay, 1)
-    ms, sp = timed(g, 25, R)
+    ms, sp = timed(g, LEG_REPLAYS, R)
     D = len(np.unique(ids))
     per_expert = weight_bytes(cfg["N_gu"], cfg["K_gu"]) + weight_bytes(cfg["N_d"], cfg["K_d"]) + 8
     b = D * per_expert + T * cfg["K_gu"] * 2 + T * cfg["N_d"] * 4
@@ -547,7 +548,7 @@ def bench_moe_prefill(nv, dev):
     g = capture(run)
     timer = Timer()
     warm_until(g.replay, 0.15)
-    ms, sp = timed(g, 25, 1)
+    ms, sp = timed(g, LEG_REPLAYS, 1)
     R = T * k
     flops = 2.0 * R * (cfg["N_gu"] * cfg["K_gu"] + cfg["N_d"] * cfg["K_d"])
     tf = flops / (ms * 1e-3) / 1e12
@@ -820,10 +821,13 @@ def main():
                     help="skip the decode sweep (profiling runs of other workloads; the line "
                          "then has no headline value)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--leg-replays", type=int, default=25,
+                    help="timed graph replays of each leg other than the decode sweep")
     ap.add_argument("--copy-probe", action="store_true", help="also time a 1 GiB device copy")
     ap.add_argument("--summarize-rocprof", metavar="DIR",
                     help="print a text summary of rocprofv3 output under DIR and exit")
     args = ap.parse_args()
+    globals()["LEG_REPLAYS"] = max(5, args.leg_replays)
     if args.summarize_rocprof:
         summarize_rocprof(args.summarize_rocprof, calib_bytes=1 << 30)
         print(f"kernel_sources_sha256: {stream_source_hash()}")
