@@ -437,6 +437,15 @@ def bench_w4a4(nv, dev):
     return out
 
 
+def bench_w4a4_probe(nv, dev):
+    """The read probe for the W4A4 weight's bytes (K = N = 4096: 9.4 MB), timed as the
+    launches above: the single-launch floor beside the quantize + linear figures."""
+    from synth import WORKLOADS
+    cfg = WORKLOADS["w4a4"]
+    p = read_probe_roof(nv, dev, weight_bytes(cfg["N"], cfg["K"]), Timer())
+    return {"bytes": p["bytes"], "us": p["us"], "GBps": p["GBps"]}
+
+
 def bench_w4a4_in_call(nv, dev):
     """W4A4 for one row two ways on the W4A4 weight (K = N = 4096): the quantizer launch
     followed by the NVFP4-activation linear, and the one-launch form that quantizes the
@@ -907,6 +916,7 @@ def run_legs(nv, dev, args, legs, rec):
         log("w4a4 ...")
         rec["w4a4"] = bench_w4a4(nv, dev)
         rec["w4a4_in_call_quantize"] = bench_w4a4_in_call(nv, dev)
+        rec["w4a4_weight_read_probe"] = bench_w4a4_probe(nv, dev)
     if want("moe"):
         log("moe ...")
         rec["moe"] = bench_moe(nv, dev)
