@@ -5,9 +5,10 @@
 // #754 and #822), with activations rounded once rather than in every tile (PR #761).
 // That design targets GB10 tensor cores; on gfx950 we keep the ideas that still hold and
 // shape the rest for CDNA4:
-//  - Large M: a 256 (M) x 256 (N) x 64 (K) tile on eight wave64s (two along M, four
-//    along N, each 128 x 64 with the 32x32x16 BF16 MFMA); the weight tile is decoded
-//    once per workgroup into LDS and read by both row halves (gemm_wide below).
+//  - Large M: a 256 (M) x 256 (N) x 64 (K) tile on twelve wave64s with split roles:
+//    eight consumer waves (two along M, four along N, each 128 x 64 with the 32x32x16
+//    BF16 MFMA) only read LDS and run MFMAs; four producer waves only load, decode the
+//    weight tile once per workgroup and write both operands to LDS (gemm_wide below).
 //  - Smaller M: a 32*MT (M) x 256 (N) tile on four wave64s side by side along N, each
 //    computing 32*MT x 64 and decoding its own weight columns in registers; two
 //    workgroups per CU.
@@ -366,27 +367,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 }
 
 // ---------------------------------------------------------------------------------------
-// Wide variant for large M: a 256 x 256 tile and eight waves, two along M and four along
-// N, two waves per SIMD. The weight tile is decoded once per workgroup (one 16-byte code
-// chunk per thread) into LDS as exact BF16 and read by both row halves, so each decoded
-// element feeds 256 rows; both operands are double buffered in LDS (147 KB), read with
-// 128-bit LDS loads (about twice the rate of narrower ones on gfx950).
+// gemm_wide: 256 x 256 tiles, wave-specialized. Eight consumer waves (two along M, four
+// along N, each 128 x 64) only read LDS and run MFMAs; four producer waves only load,
+// decode and write LDS, so no wave both waits on global loads and feeds the MFMA pipe.
+// Both operand stages are double buffered in LDS (147 KB) with one workgroup barrier per 64-k
+// step: between barriers the producers write step kt + 1's stage while the consumers
+// multiply step kt's. The producers hold two register sets of loads, issued two steps
+// ahead. Each output element sums its K products in the same order as the 64-row kernel
+// (the same 32x32x16 MFMA chain over the same k), so rows do not depend on the tiling.
 // ---------------------------------------------------------------------------------------
-template <int ACT>
-struct RegAW {  // one K step of this thread's activation loads (4 chunks)
-  u32x4 v[ACT == 0 ? 4 : 1];
-  uint32_t c[ACT == 0 ? 1 : 4];
-  uint32_t s[ACT == 0 ? 1 : 4];
-};
-struct RegBW {  // one K step of this thread's weight chunk: 32 codes and their 2 scales
-  u32x4 c;
-  uint32_t s;
-};
-
 constexpr int kWideBM = 256;
 
 template <int ACT>
-__global__ __launch_bounds__(512) void gemm_wide(GemmArgs a) {
+struct RegAP {  // one K step of a producer lane's activation loads (8 chunks)
+  u32x4 v[ACT == 0 ? 8 : 1];
+  uint32_t c[ACT == 0 ? 1 : 8];
+  uint32_t s[ACT == 0 ? 1 : 8];
+};
+struct RegBP {  // one K step of a producer lane's weight chunks (two of 32 codes)
+  u32x4 c[2];
+  uint32_t s[2];
+};
+
+template <int ACT>
+__global__ __launch_bounds__(768) void gemm_wide(GemmArgs a) {
   constexpr int BM = kWideBM;
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
   uint16_t* As = lds;                 // [2][BM * LDA]  activations [row][k]
@@ -394,8 +398,7 @@ __global__ __launch_bounds__(512) void gemm_wide(GemmArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave >> 2, wn = wave & 3;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // scalar: the role branch is uniform
   const int64_t M = a.M, N = a.N, K = a.K;
   const uint32_t Ku = (uint32_t)K;
 
@@ -408,69 +411,113 @@ __global__ __launch_bounds__(512) void gemm_wide(GemmArgs a) {
   const int64_t n0 = (lin % nbn) * BN;
   const int64_t rows_m = (M - m0) < BM ? (M - m0) : BM;
   const int64_t rows_n = (N - n0) < BN ? (N - n0) : BN;
+  const int KT = (int)((K + BK - 1) / BK);
+  const int KT2 = KT + (KT & 1);  // whole rounds of the two register sets
 
-  __amdgpu_buffer_rsrc_t xr, xsr;
-  if (ACT == 0) {
-    xr = rsrc(static_cast<const uint16_t*>(a.x) + m0 * a.ldx, ((rows_m - 1) * a.ldx + K) * 2);
-    xsr = xr;
-  } else {
-    xr = rsrc(static_cast<const uint8_t*>(a.x) + m0 * (K >> 1), rows_m * (K >> 1));
-    xsr = rsrc(a.x_scales + m0 * (K >> 4), rows_m * (K >> 4));
+  if (wave >= 8) {
+    // descriptors from values made explicitly scalar (the role branch would otherwise leave
+    // them in vector registers, and every load would loop over the lanes' descriptors)
+    auto uni = [](const void* p) -> const void* {
+      const uint64_t v = (uint64_t)(uintptr_t)p;
+      const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+      const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+      return (const void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+    };
+    auto uni64 = [](int64_t v) -> int64_t {
+      const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+      const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+      return (int64_t)(((uint64_t)hi << 32) | lo);
+    };
+    __amdgpu_buffer_rsrc_t xr, xsr;
+    if (ACT == 0) {
+      xr = rsrc(uni(static_cast<const uint16_t*>(a.x) + m0 * a.ldx), uni64(((rows_m - 1) * a.ldx + K) * 2));
+      xsr = xr;
+    } else {
+      xr = rsrc(uni(static_cast<const uint8_t*>(a.x) + m0 * (K >> 1)), uni64(rows_m * (K >> 1)));
+      xsr = rsrc(uni(a.x_scales + m0 * (K >> 4)), uni64(rows_m * (K >> 4)));
+    }
+    const auto wr = rsrc(uni(a.w_codes + n0 * (K >> 1)), uni64(rows_n * (K >> 1)));
+    const auto sr = rsrc(uni(a.w_scales + n0 * (K >> 4)), uni64(rows_n * (K >> 4)));
+    // ---------------- producers: 256 lanes ----------------
+    const int pt = tid - 512;
+    uint32_t bwoff[2], bsoff[2];
+#pragma unroll
+    for (int q = 0; q < 2; q++) {
+      const int bc = (pt + 256 * q) >> 1;
+      bwoff[q] = bc < rows_n ? (uint32_t)(bc * (K >> 1)) : kOOB;
+      bsoff[q] = bc < rows_n ? (uint32_t)(bc * (K >> 4)) : kOOB;
+    }
+    auto issue = [&](int kt, RegAP<ACT>& ra, RegBP& rb) {
+      const uint32_t k0 = (uint32_t)kt * BK;
+#pragma unroll
+      for (int q = 0; q < 2; q++) {
+        const uint32_t kh = k0 + 32u * ((pt + 256 * q) & 1);
+        rb.s[q] = __builtin_amdgcn_raw_buffer_load_b16(sr, (bsoff[q] + (kh >> 4)) | past(Ku, kh), 0, 0);
+        rb.c[q] = __builtin_amdgcn_raw_buffer_load_b128(wr, (bwoff[q] + (kh >> 1)) | past(Ku, kh), 0, 0);
+      }
+#pragma unroll
+      for (int q = 0; q < 8; q++) {
+        const int c = pt + 256 * q;
+        const int row = c >> 3, j = c & 7;
+        const uint32_t k = k0 + 8u * j;
+        if (ACT == 0) {
+          const uint32_t off = (uint32_t)(row * a.ldx * 2) + 2u * k;
+          ra.v[q] = __builtin_amdgcn_raw_buffer_load_b128(xr, off | past(Ku, k), 0, 0);
+        } else {
+          ra.c[q] = __builtin_amdgcn_raw_buffer_load_b32(
+              xr, ((uint32_t)(row * (K >> 1)) + (k >> 1)) | past(Ku, k), 0, 0);
+          ra.s[q] = __builtin_amdgcn_raw_buffer_load_b8(
+              xsr, ((uint32_t)(row * (K >> 4)) + (k >> 4)) | past(Ku, k), 0, 0);
+        }
+      }
+    };
+    auto write_stage = [&](const RegAP<ACT>& ra, const RegBP& rb, int buf) {
+      uint16_t* da = As + buf * (BM * LDA);
+#pragma unroll
+      for (int q = 0; q < 8; q++) {
+        const int c = pt + 256 * q;
+        const int row = c >> 3, j = c & 7;
+        u32x4 v;
+        if (ACT == 0) v = ra.v[q];
+        else v = decode8(ra.c[q], e4m3_to_f32<0>(ra.s[q]));  // exact BF16 activations
+        *reinterpret_cast<u32x4*>(da + row * LDA + 8 * j) = v;
+      }
+#pragma unroll
+      for (int q = 0; q < 2; q++) {
+        const int c = pt + 256 * q;
+        const int bc = c >> 1, bh = c & 1;
+        uint16_t* db = Bs + buf * (BN * LDA) + bc * LDA + 32 * bh;
+        const float s0 = e4m3_to_f32<0>(rb.s[q]), s1 = e4m3_to_f32<1>(rb.s[q]);
+#pragma unroll
+        for (int d = 0; d < 4; d++)
+          *reinterpret_cast<u32x4*>(db + 8 * d) = decode8(rb.c[q][d], d < 2 ? s0 : s1);
+      }
+    };
+    RegAP<ACT> ra[2];
+    RegBP rb[2];
+    issue(0, ra[0], rb[0]);
+    issue(1, ra[1], rb[1]);
+    write_stage(ra[0], rb[0], 0);
+    issue(2, ra[0], rb[0]);
+    __syncthreads();  // stage 0 ready
+    // step kt: write step kt + 1's stage from set (kt + 1) % 2, refill that set with step
+    // kt + 3; one barrier per step, matched by the consumers'
+    auto pstep = [&](int kt, RegAP<ACT>& ran, RegBP& rbn) {
+      write_stage(ran, rbn, (kt + 1) & 1);
+      issue(kt + 3, ran, rbn);
+      __syncthreads();
+    };
+    for (int kt = 0; kt < KT2; kt += 2) {
+      pstep(kt, ra[1], rb[1]);
+      pstep(kt + 1, ra[0], rb[0]);
+    }
+    return;
   }
-  const auto wr = rsrc(a.w_codes + n0 * (K >> 1), rows_n * (K >> 1));
-  const auto sr = rsrc(a.w_scales + n0 * (K >> 4), rows_n * (K >> 4));
-  // this thread's weight chunk: column bc, K half bh of each 64-k step
-  const int bc = tid >> 1, bh = tid & 1;
-  const uint32_t bwoff = bc < rows_n ? (uint32_t)(bc * (K >> 1)) : kOOB;
-  const uint32_t bsoff = bc < rows_n ? (uint32_t)(bc * (K >> 4)) : kOOB;
-  // MFMA operand lanes: row/column c of a 32-wide subtile, K half h
+
+  // ---------------- consumers: 8 waves ----------------
+  const int wm = wave >> 2, wn = wave & 3;
   const int col = lane & 31;
   const int h = lane >> 5;
-
-  const int KT = (int)((K + BK - 1) / BK);
-  const int KT2 = KT + (KT & 1);
-
-  auto issue = [&](int kt, RegAW<ACT>& ra, RegBW& rb) {
-    const uint32_t k0 = (uint32_t)kt * BK;
-#pragma unroll
-    for (int q = 0; q < 4; q++) {
-      const int c = tid + 512 * q;
-      const int row = c >> 3, j = c & 7;
-      const uint32_t k = k0 + 8u * j;
-      if (ACT == 0) {
-        const uint32_t off = (uint32_t)(row * a.ldx * 2) + 2u * k;
-        ra.v[q] = __builtin_amdgcn_raw_buffer_load_b128(xr, off | past(Ku, k), 0, 0);
-      } else {
-        ra.c[q] = __builtin_amdgcn_raw_buffer_load_b32(
-            xr, ((uint32_t)(row * (K >> 1)) + (k >> 1)) | past(Ku, k), 0, 0);
-        ra.s[q] = __builtin_amdgcn_raw_buffer_load_b8(
-            xsr, ((uint32_t)(row * (K >> 4)) + (k >> 4)) | past(Ku, k), 0, 0);
-      }
-    }
-    const uint32_t kh = k0 + 32u * bh;
-    rb.c = __builtin_amdgcn_raw_buffer_load_b128(wr, (bwoff + (kh >> 1)) | past(Ku, kh), 0, 0);
-    rb.s = __builtin_amdgcn_raw_buffer_load_b16(sr, (bsoff + (kh >> 4)) | past(Ku, kh), 0, 0);
-  };
-
-  // stage one K step: activations as they are (or decoded from NVFP4), weights decoded
-  auto write_tiles = [&](const RegAW<ACT>& ra, const RegBW& rb, int buf) {
-    uint16_t* da = As + buf * (BM * LDA);
-#pragma unroll
-    for (int q = 0; q < 4; q++) {
-      const int c = tid + 512 * q;
-      const int row = c >> 3, j = c & 7;
-      u32x4 v;
-      if (ACT == 0) v = ra.v[q];
-      else v = decode8(ra.c[q], e4m3_to_f32<0>(ra.s[q]));  // exact BF16 activations
-      *reinterpret_cast<u32x4*>(da + row * LDA + 8 * j) = v;
-    }
-    uint16_t* db = Bs + buf * (BN * LDA) + bc * LDA + 32 * bh;
-    const float s0 = e4m3_to_f32<0>(rb.s), s1 = e4m3_to_f32<1>(rb.s);
-#pragma unroll
-    for (int d = 0; d < 4; d++)
-      *reinterpret_cast<u32x4*>(db + 8 * d) = decode8(rb.c[d], d < 2 ? s0 : s1);
-  };
-
   f32x16 acc[4][2];
 #pragma unroll
   for (int mt = 0; mt < 4; mt++)
@@ -478,10 +525,8 @@ __global__ __launch_bounds__(512) void gemm_wide(GemmArgs a) {
     for (int st = 0; st < 2; st++)
 #pragma unroll
       for (int r = 0; r < 16; r++) acc[mt][st][r] = 0.f;
-
-  auto body = [&](int kt, RegAW<ACT>& ra_free, RegBW& rb_free, const RegAW<ACT>& ra_next,
-                  const RegBW& rb_next) {
-    issue(kt + 2, ra_free, rb_free);
+  __syncthreads();  // stage 0 ready
+  for (int kt = 0; kt < KT2; kt++) {
     const uint16_t* sa = As + (kt & 1) * (BM * LDA) + (128 * wm + col) * LDA + 32 * h;
     const uint16_t* sb = Bs + (kt & 1) * (BN * LDA) + (64 * wn + col) * LDA + 32 * h;
 #pragma unroll
@@ -497,25 +542,7 @@ __global__ __launch_bounds__(512) void gemm_wide(GemmArgs a) {
         for (int st = 0; st < 2; st++) acc[mt][st] = mfma32(A, B[st], acc[mt][st]);
       }
     }
-    write_tiles(ra_next, rb_next, (kt + 1) & 1);
-#pragma unroll
-    for (int i = 0; i < 32; i++) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  // one MFMA
-      if (i < 24) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);      // one LDS read
-      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);                  // VALU
-    }
     __syncthreads();
-  };
-
-  RegAW<ACT> ra0, ra1;
-  RegBW rb0, rb1;
-  issue(0, ra0, rb0);
-  issue(1, ra1, rb1);
-  write_tiles(ra0, rb0, 0);
-  __syncthreads();
-  for (int kt = 0; kt < KT2; kt += 2) {
-    body(kt, ra0, rb0, ra1, rb1);
-    body(kt + 1, ra1, rb1, ra0, rb0);
   }
 
   const float ts = a.w_ts[0];
@@ -814,7 +841,7 @@ template <int ACT>
 hipError_t launch_wide(const GemmArgs& a, hipStream_t stream) {
   const int64_t blocks = ((a.M + kWideBM - 1) / kWideBM) * ((a.N + BN - 1) / BN);
   const size_t lds = 2 * (size_t)(kWideBM + BN) * LDA * sizeof(uint16_t);
-  hipLaunchKernelGGL((gemm_wide<ACT>), dim3((uint32_t)blocks), dim3(512), lds, stream, a);
+  hipLaunchKernelGGL((gemm_wide<ACT>), dim3((uint32_t)blocks), dim3(768), lds, stream, a);
   return hipGetLastError();
 }
 
