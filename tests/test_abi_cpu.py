@@ -20,6 +20,11 @@ P = 0x7F0000000000  # an aligned fake device address (never dereferenced)
 
 @pytest.fixture(scope="module")
 def lib():
+    # NVFP4_TEST_LIB: another build of the same sources (the sanitizer test runs this file
+    # against a host-instrumented copy)
+    alt = os.environ.get("NVFP4_TEST_LIB")
+    if alt:
+        return nv.load_library(alt)
     if not os.path.exists(nv.LIB_PATH):
         from nvfp4_block_scaled_linear_amd import build
         build.build()
