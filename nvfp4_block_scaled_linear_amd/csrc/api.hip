@@ -79,6 +79,17 @@ bool grouped_uses_gemm(int64_t T, int top_k, int E) {
   return R >= kGroupedGemmRoutes * active;
 }
 
+// The GEMM path's wide form (each expert's first 256 routes in one 256-route tile, the
+// rest in 64-route tiles) when the experts hold at least this many routes on average;
+// below it most of a 256-route tile would be padding. Depends on the route set only, so
+// that both calls of a layer agree on the workspace's grouping.
+constexpr int64_t kGroupedWideRoutes = 192;
+bool grouped_uses_wide(int64_t T, int top_k, int E) {
+  const int64_t R = T * top_k;
+  const int64_t active = R < E ? R : E;
+  return grouped_uses_gemm(T, top_k, E) && R >= kGroupedWideRoutes * active;
+}
+
 // grouped-call workspace layout: 256-byte aligned regions
 struct Layout {
   size_t offsets, active, n_active, route_expert, sorted, slots, rows, tiles, n_tiles, chunks, total;
@@ -91,7 +102,7 @@ Layout grouped_layout(int64_t T, int top_k, int E, int64_t N, int32_t out_mode) 
   Layout L;
   const size_t R = (size_t)T * (size_t)top_k;
   const bool gemm = grouped_uses_gemm(T, top_k, E);
-  const int64_t tr = gemm_grouped_tile_rows();
+  const int64_t tr = gemm_grouped_tile_rows(grouped_uses_wide(T, top_k, E));
   L.max_tiles = gemm ? ((int64_t)R + tr - 1) / tr + E : 0;  // one partial tile per expert
   size_t o = 0;
   L.offsets = o; o = up256(o + sizeof(int32_t) * ((size_t)E + 1));
@@ -282,7 +293,9 @@ nvfp4_status nvfp4_grouped_linear(int32_t act_kind, const void* x, const uint8_t
   ws.n_tiles = reinterpret_cast<int32_t*>(base + L.n_tiles);
   ws.chunk_counts = reinterpret_cast<int32_t*>(base + L.chunks);
   const bool gemm = L.max_tiles > 0;
-  ws.tile_rows = gemm ? gemm_grouped_tile_rows() : 0;
+  const bool wide = grouped_uses_wide(T, top_k, num_experts);
+  ws.tile_rows = gemm ? gemm_grouped_tile_rows(wide) : 0;
+  ws.main_rows = wide ? kWideGroupedRows : 0;
 
   // dropped routes read as zero rows in the per-route output forms; the grouping kernel
   // clears them
@@ -312,7 +325,12 @@ nvfp4_status nvfp4_grouped_linear(int32_t act_kind, const void* x, const uint8_t
     } else {
       g.y = ws.rows; g.ldy = N; g.apply_ts = 0;
     }
-    e = launch_gemm_grouped(g, act_kind, L.max_tiles, s);
+    if (wide) {
+      g.active = ws.active; g.n_active = ws.n_active;
+      e = launch_gemm_grouped_wide(g, act_kind, R < num_experts ? R : num_experts, L.max_tiles, s);
+    } else {
+      e = launch_gemm_grouped(g, act_kind, L.max_tiles, s);
+    }
     if (e != hipSuccess) return NVFP4_ERR_LAUNCH;
     if (out_mode == NVFP4_OUT_COMBINE) {
       e = launch_combine(ws.rows, ws.route_expert, topk_w, w_ts, T, top_k, N,

@@ -563,6 +563,269 @@ __global__ __launch_bounds__(768) void gemm_wide(GemmArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------
+// gemm_wide_grouped: the wide wave-specialized tile on an expert's routes. Workgroup
+// (tile t, column block cb) takes active expert t's first routes (up to 256; the rest of
+// the expert's routes are in the grouping's tile list, for the 64-row grouped kernel),
+// gathers their activation rows through a row table in LDS and multiplies them by that
+// expert's weight. Operands, stages, MFMA chain and k order are gemm_wide's, and the
+// epilogue is the grouped 64/128-row kernel's, so a route's row is the dense product bit
+// for bit.
+//
+// SWIGLU: the tile's 256 columns are 128 gate columns (consumer waves wn = 0, 1) and the
+// matching 128 up columns N/2 + ... (wn = 2, 3); the up waves hand their scaled results
+// to the gate waves through LDS, and the gate waves write bf16_rne(silu(g) * u).
+// ---------------------------------------------------------------------------------------
+template <int ACT, bool SWIGLU>
+__global__ __launch_bounds__(768) void gemm_wide_grouped(GemmArgs a) {
+  constexpr int BM = kWideBM;
+  extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
+  uint16_t* As = lds;                 // [2][BM * LDA]  activations [row][k]
+  uint16_t* Bs = lds + 2 * BM * LDA;  // [2][BN * LDA]  decoded weight [column][k]
+  __shared__ int32_t row_x[BM];       // x row of each tile row (-1: none)
+  __shared__ int32_t row_route[BM];   // route of each tile row
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t N = a.N, K = a.K;
+  const uint32_t Ku = (uint32_t)K;
+  const int64_t half = N >> 1;
+  const int64_t nbn = SWIGLU ? (half + BN / 2 - 1) / (BN / 2) : (N + BN - 1) / BN;
+
+  // XCD x (blockIdx % 8) takes the x-th eighth of the active list, each expert with all
+  // its column blocks: the gathered rows of a tile are fetched into one XCD's L2
+  const int64_t bx = blockIdx.x;
+  const int64_t n_act = *a.n_active;
+  const int64_t per_xcd = (n_act + 7) / 8;
+  const int64_t t = (bx / 8) / nbn < per_xcd ? (bx % 8) * per_xcd + (bx / 8) / nbn : INT64_MAX;
+  if (t >= n_act) return;  // uniform over the workgroup, before any barrier
+  const int64_t cb = (bx / 8) % nbn;
+  const int e = a.active[t];
+  const int32_t beg = a.offsets[e];
+  const int32_t cnt = a.offsets[e + 1] - beg;
+  const int rows_m = cnt < BM ? cnt : BM;
+  const float ts = a.apply_ts ? a.w_ts[e] : 1.0f;
+  for (int i = tid; i < BM; i += 768) {
+    const int32_t route = i < rows_m ? a.sorted[beg + i] : -1;
+    row_route[i] = route;
+    row_x[i] = route < 0 ? -1 : (a.rows_per_token ? route / a.top_k : route);
+  }
+  __syncthreads();  // row table ready
+
+  const int KT = (int)((K + BK - 1) / BK);
+  const int KT2 = KT + (KT & 1);  // whole rounds of the two register sets
+
+  if (wave >= 8) {
+    auto uni = [](const void* p) -> const void* {
+      const uint64_t v = (uint64_t)(uintptr_t)p;
+      const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+      const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+      return (const void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+    };
+    auto uni64 = [](int64_t v) -> int64_t {
+      const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+      const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+      return (int64_t)(((uint64_t)hi << 32) | lo);
+    };
+    // all of x (rows gathered by the row table) and all of expert e's weight
+    __amdgpu_buffer_rsrc_t xr, xsr;
+    if (ACT == 0) {
+      xr = rsrc(uni(a.x), uni64(((a.x_rows - 1) * a.ldx + K) * 2));
+      xsr = xr;
+    } else {
+      xr = rsrc(uni(a.x), uni64(a.x_rows * (K >> 1)));
+      xsr = rsrc(uni(a.x_scales), uni64(a.x_rows * (K >> 4)));
+    }
+    const auto wr = rsrc(uni(a.w_codes + (int64_t)e * N * (K >> 1)), uni64(N * (K >> 1)));
+    const auto sr = rsrc(uni(a.w_scales + (int64_t)e * N * (K >> 4)), uni64(N * (K >> 4)));
+    // ---------------- producers: 256 lanes ----------------
+    const int pt = tid - 512;
+    // this lane's 8 activation chunks: tile row (pt + 256 q) / 8, 16 bytes at chunk pt % 8
+    uint32_t xoff[8], xsoff[ACT == 0 ? 1 : 8];
+#pragma unroll
+    for (int q = 0; q < 8; q++) {
+      const int32_t xrow = row_x[(pt + 256 * q) >> 3];
+      if (ACT == 0) {
+        xoff[q] = xrow < 0 ? kOOB : (uint32_t)(xrow * a.ldx * 2);
+      } else {
+        xoff[q] = xrow < 0 ? kOOB : (uint32_t)(xrow * (K >> 1));
+        xsoff[q] = xrow < 0 ? kOOB : (uint32_t)(xrow * (K >> 4));
+      }
+    }
+    // this lane's 2 weight chunks: tile column (pt + 256 q) / 2, K half (pt + 256 q) % 2
+    uint32_t bwoff[2], bsoff[2];
+#pragma unroll
+    for (int q = 0; q < 2; q++) {
+      const int bc = (pt + 256 * q) >> 1;
+      int64_t wrow;
+      bool ok;
+      if (SWIGLU) {
+        const int64_t c = cb * (BN / 2) + (bc & (BN / 2 - 1));
+        wrow = (bc < BN / 2 ? 0 : half) + c;
+        ok = c < half;
+      } else {
+        wrow = cb * BN + bc;
+        ok = wrow < N;
+      }
+      bwoff[q] = ok ? (uint32_t)(wrow * (K >> 1)) : kOOB;
+      bsoff[q] = ok ? (uint32_t)(wrow * (K >> 4)) : kOOB;
+    }
+    auto issue = [&](int kt, RegAP<ACT>& ra, RegBP& rb) {
+      const uint32_t k0 = (uint32_t)kt * BK;
+#pragma unroll
+      for (int q = 0; q < 2; q++) {
+        const uint32_t kh = k0 + 32u * ((pt + 256 * q) & 1);
+        rb.s[q] = __builtin_amdgcn_raw_buffer_load_b16(sr, (bsoff[q] + (kh >> 4)) | past(Ku, kh), 0, 0);
+        rb.c[q] = __builtin_amdgcn_raw_buffer_load_b128(wr, (bwoff[q] + (kh >> 1)) | past(Ku, kh), 0, 0);
+      }
+#pragma unroll
+      for (int q = 0; q < 8; q++) {
+        const int j = (pt + 256 * q) & 7;
+        const uint32_t k = k0 + 8u * j;
+        if (ACT == 0) {
+          ra.v[q] = __builtin_amdgcn_raw_buffer_load_b128(xr, (xoff[q] + 2u * k) | past(Ku, k), 0, 0);
+        } else {
+          ra.c[q] = __builtin_amdgcn_raw_buffer_load_b32(xr, (xoff[q] + (k >> 1)) | past(Ku, k), 0, 0);
+          ra.s[q] = __builtin_amdgcn_raw_buffer_load_b8(xsr, (xsoff[q] + (k >> 4)) | past(Ku, k), 0, 0);
+        }
+      }
+    };
+    auto write_stage = [&](const RegAP<ACT>& ra, const RegBP& rb, int buf) {
+      uint16_t* da = As + buf * (BM * LDA);
+#pragma unroll
+      for (int q = 0; q < 8; q++) {
+        const int c = pt + 256 * q;
+        const int row = c >> 3, j = c & 7;
+        u32x4 v;
+        if (ACT == 0) v = ra.v[q];
+        else v = decode8(ra.c[q], e4m3_to_f32<0>(ra.s[q]));  // exact BF16 activations
+        *reinterpret_cast<u32x4*>(da + row * LDA + 8 * j) = v;
+      }
+#pragma unroll
+      for (int q = 0; q < 2; q++) {
+        const int c = pt + 256 * q;
+        const int bc = c >> 1, bh = c & 1;
+        uint16_t* db = Bs + buf * (BN * LDA) + bc * LDA + 32 * bh;
+        const float s0 = e4m3_to_f32<0>(rb.s[q]), s1 = e4m3_to_f32<1>(rb.s[q]);
+#pragma unroll
+        for (int d = 0; d < 4; d++)
+          *reinterpret_cast<u32x4*>(db + 8 * d) = decode8(rb.c[q][d], d < 2 ? s0 : s1);
+      }
+    };
+    RegAP<ACT> ra[2];
+    RegBP rb[2];
+    issue(0, ra[0], rb[0]);
+    issue(1, ra[1], rb[1]);
+    write_stage(ra[0], rb[0], 0);
+    issue(2, ra[0], rb[0]);
+    __syncthreads();  // stage 0 ready
+    auto pstep = [&](int kt, RegAP<ACT>& ran, RegBP& rbn) {
+      write_stage(ran, rbn, (kt + 1) & 1);
+      issue(kt + 3, ran, rbn);
+      __syncthreads();
+    };
+    for (int kt = 0; kt < KT2; kt += 2) {
+      pstep(kt, ra[1], rb[1]);
+      pstep(kt + 1, ra[0], rb[0]);
+    }
+    if (SWIGLU) {  // the consumers' two epilogue barriers
+      __syncthreads();
+      __syncthreads();
+    }
+    return;
+  }
+
+  // ---------------- consumers: 8 waves ----------------
+  const int wm = wave >> 2, wn = wave & 3;
+  const int col = lane & 31;
+  const int h = lane >> 5;
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int mt = 0; mt < 4; mt++)
+#pragma unroll
+    for (int st = 0; st < 2; st++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) acc[mt][st][r] = 0.f;
+  __syncthreads();  // stage 0 ready
+  for (int kt = 0; kt < KT2; kt++) {
+    const uint16_t* sa = As + (kt & 1) * (BM * LDA) + (128 * wm + col) * LDA + 32 * h;
+    const uint16_t* sb = Bs + (kt & 1) * (BN * LDA) + (64 * wn + col) * LDA + 32 * h;
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      u32x4 B[2];
+#pragma unroll
+      for (int st = 0; st < 2; st++)
+        B[st] = *reinterpret_cast<const u32x4*>(sb + 32 * st * LDA + 8 * j);
+#pragma unroll
+      for (int mt = 0; mt < 4; mt++) {
+        const u32x4 A = *reinterpret_cast<const u32x4*>(sa + 32 * mt * LDA + 8 * j);
+#pragma unroll
+        for (int st = 0; st < 2; st++) acc[mt][st] = mfma32(A, B[st], acc[mt][st]);
+      }
+    }
+    __syncthreads();
+  }
+
+  if (SWIGLU) {
+    // up waves -> LDS (their own register layout) -> gate waves of the same rows
+    float* xch = reinterpret_cast<float*>(lds);  // [2 wm][2 wn][4 mt][2 st][16 r][64 lanes]
+    __syncthreads();  // every wave is done with the operand stages
+    if (wn >= 2) {
+#pragma unroll
+      for (int mt = 0; mt < 4; mt++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) {
+          const int lrow = 128 * wm + 32 * mt + 8 * (r >> 2) + 4 * h + (r & 3);
+          const int64_t xrow = row_x[lrow];
+          const float f = (ACT == 0 || xrow < 0) ? ts : a.x_ts[xrow] * ts;
+#pragma unroll
+          for (int st = 0; st < 2; st++)
+            xch[((((wm * 2 + (wn - 2)) * 4 + mt) * 2 + st) * 16 + r) * 64 + lane] = acc[mt][st][r] * f;
+        }
+    }
+    __syncthreads();
+    if (wn < 2) {
+#pragma unroll
+      for (int mt = 0; mt < 4; mt++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) {
+          const int lrow = 128 * wm + 32 * mt + 8 * (r >> 2) + 4 * h + (r & 3);
+          const int64_t route = row_route[lrow];
+          if (route < 0) continue;
+          const int64_t xrow = row_x[lrow];
+          const float f = (ACT == 0) ? ts : a.x_ts[xrow] * ts;
+#pragma unroll
+          for (int st = 0; st < 2; st++) {
+            const int64_t n = cb * (BN / 2) + 64 * wn + 32 * st + col;
+            if (n >= half) continue;
+            const float g = acc[mt][st][r] * f;
+            const float u = xch[((((wm * 2 + wn) * 4 + mt) * 2 + st) * 16 + r) * 64 + lane];
+            const float silu = g / (1.0f + expf(-g));
+            a.a_out[route * half + n] = (uint16_t)f32_to_bf16_rne(silu * u);
+          }
+        }
+    }
+    return;
+  }
+#pragma unroll
+  for (int mt = 0; mt < 4; mt++) {
+#pragma unroll
+    for (int r = 0; r < 16; r++) {
+      const int lrow = 128 * wm + 32 * mt + 8 * (r >> 2) + 4 * h + (r & 3);
+      const int64_t route = row_route[lrow];
+      if (route < 0) continue;
+      const int64_t xrow = row_x[lrow];
+      const float f = (ACT == 0) ? ts : a.x_ts[xrow] * ts;
+#pragma unroll
+      for (int st = 0; st < 2; st++) {
+        const int64_t n = cb * BN + 64 * wn + 32 * st + col;
+        if (n < N) a.y[route * a.ldy + n] = acc[mt][st][r] * f;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
 // gemm_splitk: problems whose 64 x 256 tiles leave most CUs idle (e.g. M = 512, N = 4096:
 // 128 tiles). A 64 (M) x 128 (N) tile on sixteen waves: four groups of four waves take
 // the four quarters of K, each wave computing 64 x 32 (two 32x32x16 subtiles) with its
@@ -852,39 +1115,71 @@ bool use_wide(int64_t M, int64_t N) {
   return ((M + kWideBM - 1) / kWideBM) * ((N + BN - 1) / BN) >= 256;
 }
 
-// grouped form: 128-route tiles, two workgroups per CU
+// grouped form: 128-route tiles, two workgroups per CU; 64-route tiles for the routes
+// past each expert's first 256 when the wide grouped form takes those
 constexpr int kGroupedMT = 4;
+constexpr int kGroupedRestMT = 1;
 
-template <int ACT>
+template <int MT, int ACT>
 hipError_t launch_grouped_mt(const GemmArgs& a, int64_t max_tiles, hipStream_t stream) {
-  constexpr int BM = 32 * kGroupedMT;
+  constexpr int BM = 32 * MT;
   const size_t lds = 2 * (size_t)BM * LDA * sizeof(uint16_t);
   // whole groups of eight tiles (the tiles past the list's end return at once)
   const int64_t tiles8 = (max_tiles + 7) / 8 * 8;
   if (a.a_out) {
     const int64_t blocks = tiles8 * (((a.N >> 1) + BN / 2 - 1) / (BN / 2));
-    const size_t xch = (size_t)2 * kGroupedMT * 2 * 16 * 64 * sizeof(float);
-    hipLaunchKernelGGL((gemm_kernel<kGroupedMT, ACT, true, true>), dim3((uint32_t)blocks),
+    const size_t xch = (size_t)2 * MT * 2 * 16 * 64 * sizeof(float);
+    hipLaunchKernelGGL((gemm_kernel<MT, ACT, true, true>), dim3((uint32_t)blocks),
                        dim3(256), lds > xch ? lds : xch, stream, a);
   } else {
     const int64_t blocks = tiles8 * ((a.N + BN - 1) / BN);
-    hipLaunchKernelGGL((gemm_kernel<kGroupedMT, ACT, true>), dim3((uint32_t)blocks), dim3(256),
+    hipLaunchKernelGGL((gemm_kernel<MT, ACT, true>), dim3((uint32_t)blocks), dim3(256),
                        lds, stream, a);
+  }
+  return hipGetLastError();
+}
+
+template <int ACT>
+hipError_t launch_grouped_wide(const GemmArgs& a, int64_t max_active, hipStream_t stream) {
+  const size_t lds = 2 * (size_t)(kWideBM + BN) * LDA * sizeof(uint16_t);
+  const int64_t act8 = (max_active + 7) / 8 * 8;
+  if (a.a_out) {
+    const int64_t blocks = act8 * (((a.N >> 1) + BN / 2 - 1) / (BN / 2));
+    hipLaunchKernelGGL((gemm_wide_grouped<ACT, true>), dim3((uint32_t)blocks), dim3(768), lds,
+                       stream, a);
+  } else {
+    const int64_t blocks = act8 * ((a.N + BN - 1) / BN);
+    hipLaunchKernelGGL((gemm_wide_grouped<ACT, false>), dim3((uint32_t)blocks), dim3(768), lds,
+                       stream, a);
   }
   return hipGetLastError();
 }
 
 }  // namespace
 
-int gemm_grouped_tile_rows() { return 32 * kGroupedMT; }
+int gemm_grouped_tile_rows(bool wide) { return 32 * (wide ? kGroupedRestMT : kGroupedMT); }
 
 hipError_t launch_gemm_grouped(const GemmArgs& a, int act_kind, int64_t max_tiles,
                                hipStream_t stream) {
   switch (act_kind) {
-    case 0: return launch_grouped_mt<0>(a, max_tiles, stream);
-    case 1: return launch_grouped_mt<1>(a, max_tiles, stream);
+    case 0: return launch_grouped_mt<kGroupedMT, 0>(a, max_tiles, stream);
+    case 1: return launch_grouped_mt<kGroupedMT, 1>(a, max_tiles, stream);
     default: return hipErrorInvalidValue;
   }
+}
+
+// the wide grouped form: each active expert's first routes in 256-route tiles, then the
+// rest of the routes (the tile list) in 64-route tiles
+hipError_t launch_gemm_grouped_wide(const GemmArgs& a, int act_kind, int64_t max_active,
+                                    int64_t max_tiles, hipStream_t stream) {
+  if (act_kind != 0 && act_kind != 1) return hipErrorInvalidValue;
+  // the short launch of the remaining routes first: the rows a following combine reads
+  // are then the wide launch's, written last
+  hipError_t e = act_kind == 0 ? launch_grouped_mt<kGroupedRestMT, 0>(a, max_tiles, stream)
+                               : launch_grouped_mt<kGroupedRestMT, 1>(a, max_tiles, stream);
+  if (e != hipSuccess) return e;
+  return act_kind == 0 ? launch_grouped_wide<0>(a, max_active, stream)
+                       : launch_grouped_wide<1>(a, max_active, stream);
 }
 
 // Largest activation row pitch (elements) the GEMM's 32-bit buffer offsets can address

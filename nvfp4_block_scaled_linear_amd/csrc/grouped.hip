@@ -30,7 +30,8 @@ __device__ __forceinline__ void zero_route_row(void* out, int64_t bytes, int64_t
 }
 
 // Tile list of the GEMM path: expert e's routes sorted[off, off + cnt) split into tiles
-// of ws.tile_rows routes; tile_off is e's first tile.
+// of ws.tile_rows routes; tile_off is e's first tile. With ws.main_rows, the list holds
+// only the routes past each expert's first main_rows (the wide grouped form takes those).
 __device__ __forceinline__ void write_tiles(const RouteWorkspace& ws, int e, int32_t off,
                                             int32_t cnt, int32_t tile_off) {
   const int32_t nt = (cnt + ws.tile_rows - 1) / ws.tile_rows;
@@ -76,7 +77,8 @@ __device__ __forceinline__ void expert_scans(const RouteWorkspace& ws, int E, in
   for (int e0 = 0; e0 < E; e0 += nt) {
     const int e = e0 + tid;
     const int32_t c = e < E ? cnt[e] : 0;
-    const int32_t ntile = ws.tile_rows > 0 ? (c + ws.tile_rows - 1) / ws.tile_rows : 0;
+    const int32_t rest = c > ws.main_rows ? c - ws.main_rows : 0;  // routes in the tile list
+    const int32_t ntile = ws.tile_rows > 0 ? (rest + ws.tile_rows - 1) / ws.tile_rows : 0;
     int32_t tot, tot_a, tot_t;
     const int32_t o = block_exclusive_scan(c, wsum, &tot) + run;
     const int32_t a = block_exclusive_scan(c > 0 ? 1 : 0, wsum, &tot_a) + act_run;
@@ -89,7 +91,7 @@ __device__ __forceinline__ void expert_scans(const RouteWorkspace& ws, int E, in
         *reinterpret_cast<int4*>(ws.slots + kSlotInts * a) = make_int4(e, o, o + c, n);
         if (slot_of) slot_of[e] = a;
       }
-      if (ntile > 0) write_tiles(ws, e, o, c, to);
+      if (ntile > 0) write_tiles(ws, e, o + (c - rest), rest, to);
       cnt[e] = o;
     }
     run += tot;

@@ -69,14 +69,24 @@ struct GemmArgs {
   // grouped SwiGLU form (NULL otherwise): BF16 rows [routes][N/2] of
   // bf16(silu(h[n]) * h[n + N/2])
   uint16_t* a_out;
+  // grouped wide form: the active experts, one 256-route tile each (their first routes)
+  const int32_t* active;     // [E]
+  const int32_t* n_active;   // [1]
 };
 
 hipError_t launch_gemm(const GemmArgs& a, int act_kind, hipStream_t stream);
 // grouped form: max_tiles bounds the tile list the route grouping writes
 hipError_t launch_gemm_grouped(const GemmArgs& a, int act_kind, int64_t max_tiles,
                                hipStream_t stream);
-// routes per tile of the grouped GEMM
-int gemm_grouped_tile_rows();
+// routes per tile of the grouped GEMM's tile list: with `wide`, the routes past each
+// expert's first kWideGroupedRows, which the wide grouped form takes
+int gemm_grouped_tile_rows(bool wide);
+// grouped wide form: each active expert's first routes (up to its tile of 256) in one
+// 256 x 256-tile workgroup per column block, then the grouping's tile list of the rest;
+// max_active bounds the active list, max_tiles the tile list
+constexpr int kWideGroupedRows = 256;
+hipError_t launch_gemm_grouped_wide(const GemmArgs& a, int act_kind, int64_t max_active,
+                                    int64_t max_tiles, hipStream_t stream);
 // largest BF16 activation row pitch (elements) the GEMM's buffer offsets address
 int64_t gemm_max_ldx();
 
@@ -95,6 +105,8 @@ struct RouteWorkspace {
   int32_t* tiles;         // GEMM path: [n_tiles][2] (expert, first slot in `sorted`)
   int32_t* n_tiles;       // [1]
   int32_t tile_rows;      // GEMM path: routes per tile (0: no tile list)
+  int32_t main_rows;      // GEMM path: routes at the start of each expert's group that the
+                          // tile list leaves out (taken by the wide grouped form; 0: none)
   int32_t* chunk_counts;  // chunked grouping: [chunks][E] counts, then first slots
   int32_t* slots;         // [max_slots][kSlotInts] slot records, one per active expert in
                           // ascending id: (expert, begin, end, n, the expert's first n

@@ -509,6 +509,60 @@ def test_grouped_prefill_gemm_several_column_blocks(dev, o):
     assert_within(y, yr, b, "column blocks: combine")
 
 
+def test_grouped_wide_tiles_every_output_form(dev, o):
+    """Routes averaging >= 192 per expert take the wide grouped form: each expert's first
+    256 routes in one 256-route tile (wave-specialized), the rest in 64-route tiles. Here
+    1600 routes over 6 experts (some above 256, so both kinds of tile run), N = 544 (a
+    ragged third column block; half = 272, a ragged third gate block), K = 320 (an odd
+    number of 64-k steps), and dropped routes: every output of every kept route against the
+    oracle, dropped routes' rows zero, SwiGLU from the rows, the ordered combine,
+    determinism, and one route per token equal to the dense product bit for bit."""
+    E, N, K, T, k = 6, 544, 320, 400, 4
+    _say(f"grouped GEMM, wide tiles: E={E} N={N} K={K} T={T} k={k}")
+    wc, wsc, wts, oc, os_, ot, ids, rw, xb = _prefill_case(dev, o, E, N, K, T, k, 151)
+    counts = np.bincount(ids.ravel(), minlength=E)
+    assert counts.max() > 256 and counts.mean() >= 192, counts
+    ids[3, 1] = -1  # dropped routes (flagged, their rows zero)
+    ids[250, 3] = E + 2
+    x = to_dev_bf16(xb, dev)
+    ids_d = torch.from_numpy(ids).to(dev)
+    faults = torch.zeros(1, dtype=torch.int32, device=dev)
+    h_d = nv.grouped_linear(x, wc, wsc, wts, ids_d, faults=faults)
+    assert int(faults.item()) & nv.FAULT_BAD_ROUTE
+    h = h_d.cpu().numpy()
+    x64 = o.bf16_to_f64(xb)
+    for e in range(E):
+        routes = np.nonzero(ids.ravel() == e)[0]
+        wdq = o.dequant(oc[e], os_[e], ot[e:e + 1], per_row=False)
+        yr, b = o.linear_f64(x64[routes // k], wdq)
+        assert_within(h[routes], yr, b, f"wide tiles: expert {e} rows")
+    assert not np.any(h[3 * k + 1]) and not np.any(h[250 * k + 3])
+    assert torch.equal(nv.grouped_linear(x, wc, wsc, wts, ids_d), h_d)
+    a = nv.grouped_linear(x, wc, wsc, wts, ids_d, out_mode=nv.OUT_SWIGLU_BF16)
+    kept = np.nonzero((ids.ravel() >= 0) & (ids.ravel() < E))[0]
+    _swiglu_bits_check(o, a[torch.from_numpy(kept).to(dev)], h[kept], "wide tiles")
+    rw_d = torch.from_numpy(rw).to(dev)
+    y = nv.grouped_linear(x, wc, wsc, wts, ids_d, topk_w=rw_d, out_mode=nv.OUT_COMBINE)
+    assert torch.equal(nv.grouped_linear(x, wc, wsc, wts, ids_d, topk_w=rw_d,
+                                         out_mode=nv.OUT_COMBINE), y)
+    valid = (ids >= 0) & (ids < E)
+    yr, b = o.moe_down_combine(np.repeat(xb, k, axis=0), np.where(valid, ids, 0).astype(np.int32),
+                               np.where(valid, rw, 0.0).astype(np.float32), oc, os_, ot)
+    assert_within(y.cpu().numpy(), yr, b, "wide tiles: combine")
+    # one route per token (800 tokens over 3 experts): each expert's rows, from its wide
+    # tile and its 64-route tiles, equal the dense product (64-row kernel, same k order)
+    T1 = 800
+    ids1 = moe_routes(152, T1, 3, 1)[0].astype(np.int32)
+    x1b = act_bf16(153, T1, K)
+    x1 = to_dev_bf16(x1b, dev)
+    h1 = nv.grouped_linear(x1, wc[:3], wsc[:3], wts[:3], torch.from_numpy(ids1).to(dev))
+    for e in range(3):
+        toks = torch.from_numpy(np.nonzero(ids1[:, 0] == e)[0]).to(dev)
+        assert len(toks) > 256
+        dense = nv.linear(x1[toks].contiguous(), wc[e], wsc[e], wts[e:e + 1])
+        assert torch.equal(h1[toks], dense), e
+
+
 def test_moe_prefill_layer_full_shape(dev, o, moe):
     """The MoE layer at prompt size as the benchmark runs it: 4096 tokens over the 128
     experts, top-8 (32768 routes, the chunked grouping, six SwiGLU column blocks of the
@@ -572,6 +626,7 @@ def _w4a4_experts_case(dev, o, E, N, K, T, k, seed):
 
 
 @pytest.mark.parametrize("E,N,K,T,k", [(8, 320, 256, 512, 2),   # GEMM path (128 per expert)
+                                       (4, 320, 256, 560, 2),   # wide grouped form (280)
                                        (16, 192, 256, 4, 4)])    # streaming path (decode size)
 def test_grouped_w4a4_every_output_form(dev, o, E, N, K, T, k):
     """NVFP4 activations (quantized on the device, bit-exact with the oracle) through the
