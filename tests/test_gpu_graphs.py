@@ -95,7 +95,8 @@ def test_graph_quantize_per_tensor(dev):
                    [c, sc, ts], lambda: nv.quantize_act(w * 3, per_tensor=True))
 
 
-@pytest.mark.parametrize("T,E,k", [(4, 16, 4), (256, 8, 2)])  # decode-sized and GEMM paths
+# decode-sized, GEMM and wide GEMM paths (the last: 300 routes per expert on average)
+@pytest.mark.parametrize("T,E,k", [(4, 16, 4), (256, 8, 2), (600, 4, 2)])
 def test_graph_moe_layer(dev, T, E, k):
     """gate_up with SwiGLU, then down with the ordered combine reusing the grouping, in one
     graph, as the MoE layer runs them."""

@@ -1,9 +1,9 @@
 """The no-allocation grouped call (nvfp4_grouped_linear_noalloc, through the C ABI) against
 the workspace form (nvfp4_grouped_linear) on the same inputs: two calls in a row, the
 second smaller, in each output form, on the decode-sized (weight-streaming) and the
-prompt-sized (grouped GEMM) paths. The two forms run the same kernels, so their outputs
-must agree bit for bit; the workspace form is itself checked against the oracle by the
-MoE parity tests."""
+prompt-sized (grouped GEMM, and its wide form) paths. The two forms run the same kernels,
+so their outputs must agree bit for bit; the workspace form is itself checked against the
+oracle by the MoE parity tests."""
 import numpy as np
 import pytest
 import torch
@@ -51,6 +51,8 @@ def _pair(dev, x, w, ids_d, rw_d, out_mode, rows_per_route=False):
     [(32, 256, 512, 16, 8), (12, 96, 256, 3, 2)],
     # prompt-sized (grouped GEMM: >= 32 routes per expert), then a smaller prompt
     [(8, 320, 256, 512, 2), (4, 64, 128, 160, 1)],
+    # the grouped GEMM's wide form (>= 192 routes per expert), then a smaller prompt
+    [(4, 320, 256, 560, 2), (4, 64, 128, 160, 1)],
 ])
 def test_noalloc_matches_workspace_form(dev, o, case):
     for i, (E, N, K, T, k) in enumerate(case):
