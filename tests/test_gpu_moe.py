@@ -511,12 +511,13 @@ def test_grouped_prefill_gemm_several_column_blocks(dev, o):
 
 def test_grouped_wide_tiles_every_output_form(dev, o):
     """Routes averaging >= 192 per expert take the wide grouped form: each expert's first
-    256 routes in one 256-route tile (wave-specialized), the rest in 64-route tiles. Here
+    256 routes in one 256-route tile (wave-specialized), the rest in 32-route tiles. Here
     1600 routes over 6 experts (some above 256, so both kinds of tile run), N = 544 (a
     ragged third column block; half = 272, a ragged third gate block), K = 320 (an odd
     number of 64-k steps), and dropped routes: every output of every kept route against the
-    oracle, dropped routes' rows zero, SwiGLU from the rows, the ordered combine,
-    determinism, and one route per token equal to the dense product bit for bit."""
+    oracle, dropped routes' rows zero, padded activation rows, SwiGLU from the rows, the
+    ordered combine, determinism, and one route per token equal to the dense product bit
+    for bit."""
     E, N, K, T, k = 6, 544, 320, 400, 4
     _say(f"grouped GEMM, wide tiles: E={E} N={N} K={K} T={T} k={k}")
     wc, wsc, wts, oc, os_, ot, ids, rw, xb = _prefill_case(dev, o, E, N, K, T, k, 151)
@@ -538,6 +539,10 @@ def test_grouped_wide_tiles_every_output_form(dev, o):
         assert_within(h[routes], yr, b, f"wide tiles: expert {e} rows")
     assert not np.any(h[3 * k + 1]) and not np.any(h[250 * k + 3])
     assert torch.equal(nv.grouped_linear(x, wc, wsc, wts, ids_d), h_d)
+    # padded activation rows (pitch K + 24, NaN in the padding, which is never read)
+    xp = torch.full((T, K + 24), float("nan"), dtype=torch.bfloat16, device=dev)
+    xp[:, :K] = x
+    assert torch.equal(nv.grouped_linear(xp[:, :K], wc, wsc, wts, ids_d), h_d)
     a = nv.grouped_linear(x, wc, wsc, wts, ids_d, out_mode=nv.OUT_SWIGLU_BF16)
     kept = np.nonzero((ids.ravel() >= 0) & (ids.ravel() < E))[0]
     _swiglu_bits_check(o, a[torch.from_numpy(kept).to(dev)], h[kept], "wide tiles")
@@ -550,7 +555,7 @@ def test_grouped_wide_tiles_every_output_form(dev, o):
                                np.where(valid, rw, 0.0).astype(np.float32), oc, os_, ot)
     assert_within(y.cpu().numpy(), yr, b, "wide tiles: combine")
     # one route per token (800 tokens over 3 experts): each expert's rows, from its wide
-    # tile and its 64-route tiles, equal the dense product (64-row kernel, same k order)
+    # tile and its 32-route tiles, equal the dense product (64-row kernel, same k order)
     T1 = 800
     ids1 = moe_routes(152, T1, 3, 1)[0].astype(np.int32)
     x1b = act_bf16(153, T1, K)
