@@ -71,7 +71,12 @@ struct RegB {  // one K step of this lane's weight loads (two 32-column subtiles
 // matching 128 up columns N/2 + ... (waves 2, 3); the up waves hand their scaled results
 // to the gate waves through LDS in the same register layout, and the gate waves write
 // bf16_rne(silu(g) * u) to a_out, g and u being exactly the per-route rows' values.
-template <int MT, int ACT, bool GROUPED = false, bool SWIGLU = false>
+//
+// SB: the weight scales come in 16-byte pieces, four 64-k steps of one column per load
+// (K a multiple of 256, scale rows 16-byte aligned). A per-step 2-byte scale load touches
+// a cache line per column for 2 bytes, as many line lookups in the vector L1 as the code
+// loads themselves; the 16-byte piece serves four steps with one.
+template <int MT, int ACT, bool GROUPED = false, bool SWIGLU = false, bool SB = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_kernel(GemmArgs a) {
   constexpr int BM = 32 * MT;
   extern __shared__ __attribute__((aligned(16))) uint16_t lds_a[];  // [2][BM * LDA]
@@ -212,9 +217,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
     for (int st = 0; st < 2; st++) {
       rb.c[st] = __builtin_amdgcn_raw_buffer_load_b128(wr, (woff[st] + (kh >> 1)) | past(Ku, kh), 0, 0);
-      rb.s[st] = __builtin_amdgcn_raw_buffer_load_b16(sr, (soff[st] + (kh >> 4)) | past(Ku, kh), 0, 0);
+      if (!SB)
+        rb.s[st] = __builtin_amdgcn_raw_buffer_load_b16(sr, (soff[st] + (kh >> 4)) | past(Ku, kh), 0, 0);
     }
   };
+  // SB: the scales of steps [kt, kt + 4) (kt a multiple of 4): 4 bytes per step, this
+  // lane's two at byte 2h of each. The next piece is loaded once the current one's last
+  // step is decoded.
+  u32x4 sblk[2];  // [st]
+  auto issue_sb = [&](int kt) {
+    const uint32_t k0 = (uint32_t)kt * BK;
+#pragma unroll
+    for (int st = 0; st < 2; st++)
+      sblk[st] = __builtin_amdgcn_raw_buffer_load_b128(sr, (soff[st] + (k0 >> 4)) | past(Ku, k0), 0, 0);
+  };
+  const uint32_t hsh = 16u * h;
 
   auto write_a = [&](const RegA<MT, ACT>& ra, int buf) {
     uint16_t* dst = lds_a + buf * (BM * LDA);
@@ -244,22 +261,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
       for (int r = 0; r < 16; r++) acc[mt][st][r] = 0.f;
 
-  auto decode = [&](const RegB& rb, u32x4 (&Bd)[2][4]) {
+  // sw[st]: the step's two scale bytes in bytes 0 and 1 (SB: picked from the piece)
+  auto decode = [&](const RegB& rb, const uint32_t (&sw)[2], u32x4 (&Bd)[2][4]) {
 #pragma unroll
     for (int st = 0; st < 2; st++) {
-      const float s0 = e4m3_to_f32<0>(rb.s[st]);
-      const float s1 = e4m3_to_f32<1>(rb.s[st]);
+      const float s0 = e4m3_to_f32<0>(sw[st]);
+      const float s1 = e4m3_to_f32<1>(sw[st]);
 #pragma unroll
       for (int j = 0; j < 4; j++) Bd[st][j] = decode8(rb.c[st][j], j < 2 ? s0 : s1);
     }
+  };
+  // the scale words of step kt: without SB the step's own loads; with SB dword kt % 4 of
+  // the piece (compile-time in the unrolled loop)
+  auto scales = [&](const RegB& rb, auto stepc, uint32_t (&sw)[2]) {
+    constexpr int j = decltype(stepc)::value;
+#pragma unroll
+    for (int st = 0; st < 2; st++) sw[st] = SB ? sblk[st][j & 3] >> hsh : rb.s[st];
   };
 
   // One K step: refill the freed register sets with step kt + 2, multiply from LDS
   // buffer kt & 1 with this step's decoded weights while decoding step kt + 1's (the
   // decode's VALU work fills the MFMA pipeline's shadow), stage step kt + 1's
   // activations into the other buffer.
-  auto body = [&](int kt, RegA<MT, ACT>& ra_free, RegB& rb_free, RegA<MT, ACT>& ra_next,
+  // jc: kt % 4 as a compile-time constant (it selects the scale word with SB)
+  auto body = [&](auto jc, int kt, RegA<MT, ACT>& ra_free, RegB& rb_free, RegA<MT, ACT>& ra_next,
                   const RegB& rb_next, const u32x4 (&Bd)[2][4], u32x4 (&Bd_next)[2][4]) {
+    constexpr int j4 = decltype(jc)::value;
     issue(kt + 2, ra_free, rb_free);
     const uint16_t* src = lds_a + (kt & 1) * (BM * LDA);
 #pragma unroll
@@ -272,7 +299,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         for (int st = 0; st < 2; st++) acc[mt][st] = mfma32(A, Bd[st][j], acc[mt][st]);
       }
     }
-    decode(rb_next, Bd_next);
+    uint32_t sw[2];
+    scales(rb_next, std::integral_constant<int, (j4 + 1) & 3>{}, sw);
+    decode(rb_next, sw, Bd_next);
+    // step kt + 1 was the piece's last: load the next one (steps kt + 2 ... kt + 5)
+    if constexpr (SB && j4 == 2) issue_sb(kt + 2);
     // interleave: each MFMA followed by a share of the decode's VALU work, with the LDS
     // operand reads spread between them (NVFP4 activations: a smaller share per MFMA,
     // which keeps the 128-row grouped form within its 256 registers, no scratch)
@@ -290,14 +321,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   RegA<MT, ACT> ra0, ra1;
   RegB rb0, rb1;
   u32x4 Bd0[2][4], Bd1[2][4];
+  using I0 = std::integral_constant<int, 0>;
+  if (SB) issue_sb(0);
   issue(0, ra0, rb0);
   issue(1, ra1, rb1);
-  decode(rb0, Bd0);
+  {
+    uint32_t sw[2];
+    scales(rb0, I0{}, sw);
+    decode(rb0, sw, Bd0);
+  }
   write_a(ra0, 0);
   __syncthreads();
-  for (int kt = 0; kt < KT2; kt += 2) {
-    body(kt, ra0, rb0, ra1, rb1, Bd0, Bd1);
-    body(kt + 1, ra1, rb1, ra0, rb0, Bd1, Bd0);
+  if constexpr (SB) {
+    // K is whole 4-step pieces (KT2 = KT, a multiple of 4)
+    for (int kt = 0; kt < KT2; kt += 4) {
+      body(I0{}, kt, ra0, rb0, ra1, rb1, Bd0, Bd1);
+      body(std::integral_constant<int, 1>{}, kt + 1, ra1, rb1, ra0, rb0, Bd1, Bd0);
+      body(std::integral_constant<int, 2>{}, kt + 2, ra0, rb0, ra1, rb1, Bd0, Bd1);
+      body(std::integral_constant<int, 3>{}, kt + 3, ra1, rb1, ra0, rb0, Bd1, Bd0);
+    }
+  } else {
+    for (int kt = 0; kt < KT2; kt += 2) {
+      body(I0{}, kt, ra0, rb0, ra1, rb1, Bd0, Bd1);
+      body(std::integral_constant<int, 1>{}, kt + 1, ra1, rb1, ra0, rb0, Bd1, Bd0);
+    }
   }
 
   if (SWIGLU) {
@@ -389,7 +436,7 @@ struct RegBP {  // one K step of a producer lane's weight chunks (two of 32 code
   uint32_t s[2];
 };
 
-template <int ACT>
+template <int ACT, bool SB = false>
 __global__ __launch_bounds__(768) void gemm_wide(GemmArgs a) {
   constexpr int BM = kWideBM;
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
@@ -452,7 +499,8 @@ __global__ __launch_bounds__(768) void gemm_wide(GemmArgs a) {
 #pragma unroll
       for (int q = 0; q < 2; q++) {
         const uint32_t kh = k0 + 32u * ((pt + 256 * q) & 1);
-        rb.s[q] = __builtin_amdgcn_raw_buffer_load_b16(sr, (bsoff[q] + (kh >> 4)) | past(Ku, kh), 0, 0);
+        if (!SB)
+          rb.s[q] = __builtin_amdgcn_raw_buffer_load_b16(sr, (bsoff[q] + (kh >> 4)) | past(Ku, kh), 0, 0);
         rb.c[q] = __builtin_amdgcn_raw_buffer_load_b128(wr, (bwoff[q] + (kh >> 1)) | past(Ku, kh), 0, 0);
       }
 #pragma unroll
@@ -471,7 +519,7 @@ __global__ __launch_bounds__(768) void gemm_wide(GemmArgs a) {
         }
       }
     };
-    auto write_stage = [&](const RegAP<ACT>& ra, const RegBP& rb, int buf) {
+    auto write_stage = [&](const RegAP<ACT>& ra, const RegBP& rb, const uint32_t (&sw)[2], int buf) {
       uint16_t* da = As + buf * (BM * LDA);
 #pragma unroll
       for (int q = 0; q < 8; q++) {
@@ -487,29 +535,68 @@ __global__ __launch_bounds__(768) void gemm_wide(GemmArgs a) {
         const int c = pt + 256 * q;
         const int bc = c >> 1, bh = c & 1;
         uint16_t* db = Bs + buf * (BN * LDA) + bc * LDA + 32 * bh;
-        const float s0 = e4m3_to_f32<0>(rb.s[q]), s1 = e4m3_to_f32<1>(rb.s[q]);
+        const float s0 = e4m3_to_f32<0>(sw[q]), s1 = e4m3_to_f32<1>(sw[q]);
 #pragma unroll
         for (int d = 0; d < 4; d++)
           *reinterpret_cast<u32x4*>(db + 8 * d) = decode8(rb.c[q][d], d < 2 ? s0 : s1);
       }
     };
+    // SB: the scales of steps [kt, kt + 4) (kt a multiple of 4), 4 bytes per step, this
+    // lane's two at byte 2 * (lane's K half) of each. The next piece is loaded once the
+    // current one's last step is staged.
+    u32x4 sblk[2];  // [q]
+    auto issue_sb = [&](int kt) {
+      const uint32_t k0 = (uint32_t)kt * BK;
+#pragma unroll
+      for (int q = 0; q < 2; q++)
+        sblk[q] = __builtin_amdgcn_raw_buffer_load_b128(sr, (bsoff[q] + (k0 >> 4)) | past(Ku, k0), 0, 0);
+    };
+    const uint32_t hsh = 16u * (pt & 1);
+    // the scale words of step j (mod 4, compile-time)
+    auto scales = [&](const RegBP& rb, auto stepc, uint32_t (&sw)[2]) {
+      constexpr int j = decltype(stepc)::value;
+#pragma unroll
+      for (int q = 0; q < 2; q++) sw[q] = SB ? sblk[q][j & 3] >> hsh : rb.s[q];
+    };
     RegAP<ACT> ra[2];
     RegBP rb[2];
+    using I0 = std::integral_constant<int, 0>;
+    if (SB) issue_sb(0);
     issue(0, ra[0], rb[0]);
     issue(1, ra[1], rb[1]);
-    write_stage(ra[0], rb[0], 0);
+    {
+      uint32_t sw[2];
+      scales(rb[0], I0{}, sw);
+      write_stage(ra[0], rb[0], sw, 0);
+    }
     issue(2, ra[0], rb[0]);
     __syncthreads();  // stage 0 ready
     // step kt: write step kt + 1's stage from set (kt + 1) % 2, refill that set with step
     // kt + 3; one barrier per step, matched by the consumers'
-    auto pstep = [&](int kt, RegAP<ACT>& ran, RegBP& rbn) {
-      write_stage(ran, rbn, (kt + 1) & 1);
+    // jc: kt % 4 as a compile-time constant (it selects the scale word with SB)
+    auto pstep = [&](auto jc, int kt, RegAP<ACT>& ran, RegBP& rbn) {
+      constexpr int j4 = decltype(jc)::value;
+      uint32_t sw[2];
+      scales(rbn, std::integral_constant<int, (j4 + 1) & 3>{}, sw);
+      write_stage(ran, rbn, sw, (kt + 1) & 1);
+      // step kt + 1 was the piece's last: load the next one (steps kt + 2 ... kt + 5)
+      if constexpr (SB && j4 == 2) issue_sb(kt + 2);
       issue(kt + 3, ran, rbn);
       __syncthreads();
     };
-    for (int kt = 0; kt < KT2; kt += 2) {
-      pstep(kt, ra[1], rb[1]);
-      pstep(kt + 1, ra[0], rb[0]);
+    if constexpr (SB) {
+      // K is whole 4-step pieces (KT2 = KT, a multiple of 4)
+      for (int kt = 0; kt < KT2; kt += 4) {
+        pstep(I0{}, kt, ra[1], rb[1]);
+        pstep(std::integral_constant<int, 1>{}, kt + 1, ra[0], rb[0]);
+        pstep(std::integral_constant<int, 2>{}, kt + 2, ra[1], rb[1]);
+        pstep(std::integral_constant<int, 3>{}, kt + 3, ra[0], rb[0]);
+      }
+    } else {
+      for (int kt = 0; kt < KT2; kt += 2) {
+        pstep(I0{}, kt, ra[1], rb[1]);
+        pstep(std::integral_constant<int, 1>{}, kt + 1, ra[0], rb[0]);
+      }
     }
     return;
   }
@@ -575,7 +662,7 @@ __global__ __launch_bounds__(768) void gemm_wide(GemmArgs a) {
 // matching 128 up columns N/2 + ... (wn = 2, 3); the up waves hand their scaled results
 // to the gate waves through LDS, and the gate waves write bf16_rne(silu(g) * u).
 // ---------------------------------------------------------------------------------------
-template <int ACT, bool SWIGLU>
+template <int ACT, bool SWIGLU, bool SB = false>
 __global__ __launch_bounds__(768) void gemm_wide_grouped(GemmArgs a) {
   constexpr int BM = kWideBM;
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
@@ -675,7 +762,8 @@ __global__ __launch_bounds__(768) void gemm_wide_grouped(GemmArgs a) {
 #pragma unroll
       for (int q = 0; q < 2; q++) {
         const uint32_t kh = k0 + 32u * ((pt + 256 * q) & 1);
-        rb.s[q] = __builtin_amdgcn_raw_buffer_load_b16(sr, (bsoff[q] + (kh >> 4)) | past(Ku, kh), 0, 0);
+        if (!SB)
+          rb.s[q] = __builtin_amdgcn_raw_buffer_load_b16(sr, (bsoff[q] + (kh >> 4)) | past(Ku, kh), 0, 0);
         rb.c[q] = __builtin_amdgcn_raw_buffer_load_b128(wr, (bwoff[q] + (kh >> 1)) | past(Ku, kh), 0, 0);
       }
 #pragma unroll
@@ -690,7 +778,7 @@ __global__ __launch_bounds__(768) void gemm_wide_grouped(GemmArgs a) {
         }
       }
     };
-    auto write_stage = [&](const RegAP<ACT>& ra, const RegBP& rb, int buf) {
+    auto write_stage = [&](const RegAP<ACT>& ra, const RegBP& rb, const uint32_t (&sw)[2], int buf) {
       uint16_t* da = As + buf * (BM * LDA);
 #pragma unroll
       for (int q = 0; q < 8; q++) {
@@ -706,27 +794,66 @@ __global__ __launch_bounds__(768) void gemm_wide_grouped(GemmArgs a) {
         const int c = pt + 256 * q;
         const int bc = c >> 1, bh = c & 1;
         uint16_t* db = Bs + buf * (BN * LDA) + bc * LDA + 32 * bh;
-        const float s0 = e4m3_to_f32<0>(rb.s[q]), s1 = e4m3_to_f32<1>(rb.s[q]);
+        const float s0 = e4m3_to_f32<0>(sw[q]), s1 = e4m3_to_f32<1>(sw[q]);
 #pragma unroll
         for (int d = 0; d < 4; d++)
           *reinterpret_cast<u32x4*>(db + 8 * d) = decode8(rb.c[q][d], d < 2 ? s0 : s1);
       }
     };
+    // SB: the scales of steps [kt, kt + 4) (kt a multiple of 4), 4 bytes per step, this
+    // lane's two at byte 2 * (lane's K half) of each. The next piece is loaded once the
+    // current one's last step is staged.
+    u32x4 sblk[2];  // [q]
+    auto issue_sb = [&](int kt) {
+      const uint32_t k0 = (uint32_t)kt * BK;
+#pragma unroll
+      for (int q = 0; q < 2; q++)
+        sblk[q] = __builtin_amdgcn_raw_buffer_load_b128(sr, (bsoff[q] + (k0 >> 4)) | past(Ku, k0), 0, 0);
+    };
+    const uint32_t hsh = 16u * (pt & 1);
+    // the scale words of step j (mod 4, compile-time)
+    auto scales = [&](const RegBP& rb, auto stepc, uint32_t (&sw)[2]) {
+      constexpr int j = decltype(stepc)::value;
+#pragma unroll
+      for (int q = 0; q < 2; q++) sw[q] = SB ? sblk[q][j & 3] >> hsh : rb.s[q];
+    };
     RegAP<ACT> ra[2];
     RegBP rb[2];
+    using I0 = std::integral_constant<int, 0>;
+    if (SB) issue_sb(0);
     issue(0, ra[0], rb[0]);
     issue(1, ra[1], rb[1]);
-    write_stage(ra[0], rb[0], 0);
+    {
+      uint32_t sw[2];
+      scales(rb[0], I0{}, sw);
+      write_stage(ra[0], rb[0], sw, 0);
+    }
     issue(2, ra[0], rb[0]);
     __syncthreads();  // stage 0 ready
-    auto pstep = [&](int kt, RegAP<ACT>& ran, RegBP& rbn) {
-      write_stage(ran, rbn, (kt + 1) & 1);
+    // jc: kt % 4 as a compile-time constant (it selects the scale word with SB)
+    auto pstep = [&](auto jc, int kt, RegAP<ACT>& ran, RegBP& rbn) {
+      constexpr int j4 = decltype(jc)::value;
+      uint32_t sw[2];
+      scales(rbn, std::integral_constant<int, (j4 + 1) & 3>{}, sw);
+      write_stage(ran, rbn, sw, (kt + 1) & 1);
+      // step kt + 1 was the piece's last: load the next one (steps kt + 2 ... kt + 5)
+      if constexpr (SB && j4 == 2) issue_sb(kt + 2);
       issue(kt + 3, ran, rbn);
       __syncthreads();
     };
-    for (int kt = 0; kt < KT2; kt += 2) {
-      pstep(kt, ra[1], rb[1]);
-      pstep(kt + 1, ra[0], rb[0]);
+    if constexpr (SB) {
+      // K is whole 4-step pieces (KT2 = KT, a multiple of 4)
+      for (int kt = 0; kt < KT2; kt += 4) {
+        pstep(I0{}, kt, ra[1], rb[1]);
+        pstep(std::integral_constant<int, 1>{}, kt + 1, ra[0], rb[0]);
+        pstep(std::integral_constant<int, 2>{}, kt + 2, ra[1], rb[1]);
+        pstep(std::integral_constant<int, 3>{}, kt + 3, ra[0], rb[0]);
+      }
+    } else {
+      for (int kt = 0; kt < KT2; kt += 2) {
+        pstep(I0{}, kt, ra[1], rb[1]);
+        pstep(std::integral_constant<int, 1>{}, kt + 1, ra[0], rb[0]);
+      }
     }
     if (SWIGLU) {  // the consumers' two epilogue barriers
       __syncthreads();
@@ -1091,12 +1218,22 @@ hipError_t launch_splitk(const GemmArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Weight scales in 16-byte pieces of four 64-k steps: K whole pieces and the scale rows
+// 16-byte aligned (with K a multiple of 256 every row is, once the base is).
+bool scale_pieces(const GemmArgs& a) {
+  return a.K % (4 * BK) == 0 && (uintptr_t)a.w_scales % 16 == 0;
+}
+
 template <int MT, int ACT>
 hipError_t launch_mt(const GemmArgs& a, hipStream_t stream) {
   constexpr int BM = 32 * MT;
   const int64_t blocks = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
   const size_t lds = 2 * (size_t)BM * LDA * sizeof(uint16_t);
-  hipLaunchKernelGGL((gemm_kernel<MT, ACT>), dim3((uint32_t)blocks), dim3(256), lds, stream, a);
+  if (scale_pieces(a))
+    hipLaunchKernelGGL((gemm_kernel<MT, ACT, false, false, true>), dim3((uint32_t)blocks), dim3(256),
+                       lds, stream, a);
+  else
+    hipLaunchKernelGGL((gemm_kernel<MT, ACT>), dim3((uint32_t)blocks), dim3(256), lds, stream, a);
   return hipGetLastError();
 }
 
@@ -1104,7 +1241,10 @@ template <int ACT>
 hipError_t launch_wide(const GemmArgs& a, hipStream_t stream) {
   const int64_t blocks = ((a.M + kWideBM - 1) / kWideBM) * ((a.N + BN - 1) / BN);
   const size_t lds = 2 * (size_t)(kWideBM + BN) * LDA * sizeof(uint16_t);
-  hipLaunchKernelGGL((gemm_wide<ACT>), dim3((uint32_t)blocks), dim3(768), lds, stream, a);
+  if (scale_pieces(a))
+    hipLaunchKernelGGL((gemm_wide<ACT, true>), dim3((uint32_t)blocks), dim3(768), lds, stream, a);
+  else
+    hipLaunchKernelGGL((gemm_wide<ACT>), dim3((uint32_t)blocks), dim3(768), lds, stream, a);
   return hipGetLastError();
 }
 
@@ -1126,15 +1266,26 @@ hipError_t launch_grouped_mt(const GemmArgs& a, int64_t max_tiles, hipStream_t s
   const size_t lds = 2 * (size_t)BM * LDA * sizeof(uint16_t);
   // whole groups of eight tiles (the tiles past the list's end return at once)
   const int64_t tiles8 = (max_tiles + 7) / 8 * 8;
+  // (the 128-route form has no registers to spare for the pieces)
+  constexpr bool kSB = MT <= 2;
+  const bool sb = kSB && scale_pieces(a);
   if (a.a_out) {
     const int64_t blocks = tiles8 * (((a.N >> 1) + BN / 2 - 1) / (BN / 2));
     const size_t xch = (size_t)2 * MT * 2 * 16 * 64 * sizeof(float);
-    hipLaunchKernelGGL((gemm_kernel<MT, ACT, true, true>), dim3((uint32_t)blocks),
-                       dim3(256), lds > xch ? lds : xch, stream, a);
+    if (sb)
+      hipLaunchKernelGGL((gemm_kernel<MT, ACT, true, true, kSB>), dim3((uint32_t)blocks),
+                         dim3(256), lds > xch ? lds : xch, stream, a);
+    else
+      hipLaunchKernelGGL((gemm_kernel<MT, ACT, true, true>), dim3((uint32_t)blocks),
+                         dim3(256), lds > xch ? lds : xch, stream, a);
   } else {
     const int64_t blocks = tiles8 * ((a.N + BN - 1) / BN);
-    hipLaunchKernelGGL((gemm_kernel<MT, ACT, true>), dim3((uint32_t)blocks), dim3(256),
-                       lds, stream, a);
+    if (sb)
+      hipLaunchKernelGGL((gemm_kernel<MT, ACT, true, false, kSB>), dim3((uint32_t)blocks),
+                         dim3(256), lds, stream, a);
+    else
+      hipLaunchKernelGGL((gemm_kernel<MT, ACT, true>), dim3((uint32_t)blocks), dim3(256),
+                         lds, stream, a);
   }
   return hipGetLastError();
 }
@@ -1143,14 +1294,23 @@ template <int ACT>
 hipError_t launch_grouped_wide(const GemmArgs& a, int64_t max_active, hipStream_t stream) {
   const size_t lds = 2 * (size_t)(kWideBM + BN) * LDA * sizeof(uint16_t);
   const int64_t act8 = (max_active + 7) / 8 * 8;
+  const bool sb = scale_pieces(a);
   if (a.a_out) {
     const int64_t blocks = act8 * (((a.N >> 1) + BN / 2 - 1) / (BN / 2));
-    hipLaunchKernelGGL((gemm_wide_grouped<ACT, true>), dim3((uint32_t)blocks), dim3(768), lds,
-                       stream, a);
+    if (sb)
+      hipLaunchKernelGGL((gemm_wide_grouped<ACT, true, true>), dim3((uint32_t)blocks), dim3(768),
+                         lds, stream, a);
+    else
+      hipLaunchKernelGGL((gemm_wide_grouped<ACT, true>), dim3((uint32_t)blocks), dim3(768), lds,
+                         stream, a);
   } else {
     const int64_t blocks = act8 * ((a.N + BN - 1) / BN);
-    hipLaunchKernelGGL((gemm_wide_grouped<ACT, false>), dim3((uint32_t)blocks), dim3(768), lds,
-                       stream, a);
+    if (sb)
+      hipLaunchKernelGGL((gemm_wide_grouped<ACT, false, true>), dim3((uint32_t)blocks), dim3(768),
+                         lds, stream, a);
+    else
+      hipLaunchKernelGGL((gemm_wide_grouped<ACT, false>), dim3((uint32_t)blocks), dim3(768), lds,
+                         stream, a);
   }
   return hipGetLastError();
 }

@@ -227,18 +227,21 @@ def test_w4a4_large_n(dev, o):
     assert_within(y, yr, b, "w4a4 N=12288")
 
 
-@pytest.mark.parametrize("M,N,K", [(17, 255, 64), (130, 600, 1056), (300, 130, 96), (64, 256, 32)])
+@pytest.mark.parametrize("M,N,K", [(17, 255, 64), (130, 600, 1056), (300, 130, 96), (64, 256, 32),
+                                   (40, 300, 512), (90, 770, 768)])
 def test_linear_gemm_ragged(dev, o, M, N, K):
     _say(f"gemm linear M={M} N={N} K={K}")
     y, yr, b = _linear_case(dev, o, M, N, K, seed=M * 3 + N)
     assert_within(y, yr, b, f"M={M} N={N} K={K}")
 
 
-def test_linear_wide_tiles_ragged(dev, o):
-    """The 256 x 256-tile GEMM (chosen when it gives every CU a workgroup) on ragged M, N
-    and an odd number of 64-k steps; sampled rows, including every row of the last,
-    partial row tile."""
-    M, N, K = 600, 86 * 256 - 100, 544
+@pytest.mark.parametrize("K", [544, 512])
+def test_linear_wide_tiles_ragged(dev, o, K):
+    """The 256 x 256-tile GEMM (chosen when it gives every CU a workgroup) on ragged M and
+    N, with an odd number of 64-k steps (K = 544: one 2-byte scale load per step) and with
+    K = 512 (the scales in 16-byte pieces of four steps); sampled rows, including every row
+    of the last, partial row tile."""
+    M, N = 600, 86 * 256 - 100
     _say(f"wide-tile gemm M={M} N={N} K={K} (sampled rows)")
     w = weight_f32(71, N, K)
     (c, s, t), oq = quantize_both(o, w, dev)
@@ -281,6 +284,39 @@ def test_linear_wide_tiles_padded_rows(dev, o):
     y4 = nv.linear(xc, c, s, t, x_scales=xs, x_ts=xt)
     yr4, b4 = o.linear_w4a4(oc[rows], os_[rows], ot[rows], *oq)
     assert_within(y4[torch.from_numpy(rows).to(dev)].cpu().numpy(), yr4, b4, "wide padded w4a4")
+
+
+def _offset_scales(s):
+    """A copy of the scales whose base is 2 bytes past a 16-byte boundary (the ABI's
+    minimum alignment), so the GEMMs take their per-step scale loads."""
+    buf = torch.empty(s.numel() + 16, dtype=torch.uint8, device=s.device)
+    v = buf[2:2 + s.numel()].view(s.shape)
+    assert v.data_ptr() % 16 == 2
+    v.copy_(s)
+    return v
+
+
+@pytest.mark.parametrize("M,N,K", [(40, 300, 512), (600, 86 * 256 - 100, 512), (90, 770, 768)])
+def test_gemm_scale_pieces_match_per_step_scales(dev, o, M, N, K):
+    """With K a multiple of 256 and 16-byte aligned scale rows, the GEMMs load the weight
+    scales in 16-byte pieces of four 64-k steps; with a scale base that is only 2-byte
+    aligned they load each step's two bytes. Both read the same scale values, so the outputs
+    are the same bits (64-row tiles, 256 x 256 tiles, BF16 and NVFP4 activations), and the
+    piece form matches the oracle."""
+    _say(f"gemm scale pieces vs per-step scales M={M} N={N} K={K}")
+    w = weight_f32(M + N, N, K)
+    (c, s, t), oq = quantize_both(o, w, dev)
+    xb = act_bf16(M + N + 1, M, K)
+    x = to_dev_bf16(xb, dev)
+    assert s.data_ptr() % 16 == 0
+    y = nv.linear(x, c, s, t)
+    assert torch.equal(nv.linear(x, c, _offset_scales(s), t), y)
+    rows = np.unique(np.r_[0, M - 1, np.arange(1, M, 13)])
+    yr, b = o.linear_f64(o.bf16_to_f64(xb[rows]), o.dequant(*oq, per_row=False))
+    assert_within(y[torch.from_numpy(rows).to(dev)].cpu().numpy(), yr, b, "scale pieces")
+    xc, xs, xt = nv.quantize_act(x)
+    y4 = nv.linear(xc, c, s, t, x_scales=xs, x_ts=xt)
+    assert torch.equal(nv.linear(xc, c, _offset_scales(s), t, x_scales=xs, x_ts=xt), y4)
 
 
 def test_linear_splitk_ragged(dev, o):

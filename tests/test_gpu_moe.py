@@ -509,16 +509,18 @@ def test_grouped_prefill_gemm_several_column_blocks(dev, o):
     assert_within(y, yr, b, "column blocks: combine")
 
 
-def test_grouped_wide_tiles_every_output_form(dev, o):
+@pytest.mark.parametrize("K", [320, 512])
+def test_grouped_wide_tiles_every_output_form(dev, o, K):
     """Routes averaging >= 192 per expert take the wide grouped form: each expert's first
     256 routes in one 256-route tile (wave-specialized), the rest in 32-route tiles. Here
     1600 routes over 6 experts (some above 256, so both kinds of tile run), N = 544 (a
     ragged third column block; half = 272, a ragged third gate block), K = 320 (an odd
-    number of 64-k steps), and dropped routes: every output of every kept route against the
+    number of 64-k steps, one 2-byte scale load per step) or 512 (the scales in 16-byte
+    pieces of four steps), and dropped routes: every output of every kept route against the
     oracle, dropped routes' rows zero, padded activation rows, SwiGLU from the rows, the
-    ordered combine, determinism, and one route per token equal to the dense product bit
-    for bit."""
-    E, N, K, T, k = 6, 544, 320, 400, 4
+    ordered combine, determinism, one route per token equal to the dense product bit for
+    bit, and (K = 512) the same bits from a scale copy that takes the per-step loads."""
+    E, N, T, k = 6, 544, 400, 4
     _say(f"grouped GEMM, wide tiles: E={E} N={N} K={K} T={T} k={k}")
     wc, wsc, wts, oc, os_, ot, ids, rw, xb = _prefill_case(dev, o, E, N, K, T, k, 151)
     counts = np.bincount(ids.ravel(), minlength=E)
@@ -566,6 +568,15 @@ def test_grouped_wide_tiles_every_output_form(dev, o):
         assert len(toks) > 256
         dense = nv.linear(x1[toks].contiguous(), wc[e], wsc[e], wts[e:e + 1])
         assert torch.equal(h1[toks], dense), e
+    if K % 256 == 0:
+        # scales 2 bytes past a 16-byte boundary: per-step scale loads, the same bits
+        buf = torch.empty(wsc.numel() + 16, dtype=torch.uint8, device=dev)
+        wsc2 = buf[2:2 + wsc.numel()].view(wsc.shape)
+        wsc2.copy_(wsc)
+        assert wsc.data_ptr() % 16 == 0 and wsc2.data_ptr() % 16 == 2
+        assert torch.equal(nv.grouped_linear(x, wc, wsc2, wts, ids_d), h_d)
+        assert torch.equal(nv.grouped_linear(x, wc, wsc2, wts, ids_d,
+                                             out_mode=nv.OUT_SWIGLU_BF16), a)
 
 
 def test_moe_prefill_layer_full_shape(dev, o, moe):
