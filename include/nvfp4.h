@@ -163,7 +163,10 @@ nvfp4_status nvfp4_quantize_act(int32_t in_type, const void* x, int64_t ldx, int
  *            bf16_rne(silu(g) * u) with g = h[0:N/2], u = h[N/2:N] of the route's fp32
  *            row h (SwiGLU rounded once to BF16, as the pages keep the down input in
  *            BF16 rounded to nearest even: issue #565 section 4, PR #914); h
- *            bit-equals the NVFP4_OUT_ROUTES row of the same call shape.
+ *            bit-equals the NVFP4_OUT_ROUTES row of the same call shape. silu(g) =
+ *            g / (1 + e^-g) is evaluated with the hardware's exp2 and reciprocal (a few
+ *            fp32 ulp), so a result is within one BF16 ulp of the correctly rounded one
+ *            and equal to it almost everywhere.
  *          NVFP4_OUT_COMBINE: needs topk_w [T][top_k] fp32; y is fp32 [T][N],
  *            y[t] = sum over t's routes in ascending expert id of
  *            (topk_w[t][j] * ts_e) * (x_row(r) w_e^T), accumulated in fp32 in that order

@@ -158,4 +158,13 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float v) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
+// silu(g) = g / (1 + e^-g), from the hardware's base-2 exponential and reciprocal (a few
+// fp32 ulp; the BF16 product it feeds rounds as the exact value does almost everywhere,
+// and never more than one BF16 ulp away). Large negative g: e^-g overflows to +inf and
+// the result is -0; large positive g: the result is g.
+__device__ __forceinline__ float silu(float g) {
+  const float e = __builtin_amdgcn_exp2f(g * -1.44269504088896341f);
+  return g * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
 }  // namespace nvfp4

@@ -389,8 +389,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             if (n >= half) continue;
             const float g = acc[mt][st][r] * f;
             const float u = xch[(((wave * MT + mt) * 2 + st) * 16 + r) * 64 + lane];
-            const float silu = g / (1.0f + expf(-g));
-            a.a_out[route * half + n] = (uint16_t)f32_to_bf16_rne(silu * u);
+            const float sg = silu(g);
+            a.a_out[route * half + n] = (uint16_t)f32_to_bf16_rne(sg * u);
           }
         }
     }
@@ -935,8 +935,8 @@ __global__ __launch_bounds__(768) void gemm_wide_grouped(GemmArgs a) {
             if (n >= half) continue;
             const float g = acc[mt][st][r] * f;
             const float u = xch[((((wm * 2 + wn) * 4 + mt) * 2 + st) * 16 + r) * 64 + lane];
-            const float silu = g / (1.0f + expf(-g));
-            a.a_out[route * half + n] = (uint16_t)f32_to_bf16_rne(silu * u);
+            const float sg = silu(g);
+            a.a_out[route * half + n] = (uint16_t)f32_to_bf16_rne(sg * u);
           }
         }
     }

@@ -700,7 +700,7 @@ __global__ __launch_bounds__(256) void stream_grouped(StreamArgs a) {
 // and the matching up rows N/2 + n0 + [0, 16) of its expert as two tiles, reduces both in
 // the same fixed order as reduce_store, and writes a = bf16_rne(silu(g) * u) where g and
 // u are exactly the per-route rows' fp32 values (sum times the same scale factor) and
-// silu(g) = g / (1 + expf(-g)).
+// silu is device.hpp's.
 template <int R, int ACT, bool SLDS>
 __global__ __launch_bounds__(256) void stream_grouped_swiglu(StreamArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -753,8 +753,8 @@ __global__ __launch_bounds__(256) void stream_grouped_swiglu(StreamArgs a) {
         }
         const float g = sg * f;
         const float u = su * f;
-        const float silu = g / (1.0f + expf(-g));
-        a.a_out[(int64_t)rr * half + n] = (uint16_t)f32_to_bf16_rne(silu * u);
+        const float sg = silu(g);
+        a.a_out[(int64_t)rr * half + n] = (uint16_t)f32_to_bf16_rne(sg * u);
       }
     }
     __syncthreads();
