@@ -67,10 +67,11 @@ struct RegB {  // one K step of this lane's weight loads (two 32-column subtiles
 // shape, epilogue) is the dense form's, so a route's row equals the dense product of its
 // activation row with the expert's weight.
 //
-// SWIGLU (grouped only): the tile's 256 columns are 128 gate columns (waves 0, 1) and the
-// matching 128 up columns N/2 + ... (waves 2, 3); the up waves hand their scaled results
-// to the gate waves through LDS in the same register layout, and the gate waves write
-// bf16_rne(silu(g) * u) to a_out, g and u being exactly the per-route rows' values.
+// SWIGLU (grouped only): the tile's 256 columns are 128 gate columns and the matching 128
+// up columns N/2 + ...; wave w takes gate columns 32w + [0, 32) of the block as its first
+// 32-column subtile and the matching up columns as its second, so each lane holds g and u
+// of the same outputs and writes bf16_rne(silu(g) * u) to a_out, g and u being exactly the
+// per-route rows' values.
 //
 // SB: the weight scales come in 16-byte pieces, four 64-k steps of one column per load
 // (K a multiple of 256, scale rows 16-byte aligned). A per-step 2-byte scale load touches
@@ -142,11 +143,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     rows_m = (M - m0) < BM ? (M - m0) : BM;
   }
   const int64_t rows_n = (N - n0) < BN ? (N - n0) : BN;
-  // this wave's first weight column: n0 + 64 * wave, or for SwiGLU the gate half (waves
-  // 0, 1: n0 = tile * 128) and the matching up half (waves 2, 3)
-  const int64_t wcol0 = SWIGLU ? (wave < 2 ? 0 : half) + cb_of * (BN / 2) + 64 * (wave & 1)
-                               : n0 + 64 * wave;
-  const int64_t col_end = SWIGLU ? (wave < 2 ? half : N) : N;
+  // this wave's weight column of subtile st and lane column col: n0 + 64 * wave + 32 st
+  // + col, or for SwiGLU gate column cb * 128 + 32 * wave + col (st = 0) and the matching
+  // up column N/2 + ... (st = 1)
+  const int64_t scol0 = SWIGLU ? cb_of * (BN / 2) + 32 * wave : 0;  // SwiGLU gate column base
+  auto wcol = [&](int st, int c) -> int64_t {
+    return SWIGLU ? (st ? half : 0) + scol0 + c : n0 + 64 * wave + 32 * st + c;
+  };
+  auto wcol_ok = [&](int st, int c) -> bool {
+    return SWIGLU ? scol0 + c < half : wcol(st, c) < N;
+  };
 
   // activation descriptors: this tile's rows (dense) or all of x (grouped)
   __amdgpu_buffer_rsrc_t xr, xsr;
@@ -179,10 +185,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   uint32_t woff[2], soff[2];
 #pragma unroll
   for (int st = 0; st < 2; st++) {
-    const int64_t n = wcol0 + 32 * st + col;
-    const int64_t nl = n - wbase;
-    woff[st] = n < col_end ? (uint32_t)(nl * (K >> 1)) : kOOB;
-    soff[st] = n < col_end ? (uint32_t)(nl * (K >> 4)) : kOOB;
+    const int64_t nl = wcol(st, col) - wbase;
+    woff[st] = wcol_ok(st, col) ? (uint32_t)(nl * (K >> 1)) : kOOB;
+    soff[st] = wcol_ok(st, col) ? (uint32_t)(nl * (K >> 4)) : kOOB;
   }
 
   const int KT = (int)((K + BK - 1) / BK);
@@ -356,44 +361,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 
   if (SWIGLU) {
-    // up waves -> LDS (their own register layout) -> gate waves
-    float* xch = reinterpret_cast<float*>(lds_a);  // [2 waves][MT][2][16][64 lanes]
-    __syncthreads();
-    if (wave >= 2) {
+    // g in subtile 0, u in subtile 1 of the same lane
+    if (!wcol_ok(0, col)) return;
+    const int64_t n = scol0 + col;
 #pragma unroll
-      for (int mt = 0; mt < MT; mt++)
+    for (int mt = 0; mt < MT; mt++)
 #pragma unroll
-        for (int r = 0; r < 16; r++) {
-          const int lrow = 32 * mt + 8 * (r >> 2) + 4 * h + (r & 3);
-          const int64_t xrow = row_x[lrow];
-          const float f = (ACT == 0 || xrow < 0) ? ts : a.x_ts[xrow] * ts;
-#pragma unroll
-          for (int st = 0; st < 2; st++)
-            xch[((((wave - 2) * MT + mt) * 2 + st) * 16 + r) * 64 + lane] = acc[mt][st][r] * f;
-        }
-    }
-    __syncthreads();
-    if (wave < 2) {
-#pragma unroll
-      for (int mt = 0; mt < MT; mt++)
-#pragma unroll
-        for (int r = 0; r < 16; r++) {
-          const int lrow = 32 * mt + 8 * (r >> 2) + 4 * h + (r & 3);
-          const int64_t route = row_route[lrow];
-          if (route < 0) continue;
-          const int64_t xrow = row_x[lrow];
-          const float f = (ACT == 0) ? ts : a.x_ts[xrow] * ts;
-#pragma unroll
-          for (int st = 0; st < 2; st++) {
-            const int64_t n = wcol0 + 32 * st + col;
-            if (n >= half) continue;
-            const float g = acc[mt][st][r] * f;
-            const float u = xch[(((wave * MT + mt) * 2 + st) * 16 + r) * 64 + lane];
-            const float sg = silu(g);
-            a.a_out[route * half + n] = (uint16_t)f32_to_bf16_rne(sg * u);
-          }
-        }
-    }
+      for (int r = 0; r < 16; r++) {
+        const int lrow = 32 * mt + 8 * (r >> 2) + 4 * h + (r & 3);
+        const int64_t route = row_route[lrow];
+        if (route < 0) continue;
+        const int64_t xrow = row_x[lrow];
+        const float f = (ACT == 0) ? ts : a.x_ts[xrow] * ts;
+        const float g = acc[mt][0][r] * f;
+        const float u = acc[mt][1][r] * f;
+        a.a_out[route * half + n] = (uint16_t)f32_to_bf16_rne(silu(g) * u);
+      }
     return;
   }
 #pragma unroll
@@ -666,9 +649,10 @@ __global__ __launch_bounds__(768) void gemm_wide(GemmArgs a) {
 // epilogue is the grouped 64/128-row kernel's, so a route's row is the dense product bit
 // for bit.
 //
-// SWIGLU: the tile's 256 columns are 128 gate columns (consumer waves wn = 0, 1) and the
-// matching 128 up columns N/2 + ... (wn = 2, 3); the up waves hand their scaled results
-// to the gate waves through LDS, and the gate waves write bf16_rne(silu(g) * u).
+// SWIGLU: the tile's 256 columns are 128 gate columns and the matching 128 up columns
+// N/2 + ...: consumer wave wn takes gate columns 32 wn + [0, 32) of the block as its first
+// 32-column subtile and the matching up columns as its second, so each lane holds g and u
+// of the same outputs and writes bf16_rne(silu(g) * u).
 // ---------------------------------------------------------------------------------------
 template <int ACT, bool SWIGLU, bool SB = false>
 __global__ __launch_bounds__(768) void gemm_wide_grouped(GemmArgs a) {
@@ -755,8 +739,10 @@ __global__ __launch_bounds__(768) void gemm_wide_grouped(GemmArgs a) {
       int64_t wrow;
       bool ok;
       if (SWIGLU) {
-        const int64_t c = cb * (BN / 2) + (bc & (BN / 2 - 1));
-        wrow = (bc < BN / 2 ? 0 : half) + c;
+        // tile column bc = 64 wn + 32 st + j: gate (st = 0) or up (st = 1) column
+        // cb * 128 + 32 wn + j
+        const int64_t c = cb * (BN / 2) + 32 * (bc >> 6) + (bc & 31);
+        wrow = ((bc >> 5) & 1 ? half : 0) + c;
         ok = c < half;
       } else {
         wrow = cb * BN + bc;
@@ -863,10 +849,6 @@ __global__ __launch_bounds__(768) void gemm_wide_grouped(GemmArgs a) {
         pstep(std::integral_constant<int, 1>{}, kt + 1, ra[0], rb[0]);
       }
     }
-    if (SWIGLU) {  // the consumers' two epilogue barriers
-      __syncthreads();
-      __syncthreads();
-    }
     return;
   }
 
@@ -902,44 +884,22 @@ __global__ __launch_bounds__(768) void gemm_wide_grouped(GemmArgs a) {
   }
 
   if (SWIGLU) {
-    // up waves -> LDS (their own register layout) -> gate waves of the same rows
-    float* xch = reinterpret_cast<float*>(lds);  // [2 wm][2 wn][4 mt][2 st][16 r][64 lanes]
-    __syncthreads();  // every wave is done with the operand stages
-    if (wn >= 2) {
+    // g in subtile 0, u in subtile 1 of the same lane
+    const int64_t n = cb * (BN / 2) + 32 * wn + col;
+    if (n >= half) return;
 #pragma unroll
-      for (int mt = 0; mt < 4; mt++)
+    for (int mt = 0; mt < 4; mt++)
 #pragma unroll
-        for (int r = 0; r < 16; r++) {
-          const int lrow = 128 * wm + 32 * mt + 8 * (r >> 2) + 4 * h + (r & 3);
-          const int64_t xrow = row_x[lrow];
-          const float f = (ACT == 0 || xrow < 0) ? ts : a.x_ts[xrow] * ts;
-#pragma unroll
-          for (int st = 0; st < 2; st++)
-            xch[((((wm * 2 + (wn - 2)) * 4 + mt) * 2 + st) * 16 + r) * 64 + lane] = acc[mt][st][r] * f;
-        }
-    }
-    __syncthreads();
-    if (wn < 2) {
-#pragma unroll
-      for (int mt = 0; mt < 4; mt++)
-#pragma unroll
-        for (int r = 0; r < 16; r++) {
-          const int lrow = 128 * wm + 32 * mt + 8 * (r >> 2) + 4 * h + (r & 3);
-          const int64_t route = row_route[lrow];
-          if (route < 0) continue;
-          const int64_t xrow = row_x[lrow];
-          const float f = (ACT == 0) ? ts : a.x_ts[xrow] * ts;
-#pragma unroll
-          for (int st = 0; st < 2; st++) {
-            const int64_t n = cb * (BN / 2) + 64 * wn + 32 * st + col;
-            if (n >= half) continue;
-            const float g = acc[mt][st][r] * f;
-            const float u = xch[((((wm * 2 + wn) * 4 + mt) * 2 + st) * 16 + r) * 64 + lane];
-            const float sg = silu(g);
-            a.a_out[route * half + n] = (uint16_t)f32_to_bf16_rne(sg * u);
-          }
-        }
-    }
+      for (int r = 0; r < 16; r++) {
+        const int lrow = 128 * wm + 32 * mt + 8 * (r >> 2) + 4 * h + (r & 3);
+        const int64_t route = row_route[lrow];
+        if (route < 0) continue;
+        const int64_t xrow = row_x[lrow];
+        const float f = (ACT == 0) ? ts : a.x_ts[xrow] * ts;
+        const float g = acc[mt][0][r] * f;
+        const float u = acc[mt][1][r] * f;
+        a.a_out[route * half + n] = (uint16_t)f32_to_bf16_rne(silu(g) * u);
+      }
     return;
   }
 #pragma unroll
@@ -1279,13 +1239,12 @@ hipError_t launch_grouped_mt(const GemmArgs& a, int64_t max_tiles, hipStream_t s
   const bool sb = kSB && scale_pieces(a);
   if (a.a_out) {
     const int64_t blocks = tiles8 * (((a.N >> 1) + BN / 2 - 1) / (BN / 2));
-    const size_t xch = (size_t)2 * MT * 2 * 16 * 64 * sizeof(float);
     if (sb)
       hipLaunchKernelGGL((gemm_kernel<MT, ACT, true, true, kSB>), dim3((uint32_t)blocks),
-                         dim3(256), lds > xch ? lds : xch, stream, a);
+                         dim3(256), lds, stream, a);
     else
       hipLaunchKernelGGL((gemm_kernel<MT, ACT, true, true>), dim3((uint32_t)blocks),
-                         dim3(256), lds > xch ? lds : xch, stream, a);
+                         dim3(256), lds, stream, a);
   } else {
     const int64_t blocks = tiles8 * ((a.N + BN - 1) / BN);
     if (sb)
