@@ -921,6 +921,357 @@ __global__ __launch_bounds__(768) void gemm_wide_grouped(GemmArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------
+// gemm_wide_grouped_p: the wide grouped form as a persistent pipeline. One workgroup per
+// CU takes its XCD's tiles in turn: tile j = blockIdx / 8 + i * (gridDim / 8) of XCD
+// blockIdx % 8's share (gridDim a multiple of 8), the order of gemm_wide_grouped, so a
+// workgroup's tiles stay on its XCD. The producers' steps run on from one tile into the
+// next: the next tile's first loads are issued three steps before the current tile ends,
+// its row table is written during the current tile's first steps, and its operand
+// offsets are read back from that table just before its first loads.
+// The consumers store a tile's results while the producers stage the next tile, so the
+// stores at the end of a tile overlap the next tile's steps instead of ending a round of
+// workgroups together. Per tile the arithmetic (MFMA chain, k order, epilogue) is
+// gemm_wide_grouped's, so every result is the same bits.
+// ---------------------------------------------------------------------------------------
+constexpr int kPersistMaxTiles = 256;  // tiles per workgroup: one header per producer lane
+
+template <int ACT>
+struct PState {  // a tile's operand offsets for the producer lane
+  uint32_t xoff[8];
+  uint32_t xsoff[ACT == 0 ? 1 : 8];
+  uint32_t bwoff[2], bsoff[2];
+  __amdgpu_buffer_rsrc_t wr, sr;
+};
+
+template <int ACT, bool SWIGLU, bool SB>
+__global__ __launch_bounds__(768) void gemm_wide_grouped_p(GemmArgs a) {
+  constexpr int BM = kWideBM;
+  extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
+  uint16_t* As = lds;                 // [2][BM * LDA]  activations [row][k]
+  uint16_t* Bs = lds + 2 * BM * LDA;  // [2][BN * LDA]  decoded weight [column][k]
+  __shared__ int32_t row_x[2][BM];    // per tile parity: x row of each tile row (-1: none)
+  __shared__ int32_t row_route[2][BM];
+  __shared__ int4 hdr[kPersistMaxTiles];  // per tile: expert, first route, routes, column block
+  __shared__ float hts[kPersistMaxTiles];  // per tile: the expert's tensor scale (or 1)
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t N = a.N, K = a.K;
+  const uint32_t Ku = (uint32_t)K;
+  const int64_t half = N >> 1;
+  const int64_t nbn = SWIGLU ? (half + BN / 2 - 1) / (BN / 2) : (N + BN - 1) / BN;
+
+  const int64_t n_act = *a.n_active;
+  const int64_t per_xcd = (n_act + 7) / 8;
+  const int64_t xcd = blockIdx.x % 8, jb = blockIdx.x / 8, jstep = gridDim.x / 8;
+  const int64_t tx = n_act - xcd * per_xcd;  // active experts in this XCD's share
+  const int64_t J = nbn * (tx <= 0 ? 0 : (tx < per_xcd ? tx : per_xcd));
+  const int ntiles = jb < J ? (int)((J - jb + jstep - 1) / jstep) : 0;
+  if (ntiles == 0) return;  // uniform over the workgroup, before any barrier
+
+  const int KT = (int)((K + BK - 1) / BK);
+  const int KT2 = KT + (KT & 1);  // whole rounds of the two register sets (>= 8 here)
+
+  if (wave >= 8 && tid - 512 < ntiles) {
+    const int i = tid - 512;
+    const int64_t j = jb + (int64_t)i * jstep;
+    const int e = a.active[xcd * per_xcd + j / nbn];
+    const int32_t beg = a.offsets[e];
+    const int32_t cnt = a.offsets[e + 1] - beg;
+    hdr[i] = make_int4(e, beg, cnt < BM ? cnt : BM, (int)(j % nbn));
+    // read here, before any store: once the kernel has stored, a load of w_ts may no
+    // longer be a scalar load, and a vector load in the epilogue would make the compiler
+    // wait for all earlier stores at each of its joins
+    hts[i] = a.apply_ts ? a.w_ts[e] : 1.0f;
+  }
+  __syncthreads();  // headers ready
+  // tile 0's row table (each producer lane writes its row pt)
+  if (wave >= 8) {
+    const int pt = tid - 512;
+    const int4 h0 = hdr[0];
+    const int32_t route = pt < h0.z ? a.sorted[h0.y + pt] : -1;
+    row_route[0][pt] = route;
+    row_x[0][pt] = route < 0 ? -1 : (a.rows_per_token ? route / a.top_k : route);
+  }
+  __syncthreads();  // tile 0's row table ready
+
+  if (wave >= 8) {
+    auto uni = [](const void* p) -> const void* {
+      const uint64_t v = (uint64_t)(uintptr_t)p;
+      const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+      const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+      return (const void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+    };
+    auto uni64 = [](int64_t v) -> int64_t {
+      const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+      const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+      return (int64_t)(((uint64_t)hi << 32) | lo);
+    };
+    __amdgpu_buffer_rsrc_t xr, xsr;
+    if (ACT == 0) {
+      xr = rsrc(uni(a.x), uni64(((a.x_rows - 1) * a.ldx + K) * 2));
+      xsr = xr;
+    } else {
+      xr = rsrc(uni(a.x), uni64(a.x_rows * (K >> 1)));
+      xsr = rsrc(uni(a.x_scales), uni64(a.x_rows * (K >> 4)));
+    }
+    const int pt = tid - 512;
+    // tiles past the last have no rows
+    const int4 nohdr = make_int4(0, 0, 0, 0);
+    auto tile_hdr = [&](int i) -> int4 { return i < ntiles ? hdr[i] : nohdr; };
+    // a tile's operand offsets from its header and its row table (parity buf)
+    auto make_state = [&](const int4& h, PState<ACT>& st, int buf) {
+#pragma unroll
+      for (int q = 0; q < 8; q++) {
+        const int64_t xrow = row_x[buf][(pt >> 3) + 32 * q];
+        if (ACT == 0) {
+          st.xoff[q] = xrow < 0 ? kOOB : (uint32_t)(xrow * a.ldx * 2);
+        } else {
+          st.xoff[q] = xrow < 0 ? kOOB : (uint32_t)(xrow * (K >> 1));
+          st.xsoff[q] = xrow < 0 ? kOOB : (uint32_t)(xrow * (K >> 4));
+        }
+      }
+      const int e = h.x;
+      const int64_t cb = h.w;
+#pragma unroll
+      for (int q = 0; q < 2; q++) {
+        const int bc = (pt + 256 * q) >> 1;
+        int64_t wrow;
+        bool ok;
+        if (SWIGLU) {
+          const int64_t c = cb * (BN / 2) + 32 * (bc >> 6) + (bc & 31);
+          wrow = ((bc >> 5) & 1 ? half : 0) + c;
+          ok = c < half && h.z > 0;
+        } else {
+          wrow = cb * BN + bc;
+          ok = wrow < N && h.z > 0;
+        }
+        st.bwoff[q] = ok ? (uint32_t)(wrow * (K >> 1)) : kOOB;
+        st.bsoff[q] = ok ? (uint32_t)(wrow * (K >> 4)) : kOOB;
+      }
+      st.wr = rsrc(uni(a.w_codes + (int64_t)e * N * (K >> 1)), uni64(N * (K >> 1)));
+      st.sr = rsrc(uni(a.w_scales + (int64_t)e * N * (K >> 4)), uni64(N * (K >> 4)));
+    };
+    auto issue = [&](const PState<ACT>& st, int kt, RegAP<ACT>& ra, RegBP& rb) {
+      const uint32_t k0 = (uint32_t)kt * BK;
+#pragma unroll
+      for (int q = 0; q < 2; q++) {
+        const uint32_t kh = k0 + 32u * ((pt + 256 * q) & 1);
+        if (!SB)
+          rb.s[q] = __builtin_amdgcn_raw_buffer_load_b16(st.sr, (st.bsoff[q] + (kh >> 4)) | past(Ku, kh), 0, 0);
+        rb.c[q] = __builtin_amdgcn_raw_buffer_load_b128(st.wr, (st.bwoff[q] + (kh >> 1)) | past(Ku, kh), 0, 0);
+      }
+#pragma unroll
+      for (int q = 0; q < 8; q++) {
+        const int j = (pt + 256 * q) & 7;
+        const uint32_t k = k0 + 8u * j;
+        if (ACT == 0) {
+          ra.v[q] = __builtin_amdgcn_raw_buffer_load_b128(xr, (st.xoff[q] + 2u * k) | past(Ku, k), 0, 0);
+        } else {
+          ra.c[q] = __builtin_amdgcn_raw_buffer_load_b32(xr, (st.xoff[q] + (k >> 1)) | past(Ku, k), 0, 0);
+          ra.s[q] = __builtin_amdgcn_raw_buffer_load_b8(xsr, (st.xsoff[q] + (k >> 4)) | past(Ku, k), 0, 0);
+        }
+      }
+    };
+    auto write_stage = [&](const RegAP<ACT>& ra, const RegBP& rb, const uint32_t (&sw)[2], int buf) {
+      uint16_t* da = As + buf * (BM * LDA);
+#pragma unroll
+      for (int q = 0; q < 8; q++) {
+        const int c = pt + 256 * q;
+        const int row = c >> 3, j = c & 7;
+        u32x4 v;
+        if (ACT == 0) v = ra.v[q];
+        else v = decode8(ra.c[q], e4m3_to_f32<0>(ra.s[q]));  // exact BF16 activations
+        *reinterpret_cast<u32x4*>(da + row * LDA + 8 * j) = v;
+      }
+#pragma unroll
+      for (int q = 0; q < 2; q++) {
+        const int c = pt + 256 * q;
+        const int bc = c >> 1, bh = c & 1;
+        uint16_t* db = Bs + buf * (BN * LDA) + bc * LDA + 32 * bh;
+        const float s0 = e4m3_to_f32<0>(sw[q]), s1 = e4m3_to_f32<1>(sw[q]);
+#pragma unroll
+        for (int d = 0; d < 4; d++)
+          *reinterpret_cast<u32x4*>(db + 8 * d) = decode8(rb.c[q][d], d < 2 ? s0 : s1);
+      }
+    };
+    u32x4 sblk[2];  // SB: the scales of a 4-step piece (see gemm_wide_grouped)
+    auto issue_sb = [&](const PState<ACT>& st, int kt) {
+      const uint32_t k0 = (uint32_t)kt * BK;
+#pragma unroll
+      for (int q = 0; q < 2; q++)
+        sblk[q] = __builtin_amdgcn_raw_buffer_load_b128(st.sr, (st.bsoff[q] + (k0 >> 4)) | past(Ku, k0), 0, 0);
+    };
+    const uint32_t hsh = 16u * (pt & 1);
+    auto scales = [&](const RegBP& rb, auto stepc, uint32_t (&sw)[2]) {
+      constexpr int j = decltype(stepc)::value;
+#pragma unroll
+      for (int q = 0; q < 2; q++) sw[q] = SB ? sblk[q][j & 3] >> hsh : rb.s[q];
+    };
+
+    RegAP<ACT> ra[2];
+    RegBP rb[2];
+    // the tile whose loads are being issued: the current one, and from three steps before
+    // its end the next one (the current tile needs no more loads by then)
+    PState<ACT> st;
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+    make_state(tile_hdr(0), st, 0);
+    if (SB) issue_sb(st, 0);
+    issue(st, 0, ra[0], rb[0]);
+    issue(st, 1, ra[1], rb[1]);
+    {
+      uint32_t sw[2];
+      scales(rb[0], I0{}, sw);
+      write_stage(ra[0], rb[0], sw, 0);
+    }
+    issue(st, 2, ra[0], rb[0]);
+    __syncthreads();  // stage 0 of tile 0 ready
+    // step kt + j of the current tile: stage the next step (or the next tile's first),
+    // issue step (kt + j + 3) % KT2 of the issue tile, and with SB at j = 2 the piece of
+    // steps (kt + 4) % KT2 ...
+    auto pstep = [&](auto jc, int kt, RegAP<ACT>& ran, RegBP& rbn) {
+      constexpr int j4 = decltype(jc)::value;
+      uint32_t sw[2];
+      scales(rbn, std::integral_constant<int, (j4 + 1) & 3>{}, sw);
+      write_stage(ran, rbn, sw, (kt + j4 + 1) & 1);
+      if constexpr (SB && j4 == 2) issue_sb(st, kt + 4 < KT2 ? kt + 4 : kt + 4 - KT2);
+      const int ik = kt + j4 + 3;
+      issue(st, ik < KT2 ? ik : ik - KT2, ran, rbn);
+      __syncthreads();
+    };
+    // the routes, for the next tiles' row tables: loaded without a branch (a lane past the
+    // tile's routes reads zero), so that no load in flight is waited for early
+    const int64_t nroutes = a.rows_per_token ? a.x_rows * a.top_k : a.x_rows;
+    const auto rr = rsrc(uni(a.sorted), uni64(nroutes * 4));
+    for (int i = 0; i < ntiles; i++) {
+      // this lane's row of the next tile's row table, in flight during the first round
+      const int4 hn = tile_hdr(i + 1);
+      const bool has = pt < hn.z;
+      int32_t rl = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(
+          rr, has ? (uint32_t)(hn.y + pt) * 4u : kOOB, 0, 0);
+      // rounds of four steps (SB: one scale piece each) or two
+      for (int kt = 0; kt < KT2; kt += SB ? 4 : 2) {
+        pstep(I0{}, kt, ra[1], rb[1]);
+        if (kt == KT2 - 4) {
+          // the current tile's loads are all issued: the next tile's offsets, from its
+          // row table (written at least one barrier ago, see below) and header
+          make_state(hn, st, (i + 1) & 1);
+        }
+        pstep(I1{}, kt, ra[0], rb[0]);
+        if constexpr (SB) {
+          pstep(I2{}, kt, ra[1], rb[1]);
+          pstep(I3{}, kt, ra[0], rb[0]);
+        }
+        if (kt == 0) {
+          // the next tile's row table, parity (i + 1) & 1, one row per lane: the consumers
+          // read parity i & 1 for the current tile, and the other parity's last reader
+          // (tile i - 1's epilogue) ran before this tile's first barrier. The empty asm
+          // keeps the route's use here: lifted to the top of the tile, it would wait there
+          // for every load in flight
+          asm volatile("" : "+v"(rl));
+          const int32_t rn = has ? rl : -1;
+          row_route[(i + 1) & 1][pt] = rn;
+          row_x[(i + 1) & 1][pt] = rn < 0 ? -1 : (a.rows_per_token ? rn / a.top_k : rn);
+        }
+      }
+    }
+    return;
+  }
+
+  // ---------------- consumers: 8 waves ----------------
+  const int wm = wave >> 2, wn = wave & 3;
+  const int col = lane & 31;
+  const int h = lane >> 5;
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int mt = 0; mt < 4; mt++)
+#pragma unroll
+    for (int st = 0; st < 2; st++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) acc[mt][st][r] = 0.f;
+  __syncthreads();  // stage 0 of tile 0 ready
+  // the output: BF16 rows [routes][N/2] (SwiGLU) or fp32 rows [routes][ldy]
+  const int64_t nroutes = a.rows_per_token ? a.x_rows * a.top_k : a.x_rows;
+  const auto yr = SWIGLU ? rsrc(a.a_out, nroutes * half * 2) : rsrc(a.y, nroutes * a.ldy * 4);
+  for (int i = 0; i < ntiles; i++) {
+    for (int kt = 0; kt < KT2; kt++) {
+      const uint16_t* sa = As + (kt & 1) * (BM * LDA) + (128 * wm + col) * LDA + 32 * h;
+      const uint16_t* sb = Bs + (kt & 1) * (BN * LDA) + (64 * wn + col) * LDA + 32 * h;
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        u32x4 B[2];
+#pragma unroll
+        for (int st = 0; st < 2; st++)
+          B[st] = *reinterpret_cast<const u32x4*>(sb + 32 * st * LDA + 8 * j);
+#pragma unroll
+        for (int mt = 0; mt < 4; mt++) {
+          const u32x4 A = *reinterpret_cast<const u32x4*>(sa + 32 * mt * LDA + 8 * j);
+#pragma unroll
+          for (int st = 0; st < 2; st++) acc[mt][st] = mfma32(A, B[st], acc[mt][st]);
+        }
+      }
+      __syncthreads();
+    }
+    // the tile's results (row table parity i & 1), while the producers stage the next tile
+    const int64_t cb = __builtin_amdgcn_readfirstlane(hdr[i].w);
+    const float ts = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(
+                                                   __builtin_bit_cast(int, hts[i])));
+    const int buf = i & 1;
+    // Branch-free stores: buffer stores with out-of-range offsets for the rows without a
+    // route and the columns past the end (the host takes this form only while the output
+    // fits 32-bit offsets). The lane's rows come four at a time (one 16-byte LDS read).
+#pragma unroll
+    for (int mt = 0; mt < 4; mt++) {
+#pragma unroll
+      for (int g4 = 0; g4 < 4; g4++) {
+        const int lrow0 = 128 * wm + 32 * mt + 8 * g4 + 4 * h;
+        const int4 rt = *reinterpret_cast<const int4*>(&row_route[buf][lrow0]);
+        int4 xr4 = make_int4(0, 0, 0, 0);
+        if (ACT != 0) xr4 = *reinterpret_cast<const int4*>(&row_x[buf][lrow0]);
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+          const int r = 4 * g4 + q;
+          const int32_t route = q == 0 ? rt.x : q == 1 ? rt.y : q == 2 ? rt.z : rt.w;
+          float f = ts;
+          if (ACT != 0) {
+            const int32_t xrow = q == 0 ? xr4.x : q == 1 ? xr4.y : q == 2 ? xr4.z : xr4.w;
+            f = a.x_ts[xrow < 0 ? 0 : xrow] * ts;
+          }
+          if (SWIGLU) {
+            const uint32_t n = (uint32_t)(cb * (BN / 2) + 32 * wn + col);
+            const uint32_t off = route < 0 || n >= (uint32_t)half
+                                     ? kOOB : ((uint32_t)route * (uint32_t)half + n) * 2u;
+            const float gg = acc[mt][0][r] * f;
+            const float u = acc[mt][1][r] * f;
+            __builtin_amdgcn_raw_buffer_store_b16(
+                (uint16_t)f32_to_bf16_rne(silu(gg) * u), yr, off, 0, 0);
+          } else {
+#pragma unroll
+            for (int st = 0; st < 2; st++) {
+              const uint32_t n = (uint32_t)(cb * BN + 64 * wn + 32 * st + col);
+              const uint32_t off = route < 0 || n >= (uint32_t)N
+                                       ? kOOB : ((uint32_t)route * (uint32_t)a.ldy + n) * 4u;
+              __builtin_amdgcn_raw_buffer_store_b32(
+                  __builtin_bit_cast(uint32_t, acc[mt][st][r] * f), yr, off, 0, 0);
+            }
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int mt = 0; mt < 4; mt++)
+#pragma unroll
+      for (int st = 0; st < 2; st++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) acc[mt][st][r] = 0.f;
+  }
+}
+
+// ---------------------------------------------------------------------------------------
 // gemm_splitk: problems whose 64 x 256 tiles leave most CUs idle (e.g. M = 512, N = 4096:
 // 128 tiles). A 64 (M) x 128 (N) tile on sixteen waves: four groups of four waves take
 // the four quarters of K, each wave computing 64 x 32 (two 32x32x16 subtiles) with its
@@ -1257,11 +1608,52 @@ hipError_t launch_grouped_mt(const GemmArgs& a, int64_t max_tiles, hipStream_t s
   return hipGetLastError();
 }
 
+// CUs of the current device, rounded down to a multiple of eight (0 if unknown): the grid
+// of the persistent wide grouped form, one workgroup per CU
+int persist_grid() {
+  static int cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return 0;
+    cached[dev] = n / 8 * 8;
+  }
+  return cached[dev];
+}
+
+template <int ACT, bool SWIGLU>
+hipError_t launch_grouped_wide_p(const GemmArgs& a, int grid, size_t lds, bool sb,
+                                 hipStream_t stream) {
+  if (sb)
+    hipLaunchKernelGGL((gemm_wide_grouped_p<ACT, SWIGLU, true>), dim3((uint32_t)grid), dim3(768),
+                       lds, stream, a);
+  else
+    hipLaunchKernelGGL((gemm_wide_grouped_p<ACT, SWIGLU, false>), dim3((uint32_t)grid), dim3(768),
+                       lds, stream, a);
+  return hipGetLastError();
+}
+
 template <int ACT>
 hipError_t launch_grouped_wide(const GemmArgs& a, int64_t max_active, hipStream_t stream) {
   const size_t lds = 2 * (size_t)(kWideBM + BN) * LDA * sizeof(uint16_t);
   const int64_t act8 = (max_active + 7) / 8 * 8;
   const bool sb = scale_pieces(a);
+  // the persistent form: at least eight steps per tile (a round of four before the next
+  // tile's offsets are built, four after), at most kPersistMaxTiles tiles per workgroup,
+  // and an output its stores reach with 32-bit offsets
+  {
+    const int64_t KT = (a.K + BK - 1) / BK;
+    const int64_t nbn = a.a_out ? ((a.N >> 1) + BN / 2 - 1) / (BN / 2) : (a.N + BN - 1) / BN;
+    const int64_t nroutes = a.rows_per_token ? a.x_rows * a.top_k : a.x_rows;
+    const int64_t out_bytes = a.a_out ? nroutes * (a.N >> 1) * 2 : nroutes * a.ldy * 4;
+    const int grid = persist_grid();
+    if (KT + (KT & 1) >= 8 && grid >= 8 && out_bytes < ((int64_t)1 << 31) &&
+        (act8 / 8 * nbn + grid / 8 - 1) / (grid / 8) <= kPersistMaxTiles)
+      return a.a_out ? launch_grouped_wide_p<ACT, true>(a, grid, lds, sb, stream)
+                     : launch_grouped_wide_p<ACT, false>(a, grid, lds, sb, stream);
+  }
   if (a.a_out) {
     const int64_t blocks = act8 * (((a.N >> 1) + BN / 2 - 1) / (BN / 2));
     if (sb)

@@ -509,14 +509,17 @@ def test_grouped_prefill_gemm_several_column_blocks(dev, o):
     assert_within(y, yr, b, "column blocks: combine")
 
 
-@pytest.mark.parametrize("K", [320, 512])
+@pytest.mark.parametrize("K", [320, 512, 544])
 def test_grouped_wide_tiles_every_output_form(dev, o, K):
     """Routes averaging >= 192 per expert take the wide grouped form: each expert's first
     256 routes in one 256-route tile (wave-specialized), the rest in 32-route tiles. Here
     1600 routes over 6 experts (some above 256, so both kinds of tile run), N = 544 (a
     ragged third column block; half = 272, a ragged third gate block), K = 320 (an odd
-    number of 64-k steps, one 2-byte scale load per step) or 512 (the scales in 16-byte
-    pieces of four steps), and dropped routes: every output of every kept route against the
+    number of 64-k steps, one 2-byte scale load per step), 512 (the scales in 16-byte
+    pieces of four steps) or 544 (nine steps, per-step scale loads); from eight steps the
+    wide tiles take the persistent form, whose workgroups run several tiles each (six
+    experts of three column blocks on 256 workgroups: one tile each here, several in the
+    prefill layer test). Dropped routes: every output of every kept route against the
     oracle, dropped routes' rows zero, padded activation rows, SwiGLU from the rows, the
     ordered combine, determinism, one route per token equal to the dense product bit for
     bit, and (K = 512) the same bits from a scale copy that takes the per-step loads."""
@@ -577,6 +580,35 @@ def test_grouped_wide_tiles_every_output_form(dev, o, K):
         assert torch.equal(nv.grouped_linear(x, wc, wsc2, wts, ids_d), h_d)
         assert torch.equal(nv.grouped_linear(x, wc, wsc2, wts, ids_d,
                                              out_mode=nv.OUT_SWIGLU_BF16), a)
+
+
+@pytest.mark.parametrize("K", [544, 512])
+def test_grouped_wide_persistent_several_tiles(dev, o, K):
+    """The persistent form of the wide grouped tiles with several tiles per workgroup: 96
+    experts of ~192 routes and N = 1024 (four column blocks) make 384 tiles on 256
+    workgroups, so a third of the workgroups run two tiles, the second staged while the
+    first one's results are stored. K = 544 (nine steps, per-step scale loads) and 512
+    (scale pieces). Every output of every route against the oracle, SwiGLU from the rows
+    (its 1024/2 columns are four gate/up blocks), determinism."""
+    E, N, T, k = 96, 1024, 4608, 4
+    _say(f"grouped GEMM, persistent wide tiles: E={E} N={N} K={K} T={T} k={k}")
+    wc, wsc, wts, oc, os_, ot, ids, rw, xb = _prefill_case(dev, o, E, N, K, T, k, 171)
+    counts = np.bincount(ids.ravel(), minlength=E)
+    assert counts.mean() >= 192 and counts.min() > 0, counts
+    x = to_dev_bf16(xb, dev)
+    ids_d = torch.from_numpy(ids).to(dev)
+    h_d = nv.grouped_linear(x, wc, wsc, wts, ids_d)
+    h = h_d.cpu().numpy()
+    x64 = o.bf16_to_f64(xb)
+    for e in range(E):
+        routes = np.nonzero(ids.ravel() == e)[0]
+        wdq = o.dequant(oc[e], os_[e], ot[e:e + 1], per_row=False)
+        yr, b = o.linear_f64(x64[routes // k], wdq)
+        assert_within(h[routes], yr, b, f"persistent wide tiles: expert {e} rows")
+    assert torch.equal(nv.grouped_linear(x, wc, wsc, wts, ids_d), h_d)
+    a = nv.grouped_linear(x, wc, wsc, wts, ids_d, out_mode=nv.OUT_SWIGLU_BF16)
+    _swiglu_bits_check(o, a, h, f"persistent wide tiles K={K}")
+    assert torch.equal(nv.grouped_linear(x, wc, wsc, wts, ids_d, out_mode=nv.OUT_SWIGLU_BF16), a)
 
 
 def test_moe_prefill_layer_full_shape(dev, o, moe):
@@ -643,6 +675,7 @@ def _w4a4_experts_case(dev, o, E, N, K, T, k, seed):
 
 @pytest.mark.parametrize("E,N,K,T,k", [(8, 320, 256, 512, 2),   # GEMM path (128 per expert)
                                        (4, 320, 256, 560, 2),   # wide grouped form (280)
+                                       (4, 544, 544, 560, 2),   # its persistent form, 10 steps
                                        (16, 192, 256, 4, 4)])    # streaming path (decode size)
 def test_grouped_w4a4_every_output_form(dev, o, E, N, K, T, k):
     """NVFP4 activations (quantized on the device, bit-exact with the oracle) through the
