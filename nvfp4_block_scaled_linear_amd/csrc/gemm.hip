@@ -82,7 +82,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   constexpr int BM = 32 * MT;
   extern __shared__ __attribute__((aligned(16))) uint16_t lds_a[];  // [2][BM * LDA]
   __shared__ int32_t row_x[GROUPED ? BM : 1];      // x row of each tile row (-1: none)
-  __shared__ int32_t row_route[GROUPED ? BM : 1];  // route of each tile row
+  __shared__ __attribute__((aligned(16))) int32_t row_route[GROUPED ? BM : 4];  // route of each tile row
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -360,6 +360,48 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
   }
 
+  // BF16 activations: branch-free stores through one descriptor over the output (grouped:
+  // every route's row; dense: the tile's rows), rows without a route, rows past M and
+  // columns past the end at out-of-range offsets, while the output fits 32-bit offsets
+  if (ACT == 0) {
+    const int64_t nroutes = a.rows_per_token ? a.x_rows * a.top_k : a.x_rows;
+    const int64_t span = SWIGLU ? nroutes * half * 2
+                                : (GROUPED ? nroutes * a.ldy * 4 : rows_m * a.ldy * 4);
+    if (span < ((int64_t)1 << 31)) {
+      const auto yr = SWIGLU ? rsrc(a.a_out, span) : rsrc(GROUPED ? a.y : a.y + m0 * a.ldy, span);
+      const uint32_t pitch = SWIGLU ? (uint32_t)half : (uint32_t)a.ldy;
+#pragma unroll
+      for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; g4++) {
+          const int lrow0 = 32 * mt + 8 * g4 + 4 * h;
+          int4 rt = make_int4(lrow0, lrow0 + 1, lrow0 + 2, lrow0 + 3);
+          if (GROUPED) rt = *reinterpret_cast<const int4*>(&row_route[lrow0]);
+#pragma unroll
+          for (int q = 0; q < 4; q++) {
+            const int r = 4 * g4 + q;
+            const int32_t row = q == 0 ? rt.x : q == 1 ? rt.y : q == 2 ? rt.z : rt.w;
+            if (SWIGLU) {
+              const uint32_t off = row < 0 || !wcol_ok(0, col)
+                                       ? kOOB : ((uint32_t)row * pitch + (uint32_t)(scol0 + col)) * 2u;
+              const float g = acc[mt][0][r] * ts;
+              const float u = acc[mt][1][r] * ts;
+              __builtin_amdgcn_raw_buffer_store_b16((uint16_t)f32_to_bf16_rne(silu(g) * u), yr, off,
+                                                    0, 0);
+            } else {
+#pragma unroll
+              for (int st = 0; st < 2; st++) {
+                const int64_t n = n0 + 64 * wave + 32 * st + col;
+                const uint32_t off = row < 0 || n >= N ? kOOB : ((uint32_t)row * pitch + (uint32_t)n) * 4u;
+                __builtin_amdgcn_raw_buffer_store_b32(
+                    __builtin_bit_cast(uint32_t, acc[mt][st][r] * ts), yr, off, 0, 0);
+              }
+            }
+          }
+        }
+      return;
+    }
+  }
   if (SWIGLU) {
     // g in subtile 0, u in subtile 1 of the same lane
     if (!wcol_ok(0, col)) return;
@@ -624,6 +666,26 @@ __global__ __launch_bounds__(768) void gemm_wide(GemmArgs a) {
   }
 
   const float ts = a.w_ts[0];
+  if (ACT == 0 && rows_m * a.ldy * 4 < ((int64_t)1 << 31)) {
+    // Branch-free stores through a descriptor over the tile's rows: rows past M fall
+    // outside its range, columns past N take an out-of-range offset.
+    const auto yr = rsrc(a.y + m0 * a.ldy, rows_m * a.ldy * 4);
+    const uint32_t ldy = (uint32_t)a.ldy;
+#pragma unroll
+    for (int mt = 0; mt < 4; mt++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) {
+        const uint32_t lrow = 128 * wm + 32 * mt + 8 * (r >> 2) + 4 * h + (r & 3);
+#pragma unroll
+        for (int st = 0; st < 2; st++) {
+          const int64_t n = n0 + 64 * wn + 32 * st + col;
+          const uint32_t off = n < N ? (lrow * ldy + (uint32_t)n) * 4u : kOOB;
+          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, acc[mt][st][r] * ts),
+                                                yr, off, 0, 0);
+        }
+      }
+    return;
+  }
 #pragma unroll
   for (int mt = 0; mt < 4; mt++) {
 #pragma unroll
