@@ -994,6 +994,9 @@ __global__ __launch_bounds__(768) void gemm_wide_grouped(GemmArgs a) {
 // stores at the end of a tile overlap the next tile's steps instead of ending a round of
 // workgroups together. Per tile the arithmetic (MFMA chain, k order, epilogue) is
 // gemm_wide_grouped's, so every result is the same bits.
+// DENSE: the plain product of gemm_wide (BF16 activations, rows [M] of x and y): the
+// tiles of the 256 x 256 grid in gemm_wide's order, XCD x taking the x-th eighth of them
+// (for the prefill shape one row block each), and the identity as each tile's row table.
 // ---------------------------------------------------------------------------------------
 constexpr int kPersistMaxTiles = 256;  // tiles per workgroup: one header per producer lane
 
@@ -1005,7 +1008,7 @@ struct PState {  // a tile's operand offsets for the producer lane
   __amdgpu_buffer_rsrc_t wr, sr;
 };
 
-template <int ACT, bool SWIGLU, bool SB>
+template <int ACT, bool SWIGLU, bool SB, bool DENSE = false>
 __global__ __launch_bounds__(768) void gemm_wide_grouped_p(GemmArgs a) {
   constexpr int BM = kWideBM;
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
@@ -1024,11 +1027,12 @@ __global__ __launch_bounds__(768) void gemm_wide_grouped_p(GemmArgs a) {
   const int64_t half = N >> 1;
   const int64_t nbn = SWIGLU ? (half + BN / 2 - 1) / (BN / 2) : (N + BN - 1) / BN;
 
-  const int64_t n_act = *a.n_active;
-  const int64_t per_xcd = (n_act + 7) / 8;
   const int64_t xcd = blockIdx.x % 8, jb = blockIdx.x / 8, jstep = gridDim.x / 8;
-  const int64_t tx = n_act - xcd * per_xcd;  // active experts in this XCD's share
-  const int64_t J = nbn * (tx <= 0 ? 0 : (tx < per_xcd ? tx : per_xcd));
+  // this XCD's share: active experts (each with its column blocks), or dense tiles
+  const int64_t n_units = DENSE ? ((a.M + BM - 1) / BM) * nbn : *a.n_active;
+  const int64_t per_xcd = (n_units + 7) / 8;
+  const int64_t tx = n_units - xcd * per_xcd;  // units in this XCD's share
+  const int64_t J = (DENSE ? 1 : nbn) * (tx <= 0 ? 0 : (tx < per_xcd ? tx : per_xcd));
   const int ntiles = jb < J ? (int)((J - jb + jstep - 1) / jstep) : 0;
   if (ntiles == 0) return;  // uniform over the workgroup, before any barrier
 
@@ -1038,21 +1042,29 @@ __global__ __launch_bounds__(768) void gemm_wide_grouped_p(GemmArgs a) {
   if (wave >= 8 && tid - 512 < ntiles) {
     const int i = tid - 512;
     const int64_t j = jb + (int64_t)i * jstep;
-    const int e = a.active[xcd * per_xcd + j / nbn];
-    const int32_t beg = a.offsets[e];
-    const int32_t cnt = a.offsets[e + 1] - beg;
-    hdr[i] = make_int4(e, beg, cnt < BM ? cnt : BM, (int)(j % nbn));
-    // read here, before any store: once the kernel has stored, a load of w_ts may no
-    // longer be a scalar load, and a vector load in the epilogue would make the compiler
-    // wait for all earlier stores at each of its joins
-    hts[i] = a.apply_ts ? a.w_ts[e] : 1.0f;
+    if (DENSE) {
+      // header: expert 0, first row, rows, column block
+      const int64_t lin = xcd * per_xcd + j;
+      const int64_t m0 = (lin / nbn) * BM;
+      hdr[i] = make_int4(0, (int)m0, (int)(a.M - m0 < BM ? a.M - m0 : BM), (int)(lin % nbn));
+      hts[i] = a.w_ts[0];
+    } else {
+      const int e = a.active[xcd * per_xcd + j / nbn];
+      const int32_t beg = a.offsets[e];
+      const int32_t cnt = a.offsets[e + 1] - beg;
+      hdr[i] = make_int4(e, beg, cnt < BM ? cnt : BM, (int)(j % nbn));
+      // read here, before any store: once the kernel has stored, a load of w_ts may no
+      // longer be a scalar load, and a vector load in the epilogue would make the
+      // compiler wait for all earlier stores at each of its joins
+      hts[i] = a.apply_ts ? a.w_ts[e] : 1.0f;
+    }
   }
   __syncthreads();  // headers ready
   // tile 0's row table (each producer lane writes its row pt)
   if (wave >= 8) {
     const int pt = tid - 512;
     const int4 h0 = hdr[0];
-    const int32_t route = pt < h0.z ? a.sorted[h0.y + pt] : -1;
+    const int32_t route = pt < h0.z ? (DENSE ? h0.y + pt : a.sorted[h0.y + pt]) : -1;
     row_route[0][pt] = route;
     row_x[0][pt] = route < 0 ? -1 : (a.rows_per_token ? route / a.top_k : route);
   }
@@ -1208,13 +1220,15 @@ __global__ __launch_bounds__(768) void gemm_wide_grouped_p(GemmArgs a) {
     // the routes, for the next tiles' row tables: loaded without a branch (a lane past the
     // tile's routes reads zero), so that no load in flight is waited for early
     const int64_t nroutes = a.rows_per_token ? a.x_rows * a.top_k : a.x_rows;
-    const auto rr = rsrc(uni(a.sorted), uni64(nroutes * 4));
+    const auto rr = rsrc(uni(DENSE ? nullptr : a.sorted), uni64(DENSE ? 0 : nroutes * 4));
     for (int i = 0; i < ntiles; i++) {
       // this lane's row of the next tile's row table, in flight during the first round
       const int4 hn = tile_hdr(i + 1);
       const bool has = pt < hn.z;
-      int32_t rl = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(
-          rr, has ? (uint32_t)(hn.y + pt) * 4u : kOOB, 0, 0);
+      int32_t rl = hn.y + pt;  // DENSE: the identity
+      if (!DENSE)
+        rl = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(rr, has ? (uint32_t)(hn.y + pt) * 4u : kOOB,
+                                                           0, 0);
       // rounds of four steps (SB: one scale piece each) or two
       for (int kt = 0; kt < KT2; kt += SB ? 4 : 2) {
         pstep(I0{}, kt, ra[1], rb[1]);
@@ -1618,10 +1632,49 @@ hipError_t launch_mt(const GemmArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// CUs of the current device, rounded down to a multiple of eight (0 if unknown): the grid
+// of the persistent wide grouped form, one workgroup per CU
+int persist_grid() {
+  static int cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return 0;
+    cached[dev] = n / 8 * 8;
+  }
+  return cached[dev];
+}
+
 template <int ACT>
 hipError_t launch_wide(const GemmArgs& a, hipStream_t stream) {
   const int64_t blocks = ((a.M + kWideBM - 1) / kWideBM) * ((a.N + BN - 1) / BN);
   const size_t lds = 2 * (size_t)(kWideBM + BN) * LDA * sizeof(uint16_t);
+  if constexpr (ACT == 0) {
+    // more tiles than CUs: the persistent pipeline (gemm_wide_grouped_p's dense form), on
+    // the conditions of its grouped use: eight steps per tile or more, at most
+    // kPersistMaxTiles tiles per workgroup, and x, the weight codes and the output within
+    // 32-bit offsets from their bases
+    const int grid = persist_grid();
+    const int64_t KT = (a.K + BK - 1) / BK;
+    constexpr int64_t kLim = (int64_t)1 << 31;
+    if (grid >= 8 && blocks > grid && KT + (KT & 1) >= 8 && a.M * a.ldy * 4 < kLim &&
+        ((a.M - 1) * a.ldx + a.K) * 2 < kLim && a.N * (a.K >> 1) < kLim &&
+        ((blocks + 7) / 8 + grid / 8 - 1) / (grid / 8) <= kPersistMaxTiles) {
+      GemmArgs d = a;
+      d.x_rows = a.M;
+      d.rows_per_token = 0;
+      d.top_k = 1;
+      if (scale_pieces(a))
+        hipLaunchKernelGGL((gemm_wide_grouped_p<0, false, true, true>), dim3((uint32_t)grid),
+                           dim3(768), lds, stream, d);
+      else
+        hipLaunchKernelGGL((gemm_wide_grouped_p<0, false, false, true>), dim3((uint32_t)grid),
+                           dim3(768), lds, stream, d);
+      return hipGetLastError();
+    }
+  }
   if (scale_pieces(a))
     hipLaunchKernelGGL((gemm_wide<ACT, true>), dim3((uint32_t)blocks), dim3(768), lds, stream, a);
   else
@@ -1670,20 +1723,6 @@ hipError_t launch_grouped_mt(const GemmArgs& a, int64_t max_tiles, hipStream_t s
   return hipGetLastError();
 }
 
-// CUs of the current device, rounded down to a multiple of eight (0 if unknown): the grid
-// of the persistent wide grouped form, one workgroup per CU
-int persist_grid() {
-  static int cached[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  if (cached[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-      return 0;
-    cached[dev] = n / 8 * 8;
-  }
-  return cached[dev];
-}
 
 template <int ACT, bool SWIGLU>
 hipError_t launch_grouped_wide_p(const GemmArgs& a, int grid, size_t lds, bool sb,

@@ -261,6 +261,29 @@ def test_linear_wide_tiles_ragged(dev, o, K):
     assert_within(y4[torch.from_numpy(rows).to(dev)].cpu().numpy(), yr4, b4, "wide ragged w4a4")
 
 
+def test_linear_wide_persistent_several_tiles(dev, o):
+    """With more 256 x 256 tiles than CUs the wide GEMM runs as a persistent pipeline, each
+    workgroup taking its XCD's tiles in turn, the next tile's loads issued while the last
+    steps of the current one run. Here 6 row blocks (the last one 20 rows) x 128 column
+    blocks (the last one ragged) = 768 tiles, three per workgroup on 256 CUs: sampled rows
+    and every row of the ragged block against the oracle, the same bits on a second call,
+    and the first 64 rows equal to the 64-row kernel's product of those rows alone (one k
+    order for every tiling)."""
+    M, N, K = 1300, 128 * 256 - 40, 512
+    _say(f"wide-tile gemm, several tiles per workgroup, M={M} N={N} K={K} (sampled rows)")
+    w = weight_f32(75, N, K)
+    (c, s, t), oq = quantize_both(o, w, dev)
+    xb = act_bf16(76, M, K)
+    xd = to_dev_bf16(xb, dev)
+    y = nv.linear(xd, c, s, t)
+    rows = np.unique(np.r_[0, 255, 256, 1023, 1024, 1279, np.arange(1280, M), np.arange(3, 1280, 41)])
+    wdq = o.dequant(*oq, per_row=False)
+    yr, b = o.linear_f64(o.bf16_to_f64(xb[rows]), wdq)
+    assert_within(y[torch.from_numpy(rows).to(dev)].cpu().numpy(), yr, b, "persistent wide rows")
+    assert torch.equal(nv.linear(xd, c, s, t), y)
+    assert torch.equal(nv.linear(xd[:64].contiguous(), c, s, t), y[:64])
+
+
 def test_linear_wide_tiles_padded_rows(dev, o):
     """The 256 x 256-tile GEMM on ragged M, N and K with an odd number of 64-k steps and
     padded activation and output rows; sampled rows, including every row of the last,
