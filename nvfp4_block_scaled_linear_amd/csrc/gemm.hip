@@ -9,6 +9,9 @@
 //    eight consumer waves (two along M, four along N, each 128 x 64 with the 32x32x16
 //    BF16 MFMA) only read LDS and run MFMAs; four producer waves only load, decode the
 //    weight tile once per workgroup and write both operands to LDS (gemm_wide below).
+//    With more such tiles than CUs (BF16 activations), one workgroup per CU takes its
+//    XCD's tiles in turn as a persistent pipeline, the next tile's loads issued while
+//    the current one's last steps and stores run (gemm_wide_grouped_p's dense form).
 //  - Smaller M: a 32*MT (M) x 256 (N) tile on four wave64s side by side along N, each
 //    computing 32*MT x 64 and decoding its own weight columns in registers; two
 //    workgroups per CU.
@@ -25,7 +28,8 @@
 //  - Workgroups are numbered per XCD (blockIdx % 8) so that the operand an XCD reuses
 //    stays in its own L2: the 256-row tiles share activation rows (A-stationary); the
 //    smaller-M kernels take an eighth of the weight's columns per XCD (weight-stationary).
-// The fp32 accumulator is scaled once by the tensor scale(s) in the epilogue.
+// The fp32 accumulator is scaled once by the tensor scale(s) in the epilogue; with BF16
+// activations the results leave through branch-free buffer stores.
 #include <type_traits>
 
 #include "device.hpp"
