@@ -70,8 +70,10 @@ __device__ __forceinline__ int32_t block_exclusive_scan(int32_t v, int32_t* wsum
 // slot record gives a streaming workgroup its expert, its route range and (when the
 // caller fills them: slot_of != NULL, then slot_of[e] is e's slot) its first routes in
 // one 64-byte read, without the dependent reads of the active list, offsets and routes.
+// write = false: only cnt becomes each expert's first slot (no workspace writes)
 __device__ __forceinline__ void expert_scans(const RouteWorkspace& ws, int E, int32_t* cnt,
-                                             int32_t* wsum, int32_t* slot_of = nullptr) {
+                                             int32_t* wsum, int32_t* slot_of = nullptr,
+                                             bool write = true) {
   const int tid = threadIdx.x, nt = blockDim.x;
   int32_t run = 0, act_run = 0, tile_run = 0;
   for (int e0 = 0; e0 < E; e0 += nt) {
@@ -83,7 +85,7 @@ __device__ __forceinline__ void expert_scans(const RouteWorkspace& ws, int E, in
     const int32_t o = block_exclusive_scan(c, wsum, &tot) + run;
     const int32_t a = block_exclusive_scan(c > 0 ? 1 : 0, wsum, &tot_a) + act_run;
     const int32_t to = block_exclusive_scan(ntile, wsum, &tot_t) + tile_run;
-    if (e < E) {
+    if (e < E && write) {
       ws.offsets[e] = o;
       if (c > 0) {
         ws.active[a] = e;
@@ -92,14 +94,14 @@ __device__ __forceinline__ void expert_scans(const RouteWorkspace& ws, int E, in
         if (slot_of) slot_of[e] = a;
       }
       if (ntile > 0) write_tiles(ws, e, o + (c - rest), rest, to);
-      cnt[e] = o;
     }
+    if (e < E) cnt[e] = o;
     run += tot;
     act_run += tot_a;
     tile_run += tot_t;
   }
-  for (int s = act_run + tid; s < ws.max_slots; s += nt) ws.slots[kSlotInts * s] = -1;
-  if (tid == 0) {
+  for (int s = act_run + tid; write && s < ws.max_slots; s += nt) ws.slots[kSlotInts * s] = -1;
+  if (tid == 0 && write) {
     ws.offsets[E] = run;
     *ws.n_active = act_run;
     if (ws.tile_rows > 0) *ws.n_tiles = tile_run;
@@ -259,6 +261,52 @@ __global__ __launch_bounds__(kChunkTokens) void route_scatter_chunks(const int32
   for (int e = tid; e < E; e += kChunkTokens) cur[e] = cc[e];
   __syncthreads();
   const int64_t t = (int64_t)blockIdx.x * kChunkTokens + tid;
+  if (t >= T) return;
+  int32_t e[KREG];
+  bool ok[KREG];
+  load_token<KREG>(ids, t, top_k, E, e, ok);
+#pragma unroll
+  for (int j = 0; j < KREG; j++) {
+    if (j >= top_k) break;
+    if (ok[j]) ws.sorted[atomicAdd(&cur[e[j]], 1)] = (int32_t)(t * top_k + j);
+  }
+}
+
+// route_scan_chunks and route_scatter_chunks in one launch, for up to kFusedScanChunks
+// chunks: every workgroup sums the chunks' counts itself (its own chunk's first slot per
+// expert: the expert's first slot plus the earlier chunks' counts), workgroup 0 also
+// writes the offsets, the active list, the slot records and the tile list, and each then
+// places its chunk's routes. The same grouping as the three launches.
+constexpr int64_t kFusedScanChunks = 32;
+
+template <int KREG>
+__global__ __launch_bounds__(kChunkTokens) void route_scan_scatter_chunks(const int32_t* ids,
+                                                                          int64_t T, int top_k_rt,
+                                                                          int E, int64_t nchunks,
+                                                                          RouteWorkspace ws) {
+  const int top_k = KREG == kRegTopK ? top_k_rt : KREG;
+  extern __shared__ int32_t sh[];
+  int32_t* wsum = sh;        // [16] wave totals of a scan
+  int32_t* cnt = sh + 16;    // [E] routes per expert, then each expert's first slot
+  int32_t* cur = cnt + E;    // [E] this chunk's next slot per expert
+  const int tid = threadIdx.x;
+  const int64_t ch = blockIdx.x;
+  for (int e = tid; e < E; e += kChunkTokens) {
+    int32_t c = 0, before = 0;
+#pragma unroll 8
+    for (int64_t k = 0; k < nchunks; k++) {
+      const int32_t v = ws.chunk_counts[k * E + e];
+      before += k < ch ? v : 0;
+      c += v;
+    }
+    cnt[e] = c;
+    cur[e] = before;
+  }
+  __syncthreads();
+  expert_scans(ws, E, cnt, wsum, nullptr, ch == 0);
+  for (int e = tid; e < E; e += kChunkTokens) cur[e] += cnt[e];
+  __syncthreads();
+  const int64_t t = ch * kChunkTokens + tid;
   if (t >= T) return;
   int32_t e[KREG];
   bool ok[KREG];
@@ -439,6 +487,17 @@ hipError_t launch_route_sort(const int32_t* topk_ids, int64_t T, int top_k, int 
                        top_k, E, ws, faults, zero_out, zero_row_bytes);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if (nchunks <= kFusedScanChunks) {
+      auto kf = top_k == 1 ? route_scan_scatter_chunks<1>
+              : top_k == 2 ? route_scan_scatter_chunks<2>
+              : top_k == 4 ? route_scan_scatter_chunks<4>
+              : top_k == 8 ? route_scan_scatter_chunks<8>
+                           : route_scan_scatter_chunks<kRegTopK>;
+      hipLaunchKernelGGL(kf, dim3((uint32_t)nchunks), dim3(kChunkTokens),
+                         sizeof(int32_t) * (16 + 2 * (size_t)E), stream, topk_ids, T, top_k, E,
+                         nchunks, ws);
+      return hipGetLastError();
+    }
     hipLaunchKernelGGL(route_scan_chunks, dim3(1), dim3(kSortThreads), lds, stream, E, nchunks, ws);
     e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -611,6 +611,48 @@ def test_grouped_wide_persistent_several_tiles(dev, o, K):
     assert torch.equal(nv.grouped_linear(x, wc, wsc, wts, ids_d, out_mode=nv.OUT_SWIGLU_BF16), a)
 
 
+def test_grouped_chunked_grouping_both_forms(dev, o):
+    """Route sets in chunks of 256 tokens are grouped in two launches up to 32 chunks (the
+    counts, then the scan folded into the scatter workgroups, each summing the chunks'
+    counts itself) and in three beyond (counts, one scan workgroup, scatter). Here 9000
+    tokens (36 chunks: three launches), top-2 over 64 experts with dropped routes: every
+    output of sampled routes against the oracle, dropped routes' rows zero, a repeated
+    call equal bit for bit, and the first 8192 tokens' rows equal to those of a call on
+    those tokens alone (32 chunks: two launches), since a route's row depends on neither
+    the grouping's form nor its order. Both forms with the combine as well."""
+    E, N, K, T, k = 64, 64, 128, 9000, 2
+    _say(f"grouped GEMM, chunked grouping in both forms: E={E} N={N} K={K} T={T} k={k}")
+    wc, wsc, wts, oc, os_, ot, ids, rw, xb = _prefill_case(dev, o, E, N, K, T, k, 181)
+    ids[17, 1] = ids[17, 0]  # repeated within its token: dropped
+    ids[8500, 0] = -3        # out of range: dropped
+    x = to_dev_bf16(xb, dev)
+    ids_d = torch.from_numpy(ids).to(dev)
+    faults = torch.zeros(1, dtype=torch.int32, device=dev)
+    h_d = nv.grouped_linear(x, wc, wsc, wts, ids_d, faults=faults)
+    assert int(faults.item()) & nv.FAULT_BAD_ROUTE
+    h = h_d.cpu().numpy()
+    assert not np.any(h[17 * k + 1]) and not np.any(h[8500 * k])
+    x64 = o.bf16_to_f64(xb)
+    rng = np.random.default_rng(182)
+    for r in np.r_[0, 1, 8191 * k, 8192 * k, T * k - 1, rng.choice(T * k, 60, replace=False)]:
+        t, j = divmod(int(r), k)
+        e = int(ids[t, j])
+        if e < 0 or e >= E or (j == 1 and t == 17):
+            continue
+        wdq = o.dequant(oc[e], os_[e], ot[e:e + 1], per_row=False)
+        yr, b = o.linear_f64(x64[t:t + 1], wdq)
+        assert_within(h[r:r + 1], yr, b, f"chunked grouping route {t},{j}")
+    assert torch.equal(nv.grouped_linear(x, wc, wsc, wts, ids_d), h_d)
+    T2 = 8192
+    h2 = nv.grouped_linear(x[:T2].contiguous(), wc, wsc, wts, ids_d[:T2].contiguous())
+    assert torch.equal(h2, h_d[:T2 * k])
+    rw_d = torch.from_numpy(rw).to(dev)
+    y = nv.grouped_linear(x, wc, wsc, wts, ids_d, topk_w=rw_d, out_mode=nv.OUT_COMBINE)
+    y2 = nv.grouped_linear(x[:T2].contiguous(), wc, wsc, wts, ids_d[:T2].contiguous(),
+                           topk_w=rw_d[:T2].contiguous(), out_mode=nv.OUT_COMBINE)
+    assert torch.equal(y2, y[:T2])
+
+
 def test_moe_prefill_layer_full_shape(dev, o, moe):
     """The MoE layer at prompt size as the benchmark runs it: 4096 tokens over the 128
     experts, top-8 (32768 routes, the chunked grouping, six SwiGLU column blocks of the
