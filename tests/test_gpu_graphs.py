@@ -67,6 +67,18 @@ def test_graph_linear(dev, M):
                    lambda: nv.linear(x2, c, s, t))
 
 
+def test_graph_linear_persistent_gemm(dev):
+    """The wide GEMM's persistent pipeline (more 256 x 256 tiles than CUs: 3 x 86 = 258,
+    ragged in M and N): each replay bit-equal to the eager call."""
+    M, N, K = 600, 86 * 256 - 100, 512
+    c, s, t = _weight(dev, 66, N, K)
+    x = to_dev_bf16(act_bf16(67, M, K), dev)
+    x2 = to_dev_bf16(act_bf16(68, M, K), dev)
+    y = torch.empty((M, N), dtype=torch.float32, device=dev)
+    _check_replays(lambda: nv.linear(x, c, s, t, out=y), [y],
+                   lambda: nv.linear(x2, c, s, t))
+
+
 def test_graph_w4a4_two_calls_and_in_call(dev):
     N, K, M = 768, 2048, 1
     c, s, t = _weight(dev, 63, N, K)
